@@ -1,0 +1,186 @@
+"""Pins for the oracle's grouped matmul and combine (CPU only).
+
+* brute force: every (token, slot) pair recomputed by pure-Python loops that
+  decode each weight from its bit fields, without the sort;
+* closed forms: all-ones weights give row sums, all-zero codes give zeros;
+* exactness: sampled outputs against exact rational dot products, within the
+  float64 summation error bound;
+* combine: one-hot, uniform and zero router weights.
+"""
+
+import math
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from oracle.gmm import bf16_bits_to_f64
+from moe_grouped_gemm_route_amd.synth import make_problem, make_config
+
+
+def _e2m1_fields(nib):
+    s, e, m = nib >> 3, (nib >> 1) & 3, nib & 1
+    mag = m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1 + m / 2)
+    return -mag if s else mag
+
+
+def _w_brute(p, e, n, kk):
+    byte = int(p["codes"][e, n, kk // 2])
+    nib = (byte >> 4) if kk % 2 else (byte & 0xF)
+    return _e2m1_fields(nib) * math.ldexp(1.0, int(p["scales"][e, n, kk // 32]) - 127)
+
+
+def _x_val(bits):
+    return float(bf16_bits_to_f64(np.array([bits]))[0])
+
+
+def _mx(p):
+    return {"fmt": "mxfp4", "codes": p["codes"], "scales": p["scales"]}
+
+
+def test_gmm_brute_force_gather():
+    p = make_problem(T=6, k=2, E=4, K=64, N=8, seed=11, empty_experts=(3,))
+    r = oracle.route_sort(p["topk_ids"], p["E"])
+    y = oracle.gmm(p["x"], r["sorted_token"], r["group_offsets"], _mx(p))
+    for t in range(p["T"]):
+        for j in range(p["k"]):
+            e = int(p["topk_ids"][t, j])
+            row = r["pair_row"][t * p["k"] + j]
+            for n in range(p["N"]):
+                ref = sum(_x_val(p["x"][t, kk]) * _w_brute(p, e, n, kk) for kk in range(p["K"]))
+                assert abs(y[row, n] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_gmm_brute_force_band_input():
+    p = make_problem(T=4, k=3, E=5, K=96, N=4, seed=12, x_rows=12)
+    r = oracle.route_sort(p["topk_ids"], p["E"])
+    y = oracle.gmm(p["x"], None, r["group_offsets"], _mx(p))
+    off = r["group_offsets"]
+    for e in range(p["E"]):
+        for row in range(off[e], off[e + 1]):
+            for n in range(p["N"]):
+                ref = sum(_x_val(p["x"][row, kk]) * _w_brute(p, e, n, kk) for kk in range(p["K"]))
+                assert abs(y[row, n] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_gmm_closed_forms():
+    p = make_problem(T=8, k=2, E=3, K=128, N=4, seed=13)
+    r = oracle.route_sort(p["topk_ids"], p["E"])
+    x = bf16_bits_to_f64(p["x"])
+    ones = {"fmt": "mxfp4", "codes": np.full_like(p["codes"], 0x22),
+            "scales": np.full_like(p["scales"], 127)}
+    y = oracle.gmm(p["x"], r["sorted_token"], r["group_offsets"], ones)
+    assert np.allclose(y, x[r["sorted_token"]].sum(axis=1, keepdims=True), rtol=0, atol=1e-12)
+    neg2 = {"fmt": "mxfp4", "codes": np.full_like(p["codes"], 0xAA),
+            "scales": np.full_like(p["scales"], 128)}
+    y = oracle.gmm(p["x"], r["sorted_token"], r["group_offsets"], neg2)
+    assert np.allclose(y, -2 * x[r["sorted_token"]].sum(axis=1, keepdims=True), rtol=0, atol=1e-12)
+    zeros = {"fmt": "mxfp4", "codes": np.zeros_like(p["codes"]), "scales": p["scales"]}
+    assert np.all(oracle.gmm(p["x"], r["sorted_token"], r["group_offsets"], zeros) == 0)
+
+
+def test_gmm_empty_band_and_trailing_rows():
+    p = make_problem(T=4, k=1, E=3, K=32, N=2, seed=14, empty_experts=(1,))
+    p["topk_ids"][0, 0] = 7                       # out of range: dropped
+    r = oracle.route_sort(p["topk_ids"], p["E"])
+    assert r["group_offsets"][2] == r["group_offsets"][1]
+    y = oracle.gmm(p["x"], np.maximum(r["sorted_token"], 0), r["group_offsets"], _mx(p))
+    assert np.all(np.isnan(y[3:])) and not np.any(np.isnan(y[:3]))
+
+
+def _exact_dot(xbits, wcol):
+    return sum(Fraction(_x_val(b)) * Fraction(float(w)) for b, w in zip(xbits, wcol))
+
+
+def test_gmm_float64_error_within_summation_bound():
+    cfg = make_config(1)
+    r = oracle.route_sort(cfg["topk_ids"], cfg["E"])
+    y = oracle.gmm(cfg["x"], r["sorted_token"], r["group_offsets"], _mx(cfg))
+    rng = np.random.default_rng(5)
+    K = cfg["K"]
+    u = 2.0 ** -53
+    gamma = K * u / (1 - K * u)
+    off = r["group_offsets"]
+    for _ in range(200):
+        row = int(rng.integers(0, off[-1]))
+        col = int(rng.integers(0, cfg["N"]))
+        e = int(np.searchsorted(off, row, side="right") - 1)
+        w = oracle.decode_mxfp4(cfg["codes"][e, col], cfg["scales"][e, col])
+        xb = cfg["x"][r["sorted_token"][row]]
+        exact = _exact_dot(xb, w)
+        bound = gamma * float(sum(abs(Fraction(_x_val(b)) * Fraction(float(v))) for b, v in zip(xb, w)))
+        assert abs(Fraction(y[row, col]) - exact) <= Fraction(bound)
+
+
+def test_gmm_sampled_matches_full():
+    p = make_problem(T=16, k=3, E=6, K=128, N=32, seed=15)
+    r = oracle.route_sort(p["topk_ids"], p["E"])
+    y = oracle.gmm(p["x"], r["sorted_token"], r["group_offsets"], _mx(p))
+    rows = np.arange(48)
+    cols = (rows * 7) % 32
+    s = oracle.gmm_sampled(p["x"], r["sorted_token"], r["group_offsets"], _mx(p), rows, cols)
+    assert np.allclose(s, y[rows, cols], rtol=1e-14, atol=1e-14)
+
+
+def test_gmm_nvfp4_equals_mxfp4_after_cast():
+    p = make_problem(T=16, k=3, E=6, K=256, N=16, seed=16)
+    r = oracle.route_sort(p["topk_ids"], p["E"])
+    bs, ts = oracle.mxfp4_to_nvfp4(p["scales"])
+    nv = {"fmt": "nvfp4", "codes": p["codes"], "block_scales": bs, "tensor_scale": ts}
+    a = oracle.gmm(p["x"], r["sorted_token"], r["group_offsets"], _mx(p))
+    b = oracle.gmm(p["x"], r["sorted_token"], r["group_offsets"], nv)
+    assert np.array_equal(a, b)
+
+
+def test_combine_special_cases():
+    rng = np.random.default_rng(6)
+    T, k, N = 5, 3, 7
+    y = rng.standard_normal((T * k, N))
+    pair_row = rng.permutation(T * k).astype(np.int32)
+    onehot = np.zeros((T, k), dtype=np.float32)
+    onehot[np.arange(T), np.arange(T) % k] = 1.0
+    out = oracle.combine(y, onehot, pair_row)
+    for t in range(T):
+        assert np.array_equal(out[t], y[pair_row[t * k + t % k]])
+    uni = np.full((T, k), 1.0 / k)
+    out = oracle.combine(y, uni, pair_row)
+    for t in range(T):
+        ref = sum(y[pair_row[t * k + j]] for j in range(k)) / k
+        assert np.allclose(out[t], ref, rtol=1e-14, atol=1e-14)
+    w = rng.random((T, k))
+    w[:, 1] = 0.0
+    pr = pair_row.copy()
+    pr[k * 2 + 2] = -1                             # dropped pair contributes nothing
+    out = oracle.combine(y, w, pr)
+    for t in range(T):
+        ref = sum(w[t, j] * y[pr[t * k + j]] for j in range(k) if pr[t * k + j] >= 0)
+        assert np.allclose(out[t], ref, rtol=1e-14, atol=1e-14)
+
+
+def test_gmm_nvfp4_brute_force_random_block_scales():
+    # general NVFP4 weights: every per-16 E4M3 byte drawn independently
+    import torch
+    p = make_problem(T=5, k=2, E=3, K=64, N=6, seed=17)
+    rng = np.random.default_rng(18)
+    bs = rng.integers(0x08, 0x78, size=(3, 6, 4)).astype(np.uint8)   # finite, non-zero
+    ts = np.array([0.25, 3.0, 1.0 / 1024], dtype=np.float32)
+    e4m3 = torch.from_numpy(bs.copy()).view(torch.float8_e4m3fn).double().numpy()
+    nv = {"fmt": "nvfp4", "codes": p["codes"], "block_scales": bs, "tensor_scale": ts}
+    r = oracle.route_sort(p["topk_ids"], p["E"])
+    y = oracle.gmm(p["x"], r["sorted_token"], r["group_offsets"], nv)
+    rows = np.arange(10)
+    cols = rows % 6
+    s = oracle.gmm_sampled(p["x"], r["sorted_token"], r["group_offsets"], nv, rows, cols)
+    for t in range(p["T"]):
+        for j in range(p["k"]):
+            e = int(p["topk_ids"][t, j])
+            row = r["pair_row"][t * p["k"] + j]
+            for n in range(p["N"]):
+                ref = 0.0
+                for kk in range(p["K"]):
+                    byte = int(p["codes"][e, n, kk // 2])
+                    nib = (byte >> 4) if kk % 2 else (byte & 0xF)
+                    ref += (_x_val(p["x"][t, kk]) * _e2m1_fields(nib)
+                            * e4m3[e, n, kk // 16] * float(ts[e]))
+                assert abs(y[row, n] - ref) <= 1e-12 * (1 + abs(ref))
+    assert np.allclose(s, y[rows, cols], rtol=1e-14, atol=1e-14)
