@@ -1,0 +1,208 @@
+/*
+ * moe_gmm.h - routed-expert W4A16 grouped matmul for AMD MI355X (gfx950).
+ *
+ * C ABI of libmoegmm.so.  The path computes one MoE layer's routed-expert
+ * matmuls the way "Running DeepSeek V4 Flash on TPU v6" (section "1. Four
+ * bits that v6e can't hold") describes them: token-expert pairs are sorted
+ * into one contiguous band of rows per expert, and for every (expert, M-tile)
+ * x N-tile the K dimension is walked with the 4-bit weight tile decoded to
+ * bf16 right after it arrives on chip, block-scaled, and accumulated in f32 on
+ * the bf16 matrix unit.  Weights are MXFP4 (e2m1 codes, one E8M0 power-of-two
+ * scale per 32 weights along K) or NVFP4 (e2m1 codes, one E4M3 scale per 16
+ * weights along K, one f32 scale per expert); activations stay bf16.
+ *
+ * Conventions for every call below:
+ *  - Every data pointer is a DEVICE pointer (hipMalloc'd or a torch CUDA
+ *    tensor's data_ptr()).  The caller owns every buffer; the library
+ *    allocates nothing and keeps no state, so calls are reentrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued asynchronously; results are valid after the caller
+ *    synchronises that stream.  No call synchronises the device.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    non-zero moe_status_t is returned and nothing is launched.  A launch
+ *    failure reported by the runtime returns MOE_ERR_HIP.
+ *  - bf16 values are passed as uint16_t bit patterns; f32 as float.
+ *  - Array shapes are row-major, written [d0, d1, ...].
+ */
+#ifndef MOE_GMM_H
+#define MOE_GMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  MOE_ERR_SHAPE = 2,       /* a size is non-positive, too large or misaligned */
+  MOE_ERR_FORMAT = 3,      /* unknown weight format or dtype enum             */
+  MOE_ERR_UNSUPPORTED = 4, /* valid request this build does not implement     */
+  MOE_ERR_HIP = 5          /* the HIP runtime reported a launch error         */
+} moe_status_t;
+
+typedef enum { MOE_W_MXFP4 = 0, MOE_W_NVFP4 = 1 } moe_wfmt_t;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* Kernel configuration of moe_gmm_ex.  AUTO picks from the problem shape. */
+typedef enum {
+  MOE_GMM_AUTO = 0,
+  MOE_GMM_STREAM = 1,  /* weight-streaming waves, no LDS: few rows per expert  */
+  MOE_GMM_TILED = 2    /* LDS-staged activation tiles: many rows per expert    */
+} moe_gmm_kernel_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(int status);
+
+/*
+ * moe_route_sort - counting sort of token-expert pairs into expert bands.
+ *
+ * Source: "Running DeepSeek V4 Flash on TPU v6", section "1. Four bits that
+ * v6e can't hold": tokens are sorted by expert so that each expert's
+ * activations form one contiguous band of rows, and the grouped matmul walks
+ * the band sizes.  Inside a band, pairs keep ascending flat pair order
+ * p = t*k + j (stable), so the result is unique and deterministic; positions
+ * are decided by counts and scans, never by atomics.
+ *
+ * topk_ids       [T, k] int32  expert of slot j of token t.
+ * group_offsets  [E+1]  int32  out: band e is rows [off[e], off[e+1]).
+ * sorted_token   [T*k]  int32  out: token of each band row; -1 past off[E].
+ * sorted_pair    [T*k]  int32  out: pair p of each band row; -1 past off[E].
+ * pair_row       [T*k]  int32  out: band row of pair p; -1 if dropped.
+ * err_count      [1]    int32  out, may be NULL: number of pairs whose id is
+ *                              outside [0, E); they are dropped from every
+ *                              band (the device-side data error).
+ * Limits: 1 <= T, 1 <= k, 1 <= E <= 1024, T*k <= 2^24.
+ */
+int moe_route_sort(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                   int32_t* group_offsets, int32_t* sorted_token,
+                   int32_t* sorted_pair, int32_t* pair_row, int32_t* err_count,
+                   void* stream);
+
+/*
+ * moe_packed_weight_bytes - size in bytes of the packed buffer that
+ * mxfp4_encode writes for E experts of an [N, K] weight (0 on bad sizes).
+ * Codes stay 4 bits per weight; scales stay one byte per block (padded to
+ * whole 256-byte groups), plus 4*E bytes of tensor scales for NVFP4.
+ */
+size_t moe_packed_weight_bytes(int fmt, int32_t E, int32_t N, int32_t K);
+
+/*
+ * mxfp4_encode - load-time repack of canonical expert weights into the
+ * packed layout moe_gmm streams.
+ *
+ * Source: "Running DeepSeek V4 Flash on TPU v6", section "1. Four bits that
+ * v6e can't hold": the expert weights are re-laid-out once when the model
+ * loads and stay 4 bits per weight in HBM; the grouped matmul streams them in
+ * BK x BN tiles.  On gfx950 the e2m1 codes are decoded natively, so the
+ * repack is a pure permutation of 16-byte code runs and scale bytes (the
+ * pages' signed re-encoding was needed only by hardware without 4-bit
+ * vectors).
+ *
+ * fmt            MOE_W_MXFP4 or MOE_W_NVFP4.
+ * codes          [E, N, K/2] uint8: two e2m1 codes per byte, the even K index
+ *                in the low nibble (bit 3 of a code = sign).
+ * scales         MXFP4: [E, N, K/32] E8M0 bytes (2^(b-127));
+ *                NVFP4: [E, N, K/16] E4M3FN bytes.
+ * tensor_scale   NVFP4: [E] float, the per-expert scale; MXFP4: must be NULL.
+ * packed         out, moe_packed_weight_bytes(fmt, E, N, K) bytes, 256-aligned.
+ * Limits: K % 128 == 0, N % 64 == 0, E >= 1, E*N*K/2 < 2^40.
+ */
+int mxfp4_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
+                 const float* tensor_scale, int32_t E, int32_t N, int32_t K,
+                 void* packed, void* stream);
+
+/*
+ * moe_gmm - routed-expert grouped matmul, W4A16 on bf16 MFMA.
+ *
+ * Source: "Running DeepSeek V4 Flash on TPU v6", section "1. Four bits that
+ * v6e can't hold" (the loop nest over N tiles and (expert, M-tile) pairs, K
+ * walked with the weight tile decoded to bf16 then block-scaled, f32
+ * accumulation on the bf16 matrix unit, ragged and empty groups) and section
+ * "Grouped matmul performance vs bf16" (the NVFP4 variant with per-16 E4M3
+ * block scales).
+ *
+ * For every row r of band e:  y[r, n] = sum_k x[src(r), k] * W_e[n, k]
+ * with W_e[n, k] = e2m1(code) * blockscale (* tensor_scale[e] for NVFP4),
+ * each decoded weight exact in bf16, products exact, sums in f32.
+ *
+ * packed         mxfp4_encode output for (fmt, E, N, K).
+ * x              bf16 [T, K] when row_index != NULL (row r reads
+ *                x[row_index[r]]), else bf16 [M, K] already in band order.
+ * row_index      [M] int32 (moe_route_sort's sorted_token) or NULL.
+ * group_offsets  [E+1] int32 device array from moe_route_sort.
+ * M              rows of y (T*k).  Rows [group_offsets[E], M) are not written.
+ * y              out [M, N], f32 or bf16 (round-to-nearest-even of the f32 sum).
+ * Preconditions not checked: row_index values index rows of x; group_offsets
+ * is non-decreasing with group_offsets[0] = 0 and group_offsets[E] <= M.
+ * Exact-decode domain: MXFP4 scale bytes 2..252 (block exponent -125..125).
+ * Limits as mxfp4_encode; M <= 2^24.
+ */
+int moe_gmm(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
+            const uint16_t* x, const int32_t* row_index,
+            const int32_t* group_offsets, int32_t M, void* y, int y_dtype,
+            void* stream);
+
+/* moe_gmm_ex - moe_gmm with an explicit kernel configuration
+ * (moe_gmm_kernel_t).  Every configuration computes the same sums in the same
+ * order, so all of them return bitwise identical y. */
+int moe_gmm_ex(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
+               const uint16_t* x, const int32_t* row_index,
+               const int32_t* group_offsets, int32_t M, void* y, int y_dtype,
+               int kernel, void* stream);
+
+/*
+ * moe_combine - top-k weighted unpermute back to token order.
+ *
+ * Source: the band layout of "Running DeepSeek V4 Flash on TPU v6", section
+ * "1. Four bits that v6e can't hold", and the deterministic expert reduction
+ * of "DeepSeek-V4-Flash" (PocketLLM docs), section "Correctness and
+ * precision": out[t, n] = sum over j = 0..k-1, in that order, of
+ * topk_weights[t, j] * y[pair_row[t*k + j], n], accumulated in f32 with
+ * fused multiply-adds; no atomics.  pair_row < 0 contributes nothing.
+ *
+ * y              [rows, N] f32 or bf16 (y_dtype), rows >= every pair_row + 1.
+ * topk_weights   [T, k] float.
+ * pair_row       [T*k] int32 (moe_route_sort output).
+ * out            [T, N] f32 or bf16 (out_dtype; bf16 = RNE of the f32 sum).
+ * Limits: N % 4 == 0, 1 <= k <= 64.
+ */
+int moe_combine(const void* y, int y_dtype, const float* topk_weights,
+                const int32_t* pair_row, int32_t T, int32_t k, int32_t N,
+                void* out, int out_dtype, void* stream);
+
+/*
+ * moe_mxfp4_to_nvfp4 - the lossless MXFP4 -> NVFP4 scale cast.
+ *
+ * Source: "DeepSeek-V4-Flash-0731-NVFP4", section "The lossless weight cast":
+ * per expert, with k_j the unbiased exponent of block j and k_max their
+ * maximum, the tensor scale is 2^(k_max - 8) and both 16-halves of block j
+ * get the E4M3 scale 2^(k_j - k_max + 8); codes are unchanged.
+ *
+ * scales         [E, N, K/32] E8M0 bytes of one expert tensor per expert.
+ * block_scales   out [E, N, K/16] E4M3FN bytes.
+ * tensor_scale   out [E] float.
+ * err_count      out [1] int32, may be NULL: blocks that cannot be held
+ *                exactly (k_j < k_max - 17, or a NaN byte 0xFF); such a
+ *                block's bytes are written as 0.
+ * Limits: K % 32 == 0, N >= 1, E >= 1.
+ */
+int moe_mxfp4_to_nvfp4(const uint8_t* scales, int32_t E, int32_t N, int32_t K,
+                       uint8_t* block_scales, float* tensor_scale,
+                       int32_t* err_count, void* stream);
+
+/*
+ * moe_debug_decode - decode a packed buffer back to dense bf16 weights
+ * [E, N, K] (test support).  Same decode as moe_gmm: e2m1 x block scale,
+ * exact in bf16; NVFP4 output excludes the per-expert tensor scale.
+ */
+int moe_debug_decode(const void* packed, int fmt, int32_t E, int32_t N,
+                     int32_t K, uint16_t* w_bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_GMM_H */

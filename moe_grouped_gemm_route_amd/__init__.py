@@ -1,0 +1,220 @@
+"""Python binding of libmoegmm.so: the routed-expert W4A16 grouped matmul for
+MI355X (gfx950).
+
+Thin ctypes marshalling over the C ABI in include/moe_gmm.h: every function
+takes torch CUDA tensors, passes their device pointers and the current HIP
+stream, allocates outputs with torch, and raises on a non-zero status.  All
+arithmetic runs in the library's HIP kernels; there is no fallback path.  The
+library is loaded on first use and its absence is an error.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MXFP4", "NVFP4", "F32", "BF16", "GMM_AUTO", "GMM_STREAM", "GMM_TILED",
+    "MoeGmmError", "library", "route_sort", "packed_weight_bytes", "mxfp4_encode",
+    "moe_gmm", "moe_combine", "mxfp4_to_nvfp4", "debug_decode",
+]
+
+MXFP4, NVFP4 = 0, 1
+F32, BF16 = 0, 1
+GMM_AUTO, GMM_STREAM, GMM_TILED = 0, 1, 2
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoegmm.so")
+_lib = None
+
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+_SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_route_sort": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_packed_weight_bytes": (_sz, [ctypes.c_int, _i32, _i32, _i32]),
+    "mxfp4_encode": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "moe_gmm": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp,
+                               ctypes.c_int, _vp]),
+    "moe_gmm_ex": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp,
+                                  ctypes.c_int, ctypes.c_int, _vp]),
+    "moe_combine": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _i32, _i32, _i32, _vp,
+                                   ctypes.c_int, _vp]),
+    "moe_mxfp4_to_nvfp4": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "moe_debug_decode": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp]),
+}
+
+
+class MoeGmmError(RuntimeError):
+    pass
+
+
+def library():
+    """The loaded libmoegmm.so (ctypes.CDLL).  torch is imported first so the
+    library binds to the HIP runtime torch already loaded."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise MoeGmmError(
+                "libmoegmm.so is not built (%s); run python -m moe_grouped_gemm_route_amd.build"
+                % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        msg = library().moe_status_string(status).decode()
+        raise MoeGmmError("libmoegmm status %d: %s" % (status, msg))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype, name, ndim=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise MoeGmmError("%s must be a CUDA (HIP) tensor" % name)
+    if t.dtype != dtype:
+        raise MoeGmmError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise MoeGmmError("%s must be contiguous" % name)
+    if ndim is not None and t.dim() != ndim:
+        raise MoeGmmError("%s must have %d dims" % (name, ndim))
+    return t
+
+
+def _bits16(t, name):
+    """bf16 tensors (or their uint16/int16 bit views) as a 16-bit view."""
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    if t.dtype == torch.uint16:
+        t = t.view(torch.int16)
+    return _dev(t, torch.int16, name)
+
+
+def route_sort(topk_ids, E):
+    """moe_route_sort.  topk_ids [T, k] int32 -> dict of int32 tensors
+    group_offsets [E+1], sorted_token, sorted_pair, pair_row [T*k] and
+    err_count [1]."""
+    _dev(topk_ids, torch.int32, "topk_ids", 2)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    out = {
+        "group_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "sorted_token": torch.empty(T * k, dtype=torch.int32, device=dev),
+        "sorted_pair": torch.empty(T * k, dtype=torch.int32, device=dev),
+        "pair_row": torch.empty(T * k, dtype=torch.int32, device=dev),
+        "err_count": torch.empty(1, dtype=torch.int32, device=dev),
+    }
+    _check(library().moe_route_sort(
+        _ptr(topk_ids), T, k, E, _ptr(out["group_offsets"]), _ptr(out["sorted_token"]),
+        _ptr(out["sorted_pair"]), _ptr(out["pair_row"]), _ptr(out["err_count"]), _stream()))
+    return out
+
+
+def packed_weight_bytes(fmt, E, N, K):
+    n = library().moe_packed_weight_bytes(fmt, E, N, K)
+    if n == 0:
+        raise MoeGmmError("unsupported weight shape E=%d N=%d K=%d" % (E, N, K))
+    return n
+
+
+def mxfp4_encode(codes, scales, tensor_scale=None, fmt=MXFP4):
+    """mxfp4_encode.  codes [E, N, K/2] uint8, scales [E, N, K/32] (MXFP4) or
+    [E, N, K/16] (NVFP4) uint8, tensor_scale [E] float32 (NVFP4 only).
+    Returns the packed uint8 buffer."""
+    _dev(codes, torch.uint8, "codes", 3)
+    _dev(scales, torch.uint8, "scales", 3)
+    E, N, K2 = codes.shape
+    K = 2 * K2
+    per = 32 if fmt == MXFP4 else 16
+    if tuple(scales.shape) != (E, N, K // per):
+        raise MoeGmmError("scales must be [E, N, K/%d]" % per)
+    if fmt == NVFP4:
+        _dev(tensor_scale, torch.float32, "tensor_scale", 1)
+    packed = torch.empty(packed_weight_bytes(fmt, E, N, K), dtype=torch.uint8, device=codes.device)
+    _check(library().mxfp4_encode(fmt, _ptr(codes), _ptr(scales), _ptr(tensor_scale), E, N, K,
+                                  _ptr(packed), _stream()))
+    return packed
+
+
+def moe_gmm(packed, fmt, E, N, K, x, group_offsets, M, row_index=None, out_dtype=F32,
+            kernel=GMM_AUTO, out=None):
+    """moe_gmm_ex.  x: bf16 [T, K] (gathered through row_index) or [M, K].
+    Returns y [M, N] float32 or bfloat16."""
+    _dev(packed, torch.uint8, "packed", 1)
+    xb = _bits16(x, "x")
+    _dev(group_offsets, torch.int32, "group_offsets", 1)
+    if group_offsets.numel() != E + 1:
+        raise MoeGmmError("group_offsets must have E+1 entries")
+    if xb.dim() != 2 or xb.shape[1] != K:
+        raise MoeGmmError("x must be [rows, K]")
+    if row_index is None:
+        if xb.shape[0] < M:
+            raise MoeGmmError("x must have M rows when row_index is None")
+    else:
+        _dev(row_index, torch.int32, "row_index", 1)
+        if row_index.numel() < M:
+            raise MoeGmmError("row_index must have M entries")
+    if packed.numel() < packed_weight_bytes(fmt, E, N, K):
+        raise MoeGmmError("packed buffer too small")
+    dt = torch.float32 if out_dtype == F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, N), dtype=dt, device=packed.device)
+    else:
+        _dev(out, dt, "out", 2)
+        if tuple(out.shape) != (M, N):
+            raise MoeGmmError("out must be [M, N]")
+    _check(library().moe_gmm_ex(_ptr(packed), fmt, E, N, K, _ptr(xb), _ptr(row_index),
+                                _ptr(group_offsets), M, _ptr(out), out_dtype, kernel, _stream()))
+    return out
+
+
+def moe_combine(y, topk_weights, pair_row, out_dtype=F32):
+    """moe_combine.  y [rows, N] float32/bfloat16, topk_weights [T, k] float32,
+    pair_row [T*k] int32 -> out [T, N]."""
+    if y.dtype not in (torch.float32, torch.bfloat16):
+        raise MoeGmmError("y must be float32 or bfloat16")
+    _dev(y, y.dtype, "y", 2)
+    _dev(topk_weights, torch.float32, "topk_weights", 2)
+    _dev(pair_row, torch.int32, "pair_row", 1)
+    T, k = topk_weights.shape
+    N = y.shape[1]
+    if pair_row.numel() != T * k:
+        raise MoeGmmError("pair_row must have T*k entries")
+    dt = torch.float32 if out_dtype == F32 else torch.bfloat16
+    out = torch.empty((T, N), dtype=dt, device=y.device)
+    _check(library().moe_combine(_ptr(y), F32 if y.dtype == torch.float32 else BF16,
+                                 _ptr(topk_weights), _ptr(pair_row), T, k, N, _ptr(out),
+                                 out_dtype, _stream()))
+    return out
+
+
+def mxfp4_to_nvfp4(scales):
+    """moe_mxfp4_to_nvfp4.  scales [E, N, K/32] uint8 E8M0 ->
+    (block_scales [E, N, K/16] uint8 E4M3, tensor_scale [E] float32,
+    err_count [1] int32)."""
+    _dev(scales, torch.uint8, "scales", 3)
+    E, N, KB = scales.shape
+    bs = torch.empty((E, N, 2 * KB), dtype=torch.uint8, device=scales.device)
+    ts = torch.empty(E, dtype=torch.float32, device=scales.device)
+    err = torch.empty(1, dtype=torch.int32, device=scales.device)
+    _check(library().moe_mxfp4_to_nvfp4(_ptr(scales), E, N, 32 * KB, _ptr(bs), _ptr(ts),
+                                        _ptr(err), _stream()))
+    return bs, ts, err
+
+
+def debug_decode(packed, fmt, E, N, K):
+    """moe_debug_decode -> dense bf16 bit patterns [E, N, K] (int16 view)."""
+    _dev(packed, torch.uint8, "packed", 1)
+    w = torch.empty((E, N, K), dtype=torch.int16, device=packed.device)
+    _check(library().moe_debug_decode(_ptr(packed), fmt, E, N, K, _ptr(w), _stream()))
+    return w

@@ -1,0 +1,135 @@
+// C ABI of libmoegmm.so (declared in include/moe_gmm.h): host-side argument
+// checks, kernel-configuration choice, and the launches.  Every check runs
+// before the first HIP call, so a rejected call enqueues nothing.
+#include "moe_gmm.h"
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxRows = int64_t(1) << 24;
+constexpr int64_t kMaxCodeBytes = int64_t(1) << 40;
+
+bool fmt_ok(int fmt) { return fmt == MOE_W_MXFP4 || fmt == MOE_W_NVFP4; }
+bool dtype_ok(int d) { return d == MOE_F32 || d == MOE_BF16; }
+
+// Weight sizes the packed layout and the kernels support.
+int check_weight_shape(int fmt, int32_t E, int32_t N, int32_t K) {
+  if (!fmt_ok(fmt)) return MOE_ERR_FORMAT;
+  if (E < 1 || N < 1 || K < 1) return MOE_ERR_SHAPE;
+  if (K % 128 != 0 || N % 64 != 0) return MOE_ERR_SHAPE;
+  if ((int64_t)E * N * (K / 2) >= kMaxCodeBytes) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "unsupported or inconsistent sizes";
+    case MOE_ERR_FORMAT: return "unknown weight format or dtype";
+    case MOE_ERR_UNSUPPORTED: return "not supported by this build";
+    case MOE_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int moe_route_sort(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                   int32_t* group_offsets, int32_t* sorted_token, int32_t* sorted_pair,
+                   int32_t* pair_row, int32_t* err_count, void* stream) {
+  if (!topk_ids || !group_offsets || !sorted_token || !sorted_pair || !pair_row) return MOE_ERR_NULL;
+  if (T < 1 || k < 1 || E < 1 || E > 1024) return MOE_ERR_SHAPE;
+  if ((int64_t)T * k > kMaxRows) return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_route_sort(topk_ids, T, k, E, group_offsets, sorted_token,
+                                           sorted_pair, pair_row, err_count,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_packed_weight_bytes(int fmt, int32_t E, int32_t N, int32_t K) {
+  if (check_weight_shape(fmt, E, N, K) != MOE_OK) return 0;
+  return (size_t)moe::make_layout(fmt, E, N, K).total_bytes;
+}
+
+int mxfp4_encode(int fmt, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                 int32_t E, int32_t N, int32_t K, void* packed, void* stream) {
+  const int st = check_weight_shape(fmt, E, N, K);
+  if (st != MOE_OK) return st;
+  if (!codes || !scales || !packed) return MOE_ERR_NULL;
+  if (fmt == MOE_W_NVFP4 && !tensor_scale) return MOE_ERR_NULL;
+  if (fmt == MOE_W_MXFP4 && tensor_scale) return MOE_ERR_FORMAT;
+  if (((uintptr_t)codes & 15) || ((uintptr_t)packed & 255)) return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_encode(fmt, codes, scales, tensor_scale, E, N, K,
+                                       static_cast<uint8_t*>(packed),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int moe_gmm_ex(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint16_t* x,
+               const int32_t* row_index, const int32_t* group_offsets, int32_t M, void* y,
+               int y_dtype, int kernel, void* stream) {
+  const int st = check_weight_shape(fmt, E, N, K);
+  if (st != MOE_OK) return st;
+  if (!dtype_ok(y_dtype)) return MOE_ERR_FORMAT;
+  if (kernel < MOE_GMM_AUTO || kernel > MOE_GMM_TILED) return MOE_ERR_FORMAT;
+  if (!packed || !x || !group_offsets || !y) return MOE_ERR_NULL;
+  if (M < 1 || M > kMaxRows) return MOE_ERR_SHAPE;
+  if (((uintptr_t)packed & 255) || ((uintptr_t)x & 15)) return MOE_ERR_SHAPE;
+  if (kernel == MOE_GMM_AUTO) {
+    // Bands averaging 32 rows or more keep the matrix cores busy enough for
+    // the LDS-tiled kernel; thinner bands are pure weight streaming.
+    kernel = ((int64_t)M >= 32 * (int64_t)E) ? MOE_GMM_TILED : MOE_GMM_STREAM;
+  }
+  return hip_status(moe::launch_gmm(static_cast<const uint8_t*>(packed), fmt, E, N, K, x,
+                                    row_index, group_offsets, M, y, y_dtype == MOE_BF16, kernel,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int moe_gmm(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint16_t* x,
+            const int32_t* row_index, const int32_t* group_offsets, int32_t M, void* y,
+            int y_dtype, void* stream) {
+  return moe_gmm_ex(packed, fmt, E, N, K, x, row_index, group_offsets, M, y, y_dtype,
+                    MOE_GMM_AUTO, stream);
+}
+
+int moe_combine(const void* y, int y_dtype, const float* topk_weights, const int32_t* pair_row,
+                int32_t T, int32_t k, int32_t N, void* out, int out_dtype, void* stream) {
+  if (!dtype_ok(y_dtype) || !dtype_ok(out_dtype)) return MOE_ERR_FORMAT;
+  if (!y || !topk_weights || !pair_row || !out) return MOE_ERR_NULL;
+  if (T < 1 || k < 1 || k > 64 || N < 4 || N % 4 != 0) return MOE_ERR_SHAPE;
+  if ((int64_t)T * k > kMaxRows || (int64_t)T * N >= (int64_t(1) << 40)) return MOE_ERR_SHAPE;
+  if (((uintptr_t)y & 15) || ((uintptr_t)out & 15)) return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_combine(y, y_dtype == MOE_BF16, topk_weights, pair_row, T, k, N,
+                                        out, out_dtype == MOE_BF16,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int moe_mxfp4_to_nvfp4(const uint8_t* scales, int32_t E, int32_t N, int32_t K,
+                       uint8_t* block_scales, float* tensor_scale, int32_t* err_count,
+                       void* stream) {
+  if (!scales || !block_scales || !tensor_scale) return MOE_ERR_NULL;
+  if (E < 1 || N < 1 || K < 32 || K % 32 != 0) return MOE_ERR_SHAPE;
+  if ((int64_t)N * (K / 32) >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  if ((uintptr_t)block_scales & 1) return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_mxfp4_to_nvfp4(scales, E, N, K, block_scales, tensor_scale,
+                                               err_count, static_cast<hipStream_t>(stream)));
+}
+
+int moe_debug_decode(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
+                     uint16_t* w_bf16, void* stream) {
+  const int st = check_weight_shape(fmt, E, N, K);
+  if (st != MOE_OK) return st;
+  if (!packed || !w_bf16) return MOE_ERR_NULL;
+  if (((uintptr_t)packed & 255) || ((uintptr_t)w_bf16 & 1)) return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_debug_decode(static_cast<const uint8_t*>(packed), fmt, E, N, K,
+                                             w_bf16, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Device-side definitions shared by the gfx950 kernels: vector types, the
+// packed weight layout, and the exact e2m1 -> bf16 decode.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Packed weight layout (written once by mxfp4_encode, streamed by moe_gmm).
+//
+// The canonical weight is [E, N, K/2] bytes: for column n, the 32 codes of
+// scale block kb (K indices kb*32 .. kb*32+31) are 16 contiguous bytes.  The
+// packed layout keeps those 16-byte runs whole and only reorders them so that
+// one wave's 16-byte-per-lane load is one contiguous 1 KiB:
+//
+//   chunk (e, nt, kc) = 1 KiB  covers columns nt*16 .. +16 and K indices
+//                               kc*128 .. +128 (four scale blocks);
+//   lane l of that chunk holds column nt*16 + (l & 15), scale block
+//   kc*4 + (l >> 4): exactly one MX block, so one scale per lane per chunk.
+//
+// Scales follow the codes.  MXFP4: for each (e, nt) and group of four chunks
+// a 256-byte record in which lane l's dword holds the E8M0 byte of its block
+// for chunks 4q .. 4q+3 (byte i = chunk 4q+i).  NVFP4: 256-byte records per
+// pair of chunks; lane l's dword holds, for chunk 2q+c, the E4M3 bytes of the
+// low and high 16-halves of its block at bytes 2c and 2c+1.  Missing chunks
+// of the last record are zero.  NVFP4 appends E floats of tensor scales.
+// ---------------------------------------------------------------------------
+struct Layout {
+  int64_t E, N, K;
+  int64_t NT, KC, KB;     // 16-column tiles, 128-deep chunks, 32-blocks
+  int64_t groups;         // scale records per (e, nt)
+  int64_t codes_bytes, scales_off, scales_bytes, tscale_off, total_bytes;
+};
+
+__host__ __device__ inline Layout make_layout(int fmt, int64_t E, int64_t N, int64_t K) {
+  Layout L;
+  L.E = E; L.N = N; L.K = K;
+  L.NT = N / 16; L.KC = K / 128; L.KB = K / 32;
+  const int64_t per = fmt == 0 ? 4 : 2;   // chunks per 256-byte scale record
+  L.groups = (L.KC + per - 1) / per;
+  L.codes_bytes = E * N * K / 2;
+  L.scales_off = L.codes_bytes;
+  L.scales_bytes = E * L.NT * L.groups * 256;
+  L.tscale_off = L.scales_off + L.scales_bytes;
+  L.total_bytes = L.tscale_off + (fmt == 0 ? 0 : ((E * 4 + 255) / 256) * 256);
+  return L;
+}
+
+// Byte offset of the 16-byte code run of (e, column n, scale block kb).
+__host__ __device__ inline int64_t code_run_offset(const Layout& L, int64_t e, int64_t n, int64_t kb) {
+  const int64_t nt = n >> 4, kc = kb >> 2;
+  const int64_t lane = ((kb & 3) << 4) | (n & 15);
+  return (((e * L.NT + nt) * L.KC + kc) << 10) + (lane << 4);
+}
+
+// ---------------------------------------------------------------------------
+// Exact decode.  v_cvt_scalef32_pk_bf16_fp4 turns the two e2m1 codes of one
+// byte into two bf16 values times an f32 scale (low nibble -> element 0).
+// An e2m1 value has at most two significant bits, so value * 2^k is exact in
+// bf16 while it stays normal; value * E4M3 has at most six significant bits
+// and is exact as well.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bf16x8_t decode8(uint32_t codes8, float scale) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes8, scale, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes8, scale, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes8, scale, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes8, scale, 3);
+  return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// E8M0 byte b (1..254) -> 2^(b - 127) as f32, by placing b in the exponent.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  return __uint_as_float(b << 23);
+}
+
+// E4M3FN byte (selected byte of a dword) -> f32.
+template <int SEL>
+__device__ __forceinline__ float e4m3_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8(w, SEL);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+  // NaN stays NaN (quiet) instead of rounding into infinity.
+  return (u & 0x7FFFFFFFu) > 0x7F800000u ? (uint16_t)((u >> 16) | 0x40u) : (uint16_t)(r >> 16);
+}
+
+}  // namespace moe

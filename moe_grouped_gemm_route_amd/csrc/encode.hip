@@ -1,0 +1,187 @@
+// Load-time weight repack (mxfp4_encode), its inverse check
+// (moe_debug_decode) and the lossless MXFP4 -> NVFP4 scale cast.
+//
+// "Running DeepSeek V4 Flash on TPU v6", section "1. Four bits that v6e can't
+// hold": the weights are re-laid-out once at load and stay 4 bits each.  Here
+// the repack moves whole 16-byte code runs (one column x one 32-block) into
+// the chunk order of the packed layout (common.h) and regroups scale bytes.
+// "DeepSeek-V4-Flash-0731-NVFP4", section "The lossless weight cast": the
+// per-expert tensor scale 2^(k_max - 8) and per-16 E4M3 scales
+// 2^(k_j - k_max + 8).
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+// One thread per 16-byte code run, in canonical order (coalesced reads).
+__global__ __launch_bounds__(256) void encode_codes_kernel(const u32x4_t* __restrict__ codes,
+                                                           Layout L, uint8_t* __restrict__ packed) {
+  const int64_t runs = L.E * L.N * L.KB;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < runs;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t kb = i % L.KB;
+    const int64_t n = (i / L.KB) % L.N;
+    const int64_t e = i / (L.KB * L.N);
+    *reinterpret_cast<u32x4_t*>(packed + code_run_offset(L, e, n, kb)) = codes[i];
+  }
+}
+
+// One thread per packed scale dword (lane l of record (e, nt, q)).
+__global__ __launch_bounds__(256) void encode_scales_kernel(int fmt, const uint8_t* __restrict__ scales,
+                                                            const float* __restrict__ tscale, Layout L,
+                                                            uint8_t* __restrict__ packed) {
+  const int64_t words = L.E * L.NT * L.groups * 64;
+  uint32_t* out = reinterpret_cast<uint32_t*>(packed + L.scales_off);
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < words;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t lane = i & 63;
+    const int64_t q = (i >> 6) % L.groups;
+    const int64_t nt = (i >> 6) / L.groups % L.NT;
+    const int64_t e = (i >> 6) / (L.groups * L.NT);
+    const int64_t n = nt * 16 + (lane & 15);
+    uint32_t word = 0;
+    if (fmt == 0) {
+      for (int c = 0; c < 4; ++c) {
+        const int64_t kc = q * 4 + c;
+        if (kc < L.KC) {
+          const int64_t kb = kc * 4 + (lane >> 4);
+          word |= (uint32_t)scales[(e * L.N + n) * L.KB + kb] << (8 * c);
+        }
+      }
+    } else {
+      for (int c = 0; c < 2; ++c) {
+        const int64_t kc = q * 2 + c;
+        if (kc < L.KC) {
+          const int64_t kb = kc * 4 + (lane >> 4);
+          const uint8_t* s = scales + (e * L.N + n) * (L.KB * 2) + kb * 2;
+          word |= ((uint32_t)s[0] | ((uint32_t)s[1] << 8)) << (16 * c);
+        }
+      }
+    }
+    out[i] = word;
+  }
+  if (fmt == 1) {
+    float* ts = reinterpret_cast<float*>(packed + L.tscale_off);
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < L.E;
+         e += (int64_t)gridDim.x * blockDim.x)
+      ts[e] = tscale[e];
+  }
+}
+
+hipError_t launch_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
+                         const float* tensor_scale, int32_t E, int32_t N, int32_t K,
+                         uint8_t* packed, hipStream_t stream) {
+  const Layout L = make_layout(fmt, E, N, K);
+  const int64_t runs = L.E * L.N * L.KB;
+  const int grid_c = (int)((runs + 255) / 256 < 65536 ? (runs + 255) / 256 : 65536);
+  hipLaunchKernelGGL(encode_codes_kernel, dim3(grid_c), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4_t*>(codes), L, packed);
+  const int64_t words = L.E * L.NT * L.groups * 64;
+  const int grid_s = (int)((words + 255) / 256 < 65536 ? (words + 255) / 256 : 65536);
+  hipLaunchKernelGGL(encode_scales_kernel, dim3(grid_s), dim3(256), 0, stream, fmt, scales,
+                     tensor_scale, L, packed);
+  return hipGetLastError();
+}
+
+// Dense bf16 [E, N, K] from the packed buffer: one thread per code run.
+__global__ __launch_bounds__(256) void debug_decode_kernel(const uint8_t* __restrict__ packed, int fmt,
+                                                           Layout L, uint16_t* __restrict__ w) {
+  const int64_t runs = L.E * L.N * L.KB;
+  const uint32_t* sw = reinterpret_cast<const uint32_t*>(packed + L.scales_off);
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < runs;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t kb = i % L.KB;
+    const int64_t n = (i / L.KB) % L.N;
+    const int64_t e = i / (L.KB * L.N);
+    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(packed + code_run_offset(L, e, n, kb));
+    const int64_t nt = n >> 4, kc = kb >> 2;
+    const int64_t lane = ((kb & 3) << 4) | (n & 15);
+    float s_lo, s_hi;
+    if (fmt == 0) {
+      const uint32_t word = sw[((e * L.NT + nt) * L.groups + (kc >> 2)) * 64 + lane];
+      s_lo = s_hi = e8m0_to_f32((word >> (8 * (kc & 3))) & 0xFF);
+    } else {
+      const uint32_t word = sw[((e * L.NT + nt) * L.groups + (kc >> 1)) * 64 + lane];
+      const uint32_t pair = (word >> (16 * (kc & 1))) & 0xFFFF;
+      s_lo = e4m3_to_f32<0>(pair);
+      s_hi = e4m3_to_f32<1>(pair);
+    }
+    uint16_t* dst = w + i * 32;
+    for (int d = 0; d < 4; ++d) {
+      const bf16x8_t v = decode8(c[d], d < 2 ? s_lo : s_hi);
+      for (int j = 0; j < 8; ++j) dst[d * 8 + j] = __builtin_bit_cast(uint16_t, v[j]);
+    }
+  }
+}
+
+hipError_t launch_debug_decode(const uint8_t* packed, int fmt, int32_t E, int32_t N, int32_t K,
+                               uint16_t* w, hipStream_t stream) {
+  const Layout L = make_layout(fmt, E, N, K);
+  const int64_t runs = L.E * L.N * L.KB;
+  const int grid = (int)((runs + 255) / 256 < 65536 ? (runs + 255) / 256 : 65536);
+  hipLaunchKernelGGL(debug_decode_kernel, dim3(grid), dim3(256), 0, stream, packed, fmt, L, w);
+  return hipGetLastError();
+}
+
+// Clears a small int32 counter with a kernel (kept out of memset nodes so the
+// call stays safe to record into a HIP graph).
+__global__ void zero_i32_kernel(int32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+// Lossless scale cast: one workgroup per expert.  Pass 1 finds the largest
+// block exponent; pass 2 writes both 16-half E4M3 bytes of every block.
+__global__ __launch_bounds__(256) void mxfp4_to_nvfp4_kernel(const uint8_t* __restrict__ scales,
+                                                             int64_t per_expert,
+                                                             uint8_t* __restrict__ bs,
+                                                             float* __restrict__ ts,
+                                                             int32_t* __restrict__ err_count) {
+  __shared__ int s_max;
+  __shared__ int s_bad;
+  const int64_t e = blockIdx.x;
+  const uint8_t* src = scales + e * per_expert;
+  if (threadIdx.x == 0) { s_max = 0; s_bad = 0; }
+  __syncthreads();
+  int mx = 0, bad = 0;
+  for (int64_t i = threadIdx.x; i < per_expert; i += blockDim.x) {
+    const int b = src[i];
+    if (b == 255) ++bad;
+    else mx = mx > b ? mx : b;
+  }
+  atomicMax(&s_max, mx);
+  __syncthreads();
+  const int bmax = s_max;           // biased k_max
+  uint16_t* dst = reinterpret_cast<uint16_t*>(bs + e * per_expert * 2);
+  for (int64_t i = threadIdx.x; i < per_expert; i += blockDim.x) {
+    const int b = src[i];
+    const int p = b - bmax + 8;     // power of two of the block scale
+    uint32_t byte;
+    if (b == 255 || p < -9) {
+      byte = 0;
+      if (b != 255) ++bad;
+    } else if (p >= -6) {
+      byte = (uint32_t)(p + 7) << 3;            // normal: exponent field p + 7
+    } else {
+      byte = 1u << (p + 9);                     // subnormal: mantissa 2^(p + 9)
+    }
+    dst[i] = (uint16_t)(byte | (byte << 8));
+  }
+  if (bad) atomicAdd(&s_bad, bad);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ts[e] = __uint_as_float((uint32_t)(bmax - 8) << 23);
+    if (err_count && s_bad) atomicAdd(err_count, s_bad);
+  }
+}
+
+hipError_t launch_mxfp4_to_nvfp4(const uint8_t* scales, int32_t E, int32_t N, int32_t K,
+                                 uint8_t* block_scales, float* tensor_scale, int32_t* err_count,
+                                 hipStream_t stream) {
+  const int64_t per_expert = (int64_t)N * (K / 32);
+  if (err_count) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, stream, err_count, 1);
+  hipLaunchKernelGGL(mxfp4_to_nvfp4_kernel, dim3(E), dim3(256), 0, stream, scales, per_expert,
+                     block_scales, tensor_scale, err_count);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,458 @@
+// moe_gmm: routed-expert grouped matmul, W4A16 on bf16 MFMA (gfx950).
+//
+// "Running DeepSeek V4 Flash on TPU v6", section "1. Four bits that v6e can't
+// hold": the grid walks (expert, M-tile) x N-tile pairs over the expert
+// bands, the inner loop walks K, each 4-bit weight tile is decoded to bf16 as
+// soon as it is on chip, multiplied by its block scale, and accumulated in an
+// f32 tile that never leaves the chip; ragged and empty bands are handled.
+// Section "Grouped matmul performance vs bf16": the NVFP4 variant reads
+// per-16 E4M3 block scales (and a per-expert tensor scale, applied here in
+// the epilogue).
+//
+// MFMA mapping.  v_mfma_f32_16x16x32_bf16 multiplies a 16x32 A fragment by a
+// 32x16 B fragment; lane l supplies row (l & 15) of A and column (l & 15) of
+// B for eight K slots picked by l >> 4, and both operands use the same slots,
+// so any fixed assignment of K indices to (lane group, slot) gives the same
+// dot products.  We assign lane group g, step s, slot i to
+//     k = chunk*128 + g*32 + s*8 + i,
+// so over the four steps of a 128-deep chunk one lane consumes one whole
+// 32-element scale block of its column: one 16-byte load of codes and one
+// scale per lane per chunk, and 64 contiguous activation bytes per row.
+//
+// Both kernels below issue, for every output element, the same MFMAs in the
+// same order (chunks ascending, steps 0..3), so they return identical bits.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+struct Tile {
+  int e;      // expert, or -1 past the last tile
+  int m0;     // first band row of the tile
+  int rows;   // valid rows in the tile (1..BM)
+};
+
+// Per-wave view of the tile list "for each expert e, ceil(count_e / BM)
+// tiles": lane l covers experts [l*per, l*per + per) and holds the number of
+// tiles before them (excl) and up to their end (incl).  total is uniform.
+struct TileScan {
+  int per, excl, incl, total;
+};
+
+__device__ __forceinline__ TileScan scan_tiles(const int32_t* __restrict__ goff, int E, int BM) {
+  const int lane = threadIdx.x & 63;
+  TileScan ts;
+  ts.per = (E + 63) >> 6;
+  const int e0 = lane * ts.per;
+  int mine = 0;
+  for (int i = 0; i < ts.per; ++i) {
+    const int e = e0 + i;
+    if (e < E) mine += (goff[e + 1] - goff[e] + BM - 1) / BM;
+  }
+  int incl = mine;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  ts.excl = incl - mine;
+  ts.incl = incl;
+  ts.total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
+  return ts;
+}
+
+// Tile t (< ts.total) of the list, found by every lane of the wave.
+__device__ __forceinline__ Tile locate_tile(const int32_t* __restrict__ goff, int E, int BM,
+                                            const TileScan& ts, int t) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t hit = __ballot(ts.excl <= t && t < ts.incl);
+  const int src = __ffsll((unsigned long long)hit) - 1;
+  int fe = -1, fm0 = 0, frows = 0;
+  if (lane == src) {
+    int acc = ts.excl;
+    for (int i = 0; i < ts.per; ++i) {
+      const int e = lane * ts.per + i;
+      if (e >= E) break;
+      const int c = goff[e + 1] - goff[e];
+      const int nt = (c + BM - 1) / BM;
+      if (t < acc + nt) {
+        const int j = t - acc;
+        fe = e;
+        fm0 = goff[e] + j * BM;
+        frows = c - j * BM < BM ? c - j * BM : BM;
+        break;
+      }
+      acc += nt;
+    }
+  }
+  Tile out;
+  out.e = __builtin_amdgcn_readfirstlane(__shfl(fe, src, 64));
+  out.m0 = __builtin_amdgcn_readfirstlane(__shfl(fm0, src, 64));
+  out.rows = __builtin_amdgcn_readfirstlane(__shfl(frows, src, 64));
+  return out;
+}
+
+// Work item of this workgroup among G = tiles * NB real items, or -1.  With
+// xcd_order, consecutive workgroup ids (which the dispatcher deals round-robin
+// to the 8 XCDs) are remapped so that each XCD walks one contiguous run of
+// items: the N tiles of one M tile then share that XCD's L2.
+__device__ __forceinline__ int work_item(int G, bool xcd_order) {
+  const int bx = blockIdx.x;
+  if (bx >= G) return -1;
+  if (!xcd_order) return bx;
+  const int x = bx & 7, idx = bx >> 3;
+  const int q = G >> 3, rem = G & 7;
+  return x * q + (x < rem ? x : rem) + idx;
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Block scales of one lane for chunk kc.  MXFP4: one E8M0 byte for the whole
+// block; NVFP4: E4M3 bytes of the low (steps 0, 1) and high (2, 3) halves.
+template <int FMT>
+__device__ __forceinline__ void chunk_scales(uint32_t word, int kc, float& lo, float& hi) {
+  if (FMT == 0) {
+    lo = hi = e8m0_to_f32((word >> (8 * (kc & 3))) & 0xFFu);
+  } else {
+    const uint32_t pair = (kc & 1) ? (word >> 16) : word;
+    lo = e4m3_to_f32<0>(pair);
+    hi = e4m3_to_f32<1>(pair);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ bool new_scale_record(int kc) {
+  return FMT == 0 ? (kc & 3) == 0 : (kc & 1) == 0;
+}
+
+template <int FMT>
+__device__ __forceinline__ int scale_record(int kc) {
+  return FMT == 0 ? (kc >> 2) : (kc >> 1);
+}
+
+// Stores the f32 accumulator of one 16x16 MFMA tile: lane l holds column
+// (l & 15), rows 4*(l >> 4) .. +3.
+template <bool OBF16>
+__device__ __forceinline__ void store_tile(void* y, int64_t N, int row0, int rows_valid, int col,
+                                           f32x4_t acc, float post) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = 4 * g + i;
+    if (rl < rows_valid) {
+      const float v = acc[i] * post;
+      const int64_t off = (int64_t)(row0 + rl) * N + col;
+      if (OBF16) reinterpret_cast<uint16_t*>(y)[off] = f32_to_bf16_rne(v);
+      else reinterpret_cast<float*>(y)[off] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weight-streaming kernel, for bands of a few rows (decode).  Each wave owns
+// NS 16-column subtiles and all 16*MS rows of its tile; there is no LDS and
+// no barrier.  Codes are double-buffered in registers one chunk ahead.
+// Activation fragments come straight from global memory (they are tiny and
+// shared by every N tile, so they live in L2).
+// ---------------------------------------------------------------------------
+template <int MS, int NS, int FMT, bool OBF16>
+__global__ __launch_bounds__(256) void gmm_stream_kernel(const uint8_t* __restrict__ packed, Layout L,
+                                                         const uint16_t* __restrict__ x,
+                                                         const int32_t* __restrict__ row_index,
+                                                         const int32_t* __restrict__ goff, int E,
+                                                         void* __restrict__ y, int NB) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const TileScan ts = scan_tiles(goff, E, 16 * MS);
+  const int item = work_item(ts.total * NB, false);
+  if (item < 0) return;
+  const int t = item / NB;
+  const int nb = item - t * NB;
+  const Tile tile = locate_tile(goff, E, 16 * MS, ts, t);
+  const int n0 = (nb * 4 + wave) * NS * 16;
+  if (n0 >= L.N) return;
+  const int K = (int)L.K;
+  const int KC = (int)L.KC;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int nsub = (tile.rows + 15) >> 4;
+
+  const u32x4_t* xp[MS];
+  bool xv[MS];
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) {
+    const int rl = ms * 16 + r;
+    xv[ms] = rl < tile.rows;
+    const int row = tile.m0 + (xv[ms] ? rl : 0);
+    const int64_t src = row_index ? row_index[row] : row;
+    xp[ms] = reinterpret_cast<const u32x4_t*>(x + src * K + g * 32);
+  }
+  const u32x4_t* cp[NS];
+  const uint32_t* sp[NS];
+#pragma unroll
+  for (int ns = 0; ns < NS; ++ns) {
+    const int64_t et = (int64_t)tile.e * L.NT + (n0 >> 4) + ns;
+    cp[ns] = reinterpret_cast<const u32x4_t*>(packed + ((et * L.KC) << 10)) + lane;
+    sp[ns] = reinterpret_cast<const uint32_t*>(packed + L.scales_off) + et * L.groups * 64 + lane;
+  }
+
+  f32x4_t acc[MS][NS];
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  u32x4_t cnext[NS];
+#pragma unroll
+  for (int ns = 0; ns < NS; ++ns) cnext[ns] = __builtin_nontemporal_load(cp[ns]);
+  uint32_t sw[NS];
+
+  for (int kc = 0; kc < KC; ++kc) {
+    u32x4_t c[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) c[ns] = cnext[ns];
+    if (kc + 1 < KC) {
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) cnext[ns] = __builtin_nontemporal_load(cp[ns] + (kc + 1) * 64);
+    }
+    if (new_scale_record<FMT>(kc)) {
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) sw[ns] = sp[ns][scale_record<FMT>(kc) * 64];
+    }
+    u32x4_t a[MS][4];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+      if (ms < nsub) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          a[ms][s] = xv[ms] ? xp[ms][kc * 16 + s] : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+    float lo[NS], hi[NS];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) chunk_scales<FMT>(sw[ns], kc, lo[ns], hi[ns]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t b[NS];
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns) b[ns] = decode8(c[ns][s], s < 2 ? lo[ns] : hi[ns]);
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) {
+        if (ms < nsub) {
+#pragma unroll
+          for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = mfma(as_bf16x8(a[ms][s]), b[ns], acc[ms][ns]);
+        }
+      }
+    }
+  }
+
+  const float post = FMT == 1 ? reinterpret_cast<const float*>(packed + L.tscale_off)[tile.e] : 1.0f;
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) {
+    if (ms < nsub) {
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+        store_tile<OBF16>(y, L.N, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + ns * 16 + r,
+                          acc[ms][ns], post);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LDS-tiled kernel, for bands of many rows (prefill).  A workgroup of four
+// waves owns a 128-row tile and 256 columns; wave w owns columns 64w..64w+63
+// (four 16-column subtiles) for all 128 rows, so every decoded weight feeds
+// eight MFMAs.  The activation tile of each 128-deep chunk (gathered rows) is
+// copied HBM -> LDS by direct-to-LDS 16-byte loads (no staging registers),
+// double-buffered.  A staged row is 256 bytes with its 16-byte segments
+// XOR-swizzled by (row & 15), so the 16 rows read by one fragment load hit 16
+// different bank groups.  Codes stream into registers one chunk ahead.
+// 16-row subtiles past the band end are skipped.
+// ---------------------------------------------------------------------------
+constexpr int TL_MS = 8;                    // 16-row subtiles per tile
+constexpr int TL_NS = 4;                    // 16-column subtiles per wave
+constexpr int TL_BM = 16 * TL_MS;           // 128
+constexpr int TL_BN = 4 * 16 * TL_NS;       // 256
+constexpr int TL_ROW_BYTES = 128 * 2;       // one staged row of a chunk
+constexpr int TL_BUF_BYTES = TL_BM * TL_ROW_BYTES;
+constexpr int TL_LOADS = TL_BUF_BYTES / 1024 / 4;   // 1 KiB wave loads per wave per chunk
+
+// Copies the activation chunk kc into an LDS buffer.  Load j of wave w fills
+// LDS bytes [(8w + j) KiB, +1 KiB): rows 4(8w + j) .. +3, lane l landing at
+// byte 16 l, i.e. row 4(8w + j) + l/16, physical segment l & 15, which holds
+// logical segment (l & 15) ^ (row & 15).
+__device__ __forceinline__ void stage_chunk(uint8_t* buf, const uint8_t* const (&ap)[TL_LOADS],
+                                            const bool (&av)[TL_LOADS], int kc, int wave) {
+#pragma unroll
+  for (int j = 0; j < TL_LOADS; ++j) {
+    if (av[j])
+      __builtin_amdgcn_global_load_lds(ap[j] + kc * 256, buf + (wave * TL_LOADS + j) * 1024, 16, 0, 0);
+  }
+}
+
+template <int FMT, bool OBF16>
+__global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __restrict__ packed, Layout L,
+                                                           const uint16_t* __restrict__ x,
+                                                           const int32_t* __restrict__ row_index,
+                                                           const int32_t* __restrict__ goff, int E,
+                                                           void* __restrict__ y, int NB) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a[2][TL_BUF_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const TileScan ts = scan_tiles(goff, E, TL_BM);
+  const int item = work_item(ts.total * NB, true);
+  if (item < 0) return;
+  const int t = item / NB;
+  const int nb = item - t * NB;
+  const Tile tile = locate_tile(goff, E, TL_BM, ts, t);
+  const int K = (int)L.K;
+  const int KC = (int)L.KC;
+  const int n0 = nb * TL_BN + wave * 16 * TL_NS;
+  const bool wave_active = n0 < L.N;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const int nsub = (tile.rows + 15) >> 4;
+
+  // Source of each of this lane's staging loads (rows past the band are not
+  // loaded: their LDS rows only feed accumulator rows that are never stored).
+  const uint8_t* ap[TL_LOADS];
+  bool av[TL_LOADS];
+#pragma unroll
+  for (int j = 0; j < TL_LOADS; ++j) {
+    const int rl = 4 * (wave * TL_LOADS + j) + (lane >> 4);
+    av[j] = rl < tile.rows;
+    const int row = tile.m0 + (av[j] ? rl : 0);
+    const int64_t src = row_index ? row_index[row] : row;
+    const int logical_seg = (lane & 15) ^ (rl & 15);
+    ap[j] = reinterpret_cast<const uint8_t*>(x + src * K) + logical_seg * 16;
+  }
+  const u32x4_t* cp[TL_NS];
+  const uint32_t* sp[TL_NS];
+#pragma unroll
+  for (int ns = 0; ns < TL_NS; ++ns) {
+    const int64_t nt = wave_active ? (n0 >> 4) + ns : 0;
+    const int64_t et = (int64_t)tile.e * L.NT + nt;
+    cp[ns] = reinterpret_cast<const u32x4_t*>(packed + ((et * L.KC) << 10)) + lane;
+    sp[ns] = reinterpret_cast<const uint32_t*>(packed + L.scales_off) + et * L.groups * 64 + lane;
+  }
+
+  f32x4_t acc[TL_MS][TL_NS];
+#pragma unroll
+  for (int ms = 0; ms < TL_MS; ++ms)
+#pragma unroll
+    for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: chunk 0 -> LDS buffer 0, codes of chunk 0 -> registers
+  stage_chunk(s_a[0], ap, av, 0, wave);
+  u32x4_t cnext[TL_NS];
+  if (wave_active) {
+#pragma unroll
+    for (int ns = 0; ns < TL_NS; ++ns) cnext[ns] = __builtin_nontemporal_load(cp[ns]);
+  }
+  uint32_t sw[TL_NS];
+  __syncthreads();
+
+  // fragment read offsets: row ms*16 + r, logical segment g*4 + s
+  int aoff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aoff[s] = r * TL_ROW_BYTES + (((g * 4 + s) ^ r) << 4);
+
+  for (int kc = 0; kc < KC; ++kc) {
+    const int buf = kc & 1;
+    const bool more = kc + 1 < KC;
+    if (more) stage_chunk(s_a[buf ^ 1], ap, av, kc + 1, wave);
+    if (wave_active) {
+      u32x4_t c[TL_NS];
+#pragma unroll
+      for (int ns = 0; ns < TL_NS; ++ns) c[ns] = cnext[ns];
+      if (more) {
+#pragma unroll
+        for (int ns = 0; ns < TL_NS; ++ns) cnext[ns] = __builtin_nontemporal_load(cp[ns] + (kc + 1) * 64);
+      }
+      if (new_scale_record<FMT>(kc)) {
+#pragma unroll
+        for (int ns = 0; ns < TL_NS; ++ns) sw[ns] = sp[ns][scale_record<FMT>(kc) * 64];
+      }
+      float lo[TL_NS], hi[TL_NS];
+#pragma unroll
+      for (int ns = 0; ns < TL_NS; ++ns) chunk_scales<FMT>(sw[ns], kc, lo[ns], hi[ns]);
+      const uint8_t* abase = s_a[buf];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8_t b[TL_NS];
+#pragma unroll
+        for (int ns = 0; ns < TL_NS; ++ns) b[ns] = decode8(c[ns][s], s < 2 ? lo[ns] : hi[ns]);
+#pragma unroll
+        for (int ms = 0; ms < TL_MS; ++ms) {
+          if (ms < nsub) {
+            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(abase + ms * 16 * TL_ROW_BYTES + aoff[s]);
+#pragma unroll
+            for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = mfma(as_bf16x8(a), b[ns], acc[ms][ns]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+  const float post = FMT == 1 ? reinterpret_cast<const float*>(packed + L.tscale_off)[tile.e] : 1.0f;
+#pragma unroll
+  for (int ms = 0; ms < TL_MS; ++ms) {
+    if (ms < nsub) {
+#pragma unroll
+      for (int ns = 0; ns < TL_NS; ++ns)
+        store_tile<OBF16>(y, L.N, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + ns * 16 + r,
+                          acc[ms][ns], post);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launch.  Tile lists live on the device (built from group_offsets by each
+// wave), so the grid is an upper bound: ceil(M / BM) + min(E, M) tiles, and
+// workgroups past the real tile count return at once.
+// ---------------------------------------------------------------------------
+constexpr int ST_MS = 1;
+constexpr int ST_NS = 2;
+
+template <int FMT, bool OBF16>
+static void launch_gmm_t(const uint8_t* packed, const Layout& L, const uint16_t* x,
+                         const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
+                         void* y, int kernel, hipStream_t stream) {
+  const int64_t em = E < M ? E : M;
+  if (kernel == 1) {
+    constexpr int BM = 16 * ST_MS;
+    const int NB = (int)((L.N + 64 * ST_NS - 1) / (64 * ST_NS));
+    const int64_t tiles = (M + BM - 1) / BM + em;
+    hipLaunchKernelGGL((gmm_stream_kernel<ST_MS, ST_NS, FMT, OBF16>), dim3((unsigned)(tiles * NB)),
+                       dim3(256), 0, stream, packed, L, x, row_index, goff, E, y, NB);
+  } else {
+    const int NB = (int)((L.N + TL_BN - 1) / TL_BN);
+    const int64_t tiles = (M + TL_BM - 1) / TL_BM + em;
+    hipLaunchKernelGGL((gmm_tiled_kernel<FMT, OBF16>), dim3((unsigned)(tiles * NB)), dim3(256), 0,
+                       stream, packed, L, x, row_index, goff, E, y, NB);
+  }
+}
+
+hipError_t launch_gmm(const uint8_t* packed, int fmt, int32_t E, int32_t N, int32_t K,
+                      const uint16_t* x, const int32_t* row_index, const int32_t* group_offsets,
+                      int32_t M, void* y, int y_bf16, int kernel, hipStream_t stream) {
+  const Layout L = make_layout(fmt, E, N, K);
+  if (fmt == 0) {
+    if (y_bf16) launch_gmm_t<0, true>(packed, L, x, row_index, group_offsets, E, M, y, kernel, stream);
+    else launch_gmm_t<0, false>(packed, L, x, row_index, group_offsets, E, M, y, kernel, stream);
+  } else {
+    if (y_bf16) launch_gmm_t<1, true>(packed, L, x, row_index, group_offsets, E, M, y, kernel, stream);
+    else launch_gmm_t<1, false>(packed, L, x, row_index, group_offsets, E, M, y, kernel, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,34 @@
+// Internal launchers behind the C ABI.  Arguments are validated by api.cpp
+// before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route_sort(const int32_t* ids, int32_t T, int32_t k, int32_t E,
+                             int32_t* group_offsets, int32_t* sorted_token, int32_t* sorted_pair,
+                             int32_t* pair_row, int32_t* err_count, hipStream_t stream);
+
+hipError_t launch_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
+                         const float* tensor_scale, int32_t E, int32_t N, int32_t K,
+                         uint8_t* packed, hipStream_t stream);
+
+hipError_t launch_debug_decode(const uint8_t* packed, int fmt, int32_t E, int32_t N, int32_t K,
+                               uint16_t* w, hipStream_t stream);
+
+hipError_t launch_mxfp4_to_nvfp4(const uint8_t* scales, int32_t E, int32_t N, int32_t K,
+                                 uint8_t* block_scales, float* tensor_scale, int32_t* err_count,
+                                 hipStream_t stream);
+
+// kernel: 1 = weight-streaming waves, 2 = LDS-tiled activations.
+hipError_t launch_gmm(const uint8_t* packed, int fmt, int32_t E, int32_t N, int32_t K,
+                      const uint16_t* x, const int32_t* row_index, const int32_t* group_offsets,
+                      int32_t M, void* y, int y_bf16, int kernel, hipStream_t stream);
+
+hipError_t launch_combine(const void* y, int y_bf16, const float* w, const int32_t* pair_row,
+                          int32_t T, int32_t k, int32_t N, void* out, int out_bf16,
+                          hipStream_t stream);
+
+}  // namespace moe

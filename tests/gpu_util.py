@@ -1,0 +1,64 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the
+binding on a synthetic problem, and compare against the oracle."""
+
+import numpy as np
+import torch
+
+import moe_grouped_gemm_route_amd as moe
+import oracle
+
+DEV = "cuda"
+REL_TOL = 1e-5        # max|gpu - oracle| / max|oracle| for f32 outputs
+
+
+def to_dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def weights_for(p, fmt):
+    """Oracle weight dict and device tensors for format fmt ('mxfp4'|'nvfp4').
+    NVFP4 scales come from the oracle's lossless cast of the MXFP4 scales."""
+    if fmt == "mxfp4":
+        w = {"fmt": "mxfp4", "codes": p["codes"], "scales": p["scales"]}
+        packed = moe.mxfp4_encode(to_dev(p["codes"]), to_dev(p["scales"]), None, moe.MXFP4)
+    else:
+        if "block_scales" in p:
+            bs, ts = p["block_scales"], p["tensor_scale"]
+        else:
+            bs, ts = oracle.mxfp4_to_nvfp4(p["scales"])
+        w = {"fmt": "nvfp4", "codes": p["codes"], "block_scales": bs, "tensor_scale": ts}
+        packed = moe.mxfp4_encode(to_dev(p["codes"]), to_dev(bs), to_dev(ts), moe.NVFP4)
+    return w, packed
+
+
+def run_gpu(p, packed, fmt, kernel=moe.GMM_AUTO, out_dtype=moe.F32, routed=None):
+    """Route-sort on the GPU, then moe_gmm.  Returns (route dict, y tensor)."""
+    E, K, N = p["E"], p["K"], p["N"]
+    M = p["T"] * p["k"]
+    r = routed if routed is not None else moe.route_sort(to_dev(p["topk_ids"]), E)
+    x = to_dev(p["x"])
+    f = moe.MXFP4 if fmt == "mxfp4" else moe.NVFP4
+    y = moe.moe_gmm(packed, f, E, N, K, x, r["group_offsets"], M,
+                    row_index=r["sorted_token"] if p["gather"] else None,
+                    out_dtype=out_dtype, kernel=kernel)
+    return r, y
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+
+
+def bf16_bits_to_f64(bits):
+    return oracle.gmm.bf16_bits_to_f64(np.asarray(bits).view(np.uint16))
+
+
+def bf16_ulp(ref):
+    """One bf16 unit in the last place at |ref| (normal range)."""
+    a = np.abs(np.asarray(ref, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.ldexp(1.0, (e - 7).astype(np.int64))

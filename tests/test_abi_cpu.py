@@ -1,0 +1,119 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function include/moe_gmm.h declares, and rejects bad arguments before any
+HIP call (so nothing is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_grouped_gemm_route_amd as moe
+from moe_grouped_gemm_route_amd.synth import CONFIGS
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe_gmm.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_FORMAT = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(1 << 20)          # never dereferenced: calls fail validation first
+FAKE_ALIGNED = ctypes.c_void_p(1 << 30)
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"moe_route_sort", "mxfp4_encode", "moe_gmm", "moe_combine"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(moe._SIGNATURES)
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.moe_status_string(s)
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+def test_packed_bytes(lib):
+    for c in CONFIGS.values():
+        E, N, K = c["E"], c["N"], c["K"]
+        mx = lib.moe_packed_weight_bytes(0, E, N, K)
+        # codes 4 bits each + one scale byte per 32 weights (K/128 chunks padded to groups of 4)
+        groups = -(-(K // 128) // 4)
+        assert mx == E * N * K // 2 + E * (N // 16) * groups * 256
+        nv = lib.moe_packed_weight_bytes(1, E, N, K)
+        groups = -(-(K // 128) // 2)
+        assert nv == E * N * K // 2 + E * (N // 16) * groups * 256 + ((4 * E + 255) // 256) * 256
+    assert lib.moe_packed_weight_bytes(0, 8, 512, 100) == 0
+    assert lib.moe_packed_weight_bytes(0, 8, 48, 256) == 0
+    assert lib.moe_packed_weight_bytes(7, 8, 512, 256) == 0
+
+
+def test_route_sort_validation(lib):
+    f = lib.moe_route_sort
+    assert f(None, 4, 2, 8, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_NULL
+    assert f(FAKE, 0, 2, 8, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert f(FAKE, 4, 0, 8, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert f(FAKE, 4, 2, 1025, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert f(FAKE, 1 << 22, 8, 8, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+
+
+def test_encode_validation(lib):
+    f = lib.mxfp4_encode
+    assert f(0, None, FAKE, None, 8, 512, 256, FAKE_ALIGNED, None) == ERR_NULL
+    assert f(0, FAKE, FAKE, None, 8, 512, 96, FAKE_ALIGNED, None) == ERR_SHAPE
+    assert f(2, FAKE, FAKE, None, 8, 512, 256, FAKE_ALIGNED, None) == ERR_FORMAT
+    assert f(1, FAKE, FAKE, None, 8, 512, 256, FAKE_ALIGNED, None) == ERR_NULL      # NVFP4 needs tensor scales
+    assert f(0, FAKE, FAKE, FAKE, 8, 512, 256, FAKE_ALIGNED, None) == ERR_FORMAT    # MXFP4 takes none
+    assert f(0, FAKE, FAKE, None, 8, 512, 256, ctypes.c_void_p((1 << 30) + 16), None) == ERR_SHAPE
+
+
+def test_gmm_validation(lib):
+    f = lib.moe_gmm_ex
+    args = lambda **kw: [kw.get("packed", FAKE_ALIGNED), kw.get("fmt", 0), kw.get("E", 8),
+                         kw.get("N", 512), kw.get("K", 256), kw.get("x", FAKE_ALIGNED), None,
+                         kw.get("off", FAKE), kw.get("M", 128), kw.get("y", FAKE),
+                         kw.get("dt", 0), kw.get("kernel", 0), None]
+    assert f(*args(packed=None)) == ERR_NULL
+    assert f(*args(y=None)) == ERR_NULL
+    assert f(*args(off=None)) == ERR_NULL
+    assert f(*args(K=200)) == ERR_SHAPE
+    assert f(*args(N=500)) == ERR_SHAPE
+    assert f(*args(E=0)) == ERR_SHAPE
+    assert f(*args(M=0)) == ERR_SHAPE
+    assert f(*args(M=(1 << 24) + 1)) == ERR_SHAPE
+    assert f(*args(fmt=3)) == ERR_FORMAT
+    assert f(*args(dt=2)) == ERR_FORMAT
+    assert f(*args(kernel=3)) == ERR_FORMAT
+    assert f(*args(packed=ctypes.c_void_p((1 << 30) + 128))) == ERR_SHAPE
+    assert lib.moe_gmm(None, 0, 8, 512, 256, FAKE, None, FAKE, 128, FAKE, 0, None) == ERR_NULL
+
+
+def test_combine_validation(lib):
+    f = lib.moe_combine
+    assert f(FAKE_ALIGNED, 0, FAKE, FAKE, 4, 2, 6, FAKE_ALIGNED, 0, None) == ERR_SHAPE
+    assert f(FAKE_ALIGNED, 0, FAKE, FAKE, 4, 0, 8, FAKE_ALIGNED, 0, None) == ERR_SHAPE
+    assert f(FAKE_ALIGNED, 5, FAKE, FAKE, 4, 2, 8, FAKE_ALIGNED, 0, None) == ERR_FORMAT
+    assert f(None, 0, FAKE, FAKE, 4, 2, 8, FAKE_ALIGNED, 0, None) == ERR_NULL
+
+
+def test_cast_and_debug_decode_validation(lib):
+    assert lib.moe_mxfp4_to_nvfp4(None, 1, 16, 64, FAKE, FAKE, None, None) == ERR_NULL
+    assert lib.moe_mxfp4_to_nvfp4(FAKE, 1, 16, 48, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert lib.moe_debug_decode(FAKE_ALIGNED, 0, 1, 64, 100, FAKE, None) == ERR_SHAPE
+    assert lib.moe_debug_decode(None, 0, 1, 64, 128, FAKE, None) == ERR_NULL
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(moe.MoeGmmError):
+        moe.route_sort(torch.zeros((4, 2), dtype=torch.int32), 8)

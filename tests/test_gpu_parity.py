@@ -1,0 +1,283 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Integer and index results are compared bit for bit; decoded weights are
+compared exactly (every decoded value is representable in bf16); f32 matmul
+outputs to max|gpu - oracle| / max|oracle| <= 1e-5; bf16 outputs to one bf16
+ulp of the oracle.  Full-size workloads are checked on sampled outputs, which
+the oracle computes one dot product at a time, plus properties that hold at
+any size (kernel configurations agree bitwise, NVFP4 built by the lossless
+cast equals MXFP4 bitwise, repeated runs are bitwise identical).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_route_amd as moe
+import oracle
+from moe_grouped_gemm_route_amd.synth import make_config, make_problem
+from gpu_util import (REL_TOL, bf16_bits_to_f64, bf16_ulp, rel_err, run_gpu, to_dev,
+                      weights_for)
+
+pytestmark = pytest.mark.gpu
+
+KERNELS = [moe.GMM_STREAM, moe.GMM_TILED]
+
+
+def _route_check(ids, E):
+    ref = oracle.route_sort(ids, E)
+    got = moe.route_sort(to_dev(ids), E)
+    torch.cuda.synchronize()
+    for key in ("group_offsets", "sorted_token", "sorted_pair", "pair_row"):
+        assert np.array_equal(got[key].cpu().numpy(), ref[key]), key
+    assert int(got["err_count"].item()) == ref["err_count"]
+
+
+# ---------------------------------------------------------------- decode ---
+
+def test_debug_decode_all_codes_mxfp4():
+    E, N, K = 2, 64, 512
+    rng = np.random.default_rng(100)
+    codes = np.tile(np.arange(256, dtype=np.uint8), E * N * K // 2 // 256).reshape(E, N, K // 2)
+    codes = rng.permuted(codes, axis=2)
+    scales = rng.integers(2, 253, size=(E, N, K // 32)).astype(np.uint8)
+    scales[0, 0, :4] = [2, 127, 252, 126]
+    packed = moe.mxfp4_encode(to_dev(codes), to_dev(scales), None, moe.MXFP4)
+    w = moe.debug_decode(packed, moe.MXFP4, E, N, K).cpu().numpy()
+    ref = oracle.decode_mxfp4(codes, scales)
+    got = bf16_bits_to_f64(w)
+    assert np.array_equal(got, ref)
+
+
+def test_debug_decode_nvfp4_general_e4m3():
+    E, N, K = 2, 64, 256
+    rng = np.random.default_rng(101)
+    codes = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    bs = rng.integers(0, 0x7F, size=(E, N, K // 16)).astype(np.uint8)   # every finite positive E4M3
+    bs[0, 0, :] = np.arange(16)                                          # subnormals and zero
+    ts = np.array([1.0, 1.0], dtype=np.float32)
+    packed = moe.mxfp4_encode(to_dev(codes), to_dev(bs), to_dev(ts), moe.NVFP4)
+    w = moe.debug_decode(packed, moe.NVFP4, E, N, K).cpu().numpy()
+    ref = oracle.decode_nvfp4(codes, bs, ts)
+    assert np.array_equal(bf16_bits_to_f64(w), ref)
+
+
+def test_nvfp4_cast_gpu_matches_oracle():
+    p = make_problem(T=8, k=2, E=4, K=512, N=64, seed=102, exp_range=(-12, 5))
+    bs_ref, ts_ref = oracle.mxfp4_to_nvfp4(p["scales"])
+    bs, ts, err = moe.mxfp4_to_nvfp4(to_dev(p["scales"]))
+    assert np.array_equal(bs.cpu().numpy(), bs_ref)
+    assert np.array_equal(ts.cpu().numpy(), ts_ref)
+    assert err.item() == 0
+    bad = p["scales"].copy()
+    bad[1, 3, 2] = bad[1].max() - 18                  # below k_max - 17: not castable
+    _, _, err = moe.mxfp4_to_nvfp4(to_dev(bad))
+    assert err.item() == 1
+
+
+# ------------------------------------------------------------ route sort ---
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_route_sort_configs(cfg):
+    from moe_grouped_gemm_route_amd.synth import CONFIGS
+    c = CONFIGS[cfg]
+    p = make_problem(T=c["T"], k=c["k"], E=c["E"], K=32, N=1, seed=cfg, routing=c["routing"],
+                     empty_experts=c.get("empty_experts", ()))
+    _route_check(p["topk_ids"], c["E"])
+
+
+def test_route_sort_edge_cases():
+    _route_check(np.zeros((1, 1), dtype=np.int32), 1)                       # single pair, E = 1
+    _route_check(np.full((300, 4), 5, dtype=np.int32), 8)                   # all on one expert
+    rng = np.random.default_rng(7)
+    ids = rng.integers(-3, 260, size=(777, 6)).astype(np.int32)            # invalid ids dropped
+    _route_check(ids, 256)
+    _route_check(rng.integers(0, 1024, size=(3000, 8)).astype(np.int32), 1024)
+    _route_check(rng.integers(0, 3, size=(5000, 1)).astype(np.int32), 3)
+
+
+# ------------------------------------------------------------------- gmm ---
+
+SMALL = [
+    # T, k, E, K, N, routing, band input, empty experts
+    dict(T=64, k=2, E=8, K=256, N=512, routing="uniform", empty=(7,)),
+    dict(T=200, k=4, E=16, K=1024, N=320, routing="zipf", empty=(3,)),
+    dict(T=37, k=3, E=5, K=384, N=192, routing="uniform", x_rows=111),
+    dict(T=300, k=1, E=1, K=128, N=64, routing="uniform"),
+    dict(T=1, k=1, E=4, K=128, N=256, routing="uniform"),
+]
+
+
+def _small(i):
+    c = SMALL[i]
+    return make_problem(T=c["T"], k=c["k"], E=c["E"], K=c["K"], N=c["N"], seed=200 + i,
+                        routing=c["routing"], empty_experts=c.get("empty", ()),
+                        x_rows=c.get("x_rows"), exp_range=(-6, -2))
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_gmm_small_full_oracle(case, fmt, kernel):
+    p = _small(case)
+    w, packed = weights_for(p, fmt)
+    r, y = run_gpu(p, packed, fmt, kernel=kernel)
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    ref = oracle.gmm(p["x"], ref_r["sorted_token"] if p["gather"] else None,
+                     ref_r["group_offsets"], w)
+    got = y.cpu().numpy()
+    assert np.array_equal(r["group_offsets"].cpu().numpy(), ref_r["group_offsets"])
+    assert rel_err(got, ref) <= REL_TOL
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_gmm_kernels_agree_bitwise_and_bf16_output(case):
+    p = _small(case)
+    w, packed = weights_for(p, "mxfp4")
+    _, ys = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_STREAM)
+    _, yt = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_TILED)
+    r, yb = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_TILED, out_dtype=moe.BF16)
+    _, yb2 = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_STREAM, out_dtype=moe.BF16)
+    assert torch.equal(ys, yt)
+    assert torch.equal(yb.view(torch.int16), yb2.view(torch.int16))
+    assert torch.equal(yb, ys.to(torch.bfloat16))            # bf16 = RNE of the f32 sum
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    ref = oracle.gmm(p["x"], ref_r["sorted_token"] if p["gather"] else None,
+                     ref_r["group_offsets"], w)
+    got = yb.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= bf16_ulp(ref))
+
+
+def test_gmm_rows_past_bands_untouched_and_canary():
+    # dropped pairs leave rows [group_offsets[E], M) unwritten; nothing is
+    # written past the end of y
+    p = make_problem(T=50, k=2, E=6, K=256, N=128, seed=300)
+    p["topk_ids"][3, 1] = 99
+    p["topk_ids"][10, 0] = -1
+    w, packed = weights_for(p, "mxfp4")
+    M, N = p["T"] * p["k"], p["N"]
+    r = moe.route_sort(to_dev(p["topk_ids"]), p["E"])
+    for kernel in KERNELS:
+        buf = torch.full((M + 4, N), 12345.0, dtype=torch.float32, device="cuda")
+        moe.moe_gmm(packed, moe.MXFP4, p["E"], N, p["K"], to_dev(p["x"]), r["group_offsets"],
+                    M, row_index=r["sorted_token"], kernel=kernel, out=buf[:M])
+        got = buf.cpu().numpy()
+        assert np.all(got[M - 2:] == 12345.0)
+        ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+        ref = oracle.gmm(p["x"], np.maximum(ref_r["sorted_token"], 0), ref_r["group_offsets"], w)
+        assert rel_err(got[:M - 2], ref[:M - 2]) <= REL_TOL
+
+
+def test_gmm_deterministic():
+    p = _small(1)
+    _, packed = weights_for(p, "mxfp4")
+    for kernel in KERNELS:
+        _, a = run_gpu(p, packed, "mxfp4", kernel=kernel)
+        _, b = run_gpu(p, packed, "mxfp4", kernel=kernel)
+        assert torch.equal(a, b)
+
+
+# ------------------------------------------------- full-size workloads ---
+
+def _sample(M_valid, N, n, seed):
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, M_valid, size=n)
+    cols = rng.integers(0, N, size=n)
+    rows[:8] = [0, M_valid - 1] * 4
+    cols[:8] = [0, N - 1, 0, N - 1, 1, N - 2, 15, 16]
+    return rows, cols
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_gmm_config_sampled(cfg):
+    p = make_config(cfg)
+    fmt = "nvfp4" if cfg == 5 else "mxfp4"
+    w, packed = weights_for(p, fmt)
+    out_dtype = moe.BF16 if p["out"] == "bf16" else moe.F32
+    r, y = run_gpu(p, packed, fmt, out_dtype=out_dtype)
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    assert np.array_equal(r["sorted_token"].cpu().numpy(), ref_r["sorted_token"])
+    M = p["T"] * p["k"]
+    rows, cols = _sample(M, p["N"], 3000, 400 + cfg)
+    ri = ref_r["sorted_token"] if p["gather"] else None
+    ref = oracle.gmm_sampled(p["x"], ri, ref_r["group_offsets"], w, rows, cols)
+    got = y.float().cpu().numpy()[rows, cols].astype(np.float64)
+    if out_dtype == moe.BF16:
+        assert np.all(np.abs(got - ref) <= bf16_ulp(ref))
+        _, y32 = run_gpu(p, packed, fmt, routed=r)
+        got = y32.cpu().numpy()[rows, cols]
+    assert rel_err(got, ref) <= REL_TOL
+    if cfg == 1:
+        full = oracle.gmm(p["x"], ref_r["sorted_token"], ref_r["group_offsets"], w)
+        _, y32 = run_gpu(p, packed, fmt, routed=r)
+        assert rel_err(y32.cpu().numpy(), full) <= REL_TOL
+
+
+@pytest.mark.slow
+def test_config5_nvfp4_equals_mxfp4_bitwise():
+    p = make_config(5)
+    _, packed_mx = weights_for(p, "mxfp4")
+    # NVFP4 scales produced on the GPU by the library's own lossless cast
+    bs, ts, err = moe.mxfp4_to_nvfp4(to_dev(p["scales"]))
+    assert err.item() == 0
+    packed_nv = moe.mxfp4_encode(to_dev(p["codes"]), bs, ts, moe.NVFP4)
+    r = moe.route_sort(to_dev(p["topk_ids"]), p["E"])
+    for kernel in KERNELS:
+        _, a = run_gpu(p, packed_mx, "mxfp4", kernel=kernel, routed=r)
+        _, b = run_gpu(p, packed_nv, "nvfp4", kernel=kernel, routed=r)
+        assert torch.equal(a, b)
+    del packed_mx, packed_nv
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_full_size_kernels_agree_bitwise(cfg):
+    p = make_config(cfg)
+    _, packed = weights_for(p, "mxfp4")
+    r = moe.route_sort(to_dev(p["topk_ids"]), p["E"])
+    _, a = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_STREAM, routed=r)
+    _, b = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_TILED, routed=r)
+    assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------- combine ---
+
+@pytest.mark.parametrize("ydt", [moe.F32, moe.BF16])
+def test_combine_matches_oracle(ydt):
+    p = make_problem(T=256, k=6, E=32, K=128, N=512, seed=500, routing="zipf")
+    p["topk_ids"][5, 2] = -7                          # a dropped pair
+    rng = np.random.default_rng(501)
+    M = p["T"] * p["k"]
+    yf = rng.standard_normal((M, p["N"])).astype(np.float32)
+    y = to_dev(yf)
+    if ydt == moe.BF16:
+        y = y.to(torch.bfloat16)
+        yf = y.float().cpu().numpy()
+    r = moe.route_sort(to_dev(p["topk_ids"]), p["E"])
+    out = moe.moe_combine(y, to_dev(p["topk_weights"]), r["pair_row"]).cpu().numpy()
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    ref = oracle.combine(yf, p["topk_weights"], ref_r["pair_row"])
+    assert rel_err(out, ref) <= REL_TOL
+
+
+@pytest.mark.slow
+def test_config3_w2_then_combine():
+    p = make_config(3)
+    w, packed = weights_for(p, "mxfp4")
+    r, y = run_gpu(p, packed, "mxfp4")
+    out = moe.moe_combine(y, to_dev(p["topk_weights"]), r["pair_row"]).cpu().numpy()
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    # the oracle combine over oracle rows needed by the sampled tokens only
+    rng = np.random.default_rng(503)
+    toks = rng.choice(p["T"], size=12, replace=False)
+    cols = np.arange(0, p["N"], 37)
+    k = p["k"]
+    rows = np.array([ref_r["pair_row"][t * k + j] for t in toks for j in range(k)])
+    rr, cc = np.repeat(rows, len(cols)), np.tile(cols, len(rows))
+    yref = oracle.gmm_sampled(p["x"], None, ref_r["group_offsets"], w, rr, cc).reshape(len(rows), len(cols))
+    ref = np.zeros((len(toks), len(cols)))
+    for i, t in enumerate(toks):
+        for j in range(k):
+            ref[i] += float(p["topk_weights"][t, j]) * yref[i * k + j]
+    assert rel_err(out[np.ix_(toks, cols)], ref) <= REL_TOL
