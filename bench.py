@@ -1,0 +1,249 @@
+"""Benchmark of the routed-expert W4A16 grouped matmul on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the hot path over one batch of synthetic input with the
+expert weights already packed and resident in HBM (the one-time load-time
+repack is excluded, as the grouped-matmul timings of "Running DeepSeek V4
+Flash on TPU v6", section "Grouped matmul performance vs bf16", exclude it):
+  route-sort of the top-k ids -> grouped matmul (-> top-k combine for the
+  down-projection workload, whose router weights are given).
+The default workload is the gate/up (w13) decode: 64 tokens, hidden 4096,
+256 experts, top-6 uniform routing, fused gate+up weight K = N = 4096 in
+MXFP4, bf16 output.
+
+One JSON line is printed.  value is the whole step's throughput in the
+algorithmic bytes of the matmul (codes + scales of the experts that received
+tokens, plus the activations read) per second; roofline.achieved is the same
+bytes over the grouped-matmul kernel's own average duration, timed with HIP
+events on the stream it runs on.  The CPU baseline times the float64 oracle on
+a bounded sample of the same workload on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+
+WORKLOADS = {
+    "tiny": 1, "w13_decode": 2, "w2_decode": 3, "w13_prefill": 4, "nvfp4_w13": 5,
+}
+KERNELS = {"auto": 0, "stream": 1, "tiled": 2}
+GMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_route_amd", "csrc", "gmm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def gmm_source_hash():
+    with open(GMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(p, fmt):
+    """Codes + scales of every expert with a non-empty band, plus the
+    activation bytes the matmul reads (unique token rows when gathering)."""
+    counts = np.bincount(p["topk_ids"].reshape(-1), minlength=p["E"])
+    active = int(np.count_nonzero(counts))
+    per_weight = 0.5 + (1.0 / 32 if fmt == "mxfp4" else 1.0 / 16)
+    w_bytes = active * p["N"] * p["K"] * per_weight + (active * 4 if fmt == "nvfp4" else 0)
+    x_rows = p["T"] if p["gather"] else p["T"] * p["k"]
+    return w_bytes + x_rows * p["K"] * 2, active
+
+
+def cpu_baseline(p, fmt, unit, target_s=15.0):
+    """The float64 oracle on the host: route-sort of the whole batch, then the
+    grouped matmul of as many expert bands (in expert order) as fit in about
+    target_s seconds.  Reported as the same algorithmic bytes per second."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    if fmt == "nvfp4":
+        bs, ts = oracle.mxfp4_to_nvfp4(p["scales"])
+        w = {"fmt": "nvfp4", "codes": p["codes"], "block_scales": bs, "tensor_scale": ts}
+    else:
+        w = {"fmt": "mxfp4", "codes": p["codes"], "scales": p["scales"]}
+    t0 = time.perf_counter()
+    r = oracle.route_sort(p["topk_ids"], p["E"])
+    off = r["group_offsets"]
+    active = [e for e in range(p["E"]) if off[e + 1] > off[e]]
+    done, nbytes = 0, 0.0
+    per_weight = 0.5 + (1.0 / 32 if fmt == "mxfp4" else 1.0 / 16)
+    rows_done = 0
+    while done < len(active) and time.perf_counter() - t0 < target_s:
+        e = active[done]
+        sub_off = np.array([off[e], off[e + 1]], dtype=np.int32)
+        sub = dict(w)
+        sub["codes"] = w["codes"][e:e + 1]
+        if fmt == "mxfp4":
+            sub["scales"] = w["scales"][e:e + 1]
+        else:
+            sub["block_scales"] = w["block_scales"][e:e + 1]
+            sub["tensor_scale"] = w["tensor_scale"][e:e + 1]
+        ri = r["sorted_token"] if p["gather"] else None
+        oracle.gmm(p["x"], ri, sub_off, sub)
+        nbytes += p["N"] * p["K"] * per_weight
+        rows_done += int(off[e + 1] - off[e])
+        done += 1
+    elapsed = time.perf_counter() - t0
+    x_rows = (p["T"] * rows_done / (p["T"] * p["k"])) if p["gather"] else rows_done
+    nbytes += x_rows * p["K"] * 2
+    if unit == "TFLOP/s":
+        value = 2.0 * rows_done * p["K"] * p["N"] / elapsed / 1e12
+    else:
+        value = nbytes / elapsed / 1e9
+    return {
+        "value": round(value, 6), "unit": unit, "cores": int(threads),
+        "kind": "oracle",
+        "sample": "float64 numpy oracle: route-sort of all %d pairs + grouped matmul of the "
+                  "first %d of %d active experts' bands (%d rows), %.1f s"
+                  % (p["T"] * p["k"], done, len(active), rows_done, elapsed),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="w13_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--kernel", default="auto", choices=sorted(KERNELS))
+    ap.add_argument("--out-dtype", default=None, choices=["f32", "bf16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the routed-expert matmul would shard by experts; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_grouped_gemm_route_amd as moe
+    from moe_grouped_gemm_route_amd.synth import make_config
+
+    cfg = WORKLOADS[args.workload]
+    p = make_config(cfg)
+    fmt = "nvfp4" if cfg == 5 else "mxfp4"
+    out_dtype = args.out_dtype or p["out"]
+    odt = moe.BF16 if out_dtype == "bf16" else moe.F32
+    E, K, N, T, k = p["E"], p["K"], p["N"], p["T"], p["k"]
+    M = T * k
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    ids = d(p["topk_ids"])
+    x = d(p["x"])
+    codes = d(p["codes"])
+    if fmt == "mxfp4":
+        packed = moe.mxfp4_encode(codes, d(p["scales"]), None, moe.MXFP4)
+        wf = moe.MXFP4
+    else:
+        bs, ts, err = moe.mxfp4_to_nvfp4(d(p["scales"]))
+        packed = moe.mxfp4_encode(codes, bs, ts, moe.NVFP4)
+        wf = moe.NVFP4
+        assert err.item() == 0
+    del codes
+    tw = d(p["topk_weights"])
+    combine = cfg == 3
+    y = torch.empty((M, N), dtype=torch.bfloat16 if odt == moe.BF16 else torch.float32, device=dev)
+    kernel = KERNELS[args.kernel]
+    torch.cuda.synchronize()
+
+    ev = []
+
+    def step(timed):
+        r = moe.route_sort(ids, E)
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        moe.moe_gmm(packed, wf, E, N, K, x, r["group_offsets"], M,
+                    row_index=r["sorted_token"] if p["gather"] else None,
+                    out_dtype=odt, kernel=kernel, out=y)
+        if timed:
+            e1.record()
+            ev.append((e0, e1))
+        if combine:
+            moe.moe_combine(y, tw, r["pair_row"])
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    gmm_ms = [a.elapsed_time(b) for a, b in ev]
+    gmm_avg_s = float(np.mean(gmm_ms)) / 1e3
+    nbytes, active = algorithmic_bytes(p, fmt)
+    flops = 2.0 * M * K * N
+    step_s = wall / args.steps
+    prefill = cfg == 4
+    if prefill:
+        achieved = flops / gmm_avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+        value, unit = flops / step_s / 1e12, "TFLOP/s"
+    else:
+        achieved = nbytes / gmm_avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        value, unit = nbytes / step_s / 1e9, "GB/s"
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tf = json.load(open(TRAFFIC_FILE))
+            entry = tf.get(args.workload, {})
+            if entry.get("gmm_source_sha256_16") == gmm_source_hash():
+                traffic = entry.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    roof["traffic"] = traffic
+
+    out = {
+        "metric": "moe_gmm TFLOP/s and HBM GB/s (% roofline), w13/w2, 256 experts top-6",
+        "value": round(value, 2),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "top_k": k, "experts": E, "K": K,
+                   "N": N, "routed_rows": M, "weights": fmt, "activations": "bf16",
+                   "output": out_dtype, "kernel": args.kernel,
+                   "step": "route_sort + moe_gmm" + (" + moe_combine" if combine else "")},
+        "gmm_us": round(gmm_avg_s * 1e6, 2),
+        "gmm_tflops": round(flops / gmm_avg_s / 1e12, 2),
+        "gmm_gbs": round(nbytes / gmm_avg_s / 1e9, 1),
+        "active_experts": active,
+        "algorithmic_bytes": int(nbytes),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p, fmt, unit)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -67,13 +67,43 @@ __host__ __device__ inline int64_t code_run_offset(const Layout& L, int64_t e, i
 // An e2m1 value has at most two significant bits, so value * 2^k is exact in
 // bf16 while it stays normal; value * E4M3 has at most six significant bits
 // and is exact as well.
+//
+// The four converted pairs are only ever moved as whole 32-bit words (bit
+// casts of the packed bf16x2 results): splitting them into bf16 elements lets
+// this compiler fold the four byte selects into one, which duplicates values.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bf16x8_t decode8(uint32_t codes8, float scale) {
-  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes8, scale, 0);
-  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes8, scale, 1);
-  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes8, scale, 2);
-  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes8, scale, 3);
-  return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+__device__ __forceinline__ u32x4_t decode8(uint32_t codes8, float scale) {
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes8, scale, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes8, scale, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes8, scale, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes8, scale, 3));
+  return r;
+}
+
+// The scaled convert applies only the exponent of its f32 scale operand, which
+// is exact for every E8M0 scale and for power-of-two E4M3 scales.  A general
+// E4M3 scale s (up to four significant bits) goes through f32 instead: codes
+// -> f32 (scale 1), times s (exact: at most six significant bits), then the
+// upper halves are packed into bf16 pairs (exact: the values fit bf16).
+__device__ __forceinline__ u32x4_t decode8_any_scale(uint32_t codes8, float s) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  u32x4_t r;
+#define MOE_PAIR(i)                                                                 \
+  {                                                                                 \
+    const f32x2_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes8, 1.0f, i);    \
+    r[i] = __builtin_amdgcn_perm(__float_as_uint(v[1] * s), __float_as_uint(v[0] * s), \
+                                 0x07060302u);                                      \
+  }
+  MOE_PAIR(0) MOE_PAIR(1) MOE_PAIR(2) MOE_PAIR(3)
+#undef MOE_PAIR
+  return r;
+}
+
+// True for a positive power of two (the scales decode8 handles exactly).
+__device__ __forceinline__ bool is_pow2_scale(float s) {
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x807FFFFFu) == 0 && (u & 0x7F800000u) != 0 && (u & 0x7F800000u) != 0x7F800000u;
 }
 
 // E8M0 byte b (1..254) -> 2^(b - 127) as f32, by placing b in the exponent.

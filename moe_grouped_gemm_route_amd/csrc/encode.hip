@@ -106,10 +106,11 @@ __global__ __launch_bounds__(256) void debug_decode_kernel(const uint8_t* __rest
       s_lo = e4m3_to_f32<0>(pair);
       s_hi = e4m3_to_f32<1>(pair);
     }
-    uint16_t* dst = w + i * 32;
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(w + i * 32);
+#pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const bf16x8_t v = decode8(c[d], d < 2 ? s_lo : s_hi);
-      for (int j = 0; j < 8; ++j) dst[d * 8 + j] = __builtin_bit_cast(uint16_t, v[j]);
+      const float s = d < 2 ? s_lo : s_hi;
+      dst[d] = is_pow2_scale(s) || fmt == 0 ? decode8(c[d], s) : decode8_any_scale(c[d], s);
     }
   }
 }

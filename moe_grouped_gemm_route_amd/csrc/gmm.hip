@@ -124,6 +124,25 @@ __device__ __forceinline__ void chunk_scales(uint32_t word, int kc, float& lo, f
   }
 }
 
+// NVFP4 chunks whose E4M3 scales are all powers of two (for instance every
+// chunk made by the lossless MXFP4 cast) take the one-instruction decode; a
+// wave with any other scale in the chunk takes the general exact decode.
+// Both give the same bits.
+template <int FMT, int NS>
+__device__ __forceinline__ bool general_scales(const float (&lo)[NS], const float (&hi)[NS]) {
+  if (FMT == 0) return false;
+  bool all = true;
+#pragma unroll
+  for (int ns = 0; ns < NS; ++ns) all = all && is_pow2_scale(lo[ns]) && is_pow2_scale(hi[ns]);
+  return __ballot(!all) != 0;
+}
+
+template <int FMT>
+__device__ __forceinline__ u32x4_t decode_step(uint32_t codes8, float scale, bool general) {
+  if (FMT == 1 && general) return decode8_any_scale(codes8, scale);
+  return decode8(codes8, scale);
+}
+
 template <int FMT>
 __device__ __forceinline__ bool new_scale_record(int kc) {
   return FMT == 0 ? (kc & 3) == 0 : (kc & 1) == 0;
@@ -235,16 +254,17 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(const uint8_t* __restri
     float lo[NS], hi[NS];
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) chunk_scales<FMT>(sw[ns], kc, lo[ns], hi[ns]);
+    const bool general = general_scales<FMT, NS>(lo, hi);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bf16x8_t b[NS];
+      u32x4_t b[NS];
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns) b[ns] = decode8(c[ns][s], s < 2 ? lo[ns] : hi[ns]);
+      for (int ns = 0; ns < NS; ++ns) b[ns] = decode_step<FMT>(c[ns][s], s < 2 ? lo[ns] : hi[ns], general);
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms) {
         if (ms < nsub) {
 #pragma unroll
-          for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = mfma(as_bf16x8(a[ms][s]), b[ns], acc[ms][ns]);
+          for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = mfma(as_bf16x8(a[ms][s]), as_bf16x8(b[ns]), acc[ms][ns]);
         }
       }
     }
@@ -382,18 +402,19 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
       float lo[TL_NS], hi[TL_NS];
 #pragma unroll
       for (int ns = 0; ns < TL_NS; ++ns) chunk_scales<FMT>(sw[ns], kc, lo[ns], hi[ns]);
+      const bool general = general_scales<FMT, TL_NS>(lo, hi);
       const uint8_t* abase = s_a[buf];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        bf16x8_t b[TL_NS];
+        u32x4_t b[TL_NS];
 #pragma unroll
-        for (int ns = 0; ns < TL_NS; ++ns) b[ns] = decode8(c[ns][s], s < 2 ? lo[ns] : hi[ns]);
+        for (int ns = 0; ns < TL_NS; ++ns) b[ns] = decode_step<FMT>(c[ns][s], s < 2 ? lo[ns] : hi[ns], general);
 #pragma unroll
         for (int ms = 0; ms < TL_MS; ++ms) {
           if (ms < nsub) {
             const u32x4_t a = *reinterpret_cast<const u32x4_t*>(abase + ms * 16 * TL_ROW_BYTES + aoff[s]);
 #pragma unroll
-            for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = mfma(as_bf16x8(a), b[ns], acc[ms][ns]);
+            for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = mfma(as_bf16x8(a), as_bf16x8(b[ns]), acc[ms][ns]);
           }
         }
       }

@@ -54,7 +54,8 @@ def rel_err(got, ref):
 
 
 def bf16_bits_to_f64(bits):
-    return oracle.gmm.bf16_bits_to_f64(np.asarray(bits).view(np.uint16))
+    from oracle.gmm import bf16_bits_to_f64 as to_f64
+    return to_f64(np.asarray(bits).view(np.uint16))
 
 
 def bf16_ulp(ref):

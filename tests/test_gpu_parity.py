@@ -148,6 +148,23 @@ def test_gmm_kernels_agree_bitwise_and_bf16_output(case):
     assert np.all(np.abs(got - ref) <= bf16_ulp(ref))
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_gmm_nvfp4_general_e4m3_scales(kernel):
+    # NVFP4 weights whose per-16 scales are arbitrary E4M3 values (not only
+    # the powers of two the lossless cast produces), mixed per chunk
+    p = make_problem(T=96, k=4, E=8, K=512, N=256, seed=250, routing="zipf")
+    rng = np.random.default_rng(251)
+    bs = rng.integers(0x20, 0x50, size=(8, 256, 32)).astype(np.uint8)
+    bs[:, :, 8:16] &= 0xF8                        # some chunks hold only powers of two
+    p["block_scales"] = bs
+    p["tensor_scale"] = np.ldexp(1.0, rng.integers(-4, 4, size=8)).astype(np.float32)
+    w, packed = weights_for(p, "nvfp4")
+    _, y = run_gpu(p, packed, "nvfp4", kernel=kernel)
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    ref = oracle.gmm(p["x"], ref_r["sorted_token"], ref_r["group_offsets"], w)
+    assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
+
+
 def test_gmm_rows_past_bands_untouched_and_canary():
     # dropped pairs leave rows [group_offsets[E], M) unwritten; nothing is
     # written past the end of y
