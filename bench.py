@@ -40,7 +40,7 @@ WORKLOADS = {
 }
 KERNELS = {"auto": 0, "stream": 1, "tiled": 2}
 GMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_route_amd", "csrc", "gmm.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
 
 
 def gmm_source_hash():
@@ -121,6 +121,9 @@ def main():
     ap.add_argument("--kernel", default="auto", choices=sorted(KERNELS))
     ap.add_argument("--out-dtype", default=None, choices=["f32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-sized device buffer --steps times (a plain copy "
+                         "kernel of known size, to scale hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -131,6 +134,16 @@ def main():
     import torch
     import moe_grouped_gemm_route_amd as moe
     from moe_grouped_gemm_route_amd.synth import make_config
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps}), flush=True)
+        return
 
     cfg = WORKLOADS[args.workload]
     p = make_config(cfg)
