@@ -129,19 +129,20 @@ int mxfp4_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
  * each decoded weight exact in bf16, products exact, sums in f32.
  *
  * packed         mxfp4_encode output for (fmt, E, N, K).
- * x              bf16 [T, K] when row_index != NULL (row r reads
- *                x[row_index[r]]), else bf16 [M, K] already in band order.
+ * x              bf16 [x_rows, K]: the token rows when row_index != NULL
+ *                (band row r reads x[row_index[r]]), else the band-ordered
+ *                rows (x_rows >= M).
  * row_index      [M] int32 (moe_route_sort's sorted_token) or NULL.
  * group_offsets  [E+1] int32 device array from moe_route_sort.
  * M              rows of y (T*k).  Rows [group_offsets[E], M) are not written.
  * y              out [M, N], f32 or bf16 (round-to-nearest-even of the f32 sum).
- * Preconditions not checked: row_index values index rows of x; group_offsets
+ * Preconditions not checked: row_index values lie in [0, x_rows); group_offsets
  * is non-decreasing with group_offsets[0] = 0 and group_offsets[E] <= M.
  * Exact-decode domain: MXFP4 scale bytes 2..252 (block exponent -125..125).
- * Limits as mxfp4_encode; M <= 2^24.
+ * Limits as mxfp4_encode; M <= 2^24; x_rows * K * 2 < 2^31 bytes.
  */
 int moe_gmm(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
-            const uint16_t* x, const int32_t* row_index,
+            const uint16_t* x, int32_t x_rows, const int32_t* row_index,
             const int32_t* group_offsets, int32_t M, void* y, int y_dtype,
             void* stream);
 
@@ -149,7 +150,7 @@ int moe_gmm(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
  * (moe_gmm_kernel_t).  Every configuration computes the same sums in the same
  * order, so all of them return bitwise identical y. */
 int moe_gmm_ex(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
-               const uint16_t* x, const int32_t* row_index,
+               const uint16_t* x, int32_t x_rows, const int32_t* row_index,
                const int32_t* group_offsets, int32_t M, void* y, int y_dtype,
                int kernel, void* stream);
 

@@ -32,10 +32,10 @@ _SIGNATURES = {
     "moe_route_sort": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_packed_weight_bytes": (_sz, [ctypes.c_int, _i32, _i32, _i32]),
     "mxfp4_encode": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
-    "moe_gmm": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp,
-                               ctypes.c_int, _vp]),
-    "moe_gmm_ex": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp,
-                                  ctypes.c_int, ctypes.c_int, _vp]),
+    "moe_gmm": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32,
+                               _vp, ctypes.c_int, _vp]),
+    "moe_gmm_ex": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32,
+                                  _vp, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_combine": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _i32, _i32, _i32, _vp,
                                    ctypes.c_int, _vp]),
     "moe_mxfp4_to_nvfp4": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
@@ -173,7 +173,7 @@ def moe_gmm(packed, fmt, E, N, K, x, group_offsets, M, row_index=None, out_dtype
         _dev(out, dt, "out", 2)
         if tuple(out.shape) != (M, N):
             raise MoeGmmError("out must be [M, N]")
-    _check(library().moe_gmm_ex(_ptr(packed), fmt, E, N, K, _ptr(xb), _ptr(row_index),
+    _check(library().moe_gmm_ex(_ptr(packed), fmt, E, N, K, _ptr(xb), xb.shape[0], _ptr(row_index),
                                 _ptr(group_offsets), M, _ptr(out), out_dtype, kernel, _stream()))
     return out
 

@@ -21,6 +21,9 @@
 //
 // Both kernels below issue, for every output element, the same MFMAs in the
 // same order (chunks ascending, steps 0..3), so they return identical bits.
+#include <stdlib.h>
+#include <string.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -171,100 +174,114 @@ __device__ __forceinline__ void store_tile(void* y, int64_t N, int row0, int row
   }
 }
 
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+constexpr int BUF_NT = 2;                  // buffer-load cache policy: non-temporal
+constexpr uint32_t BUF_OOB = 0x7FFF0000u;  // a lane offset that reads zeros
+
 // ---------------------------------------------------------------------------
 // Weight-streaming kernel, for bands of a few rows (decode).  Each wave owns
-// NS 16-column subtiles and all 16*MS rows of its tile; there is no LDS and
-// no barrier.  Codes are double-buffered in registers one chunk ahead.
-// Activation fragments come straight from global memory (they are tiny and
-// shared by every N tile, so they live in L2).
+// NS 16-column subtiles and the 16 rows of one tile, walks the whole K, and
+// has no LDS and no barrier.
+//
+// Pipelining.  A wave's vector loads complete in issue order, so waiting for
+// one load also waits for every load issued before it.  The activations of a
+// step are therefore loaded together with its codes, D steps ahead, into a
+// ring of D register slots: step kc reads slot kc % D, then refills it with
+// step kc + D.  Waiting for step kc's data then never waits for a later
+// step's, and D steps of codes stay in flight.  Codes, scale words and
+// activations go through buffer loads (base in scalar registers, 32-bit
+// lane offsets); activation rows past the band read zeros from outside the
+// buffer.
 // ---------------------------------------------------------------------------
-template <int MS, int NS, int FMT, bool OBF16>
+template <int NS, int D, int FMT, bool OBF16>
 __global__ __launch_bounds__(256) void gmm_stream_kernel(const uint8_t* __restrict__ packed, Layout L,
                                                          const uint16_t* __restrict__ x,
+                                                         uint32_t x_bytes,
                                                          const int32_t* __restrict__ row_index,
                                                          const int32_t* __restrict__ goff, int E,
                                                          void* __restrict__ y, int NB) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const TileScan ts = scan_tiles(goff, E, 16 * MS);
+  const TileScan ts = scan_tiles(goff, E, 16);
   const int item = work_item(ts.total * NB, false);
   if (item < 0) return;
   const int t = item / NB;
   const int nb = item - t * NB;
-  const Tile tile = locate_tile(goff, E, 16 * MS, ts, t);
+  const Tile tile = locate_tile(goff, E, 16, ts, t);
   const int n0 = (nb * 4 + wave) * NS * 16;
   if (n0 >= L.N) return;
   const int K = (int)L.K;
   const int KC = (int)L.KC;
+  const int groups = (int)L.groups;
   const int r = lane & 15;
   const int g = lane >> 4;
-  const int nsub = (tile.rows + 15) >> 4;
 
-  const u32x4_t* xp[MS];
-  bool xv[MS];
-#pragma unroll
-  for (int ms = 0; ms < MS; ++ms) {
-    const int rl = ms * 16 + r;
-    xv[ms] = rl < tile.rows;
-    const int row = tile.m0 + (xv[ms] ? rl : 0);
+  const int64_t et = (int64_t)tile.e * L.NT + (n0 >> 4);
+  const __amdgpu_buffer_rsrc_t cr = buffer_rsrc(packed + ((et * L.KC) << 10), (uint32_t)(NS * KC) << 10);
+  const __amdgpu_buffer_rsrc_t sr =
+      buffer_rsrc(packed + L.scales_off + et * L.groups * 256, (uint32_t)(NS * groups) * 256);
+  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, x_bytes);
+  const uint32_t c_voff = lane * 16;
+  const uint32_t s_voff = lane * 4;
+  uint32_t a_voff = BUF_OOB;
+  if (r < tile.rows) {
+    const int row = tile.m0 + r;
     const int64_t src = row_index ? row_index[row] : row;
-    xp[ms] = reinterpret_cast<const u32x4_t*>(x + src * K + g * 32);
-  }
-  const u32x4_t* cp[NS];
-  const uint32_t* sp[NS];
-#pragma unroll
-  for (int ns = 0; ns < NS; ++ns) {
-    const int64_t et = (int64_t)tile.e * L.NT + (n0 >> 4) + ns;
-    cp[ns] = reinterpret_cast<const u32x4_t*>(packed + ((et * L.KC) << 10)) + lane;
-    sp[ns] = reinterpret_cast<const uint32_t*>(packed + L.scales_off) + et * L.groups * 64 + lane;
+    a_voff = (uint32_t)(src * K * 2 + g * 64);
   }
 
-  f32x4_t acc[MS][NS];
+  u32x4_t cring[D][NS];
+  uint32_t sring[D][NS];
+  u32x4_t aring[D][4];
+  auto load_step = [&](int slot, int kc) {
 #pragma unroll
-  for (int ms = 0; ms < MS; ++ms)
+    for (int q = 0; q < 4; ++q)
+      aring[slot][q] = __builtin_amdgcn_raw_buffer_load_b128(xr, a_voff, kc * 256 + q * 16, 0);
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ns = 0; ns < NS; ++ns) {
+      cring[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, (ns * KC + kc) << 10, BUF_NT);
+      const int rec = FMT == 0 ? (kc >> 2) : (kc >> 1);
+      sring[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (ns * groups + rec) * 256, 0);
+    }
+  };
 
-  u32x4_t cnext[NS];
+  f32x4_t acc[NS];
 #pragma unroll
-  for (int ns = 0; ns < NS; ++ns) cnext[ns] = __builtin_nontemporal_load(cp[ns]);
-  uint32_t sw[NS];
+  for (int ns = 0; ns < NS; ++ns) acc[ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < KC) load_step(d, d);
 
-  for (int kc = 0; kc < KC; ++kc) {
-    u32x4_t c[NS];
+  for (int k0 = 0; k0 < KC; k0 += D) {
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) c[ns] = cnext[ns];
-    if (kc + 1 < KC) {
+    for (int d = 0; d < D; ++d) {
+      const int kc = k0 + d;
+      if (kc < KC) {
+        u32x4_t c[NS], a[4];
+        uint32_t w[NS];
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns) cnext[ns] = __builtin_nontemporal_load(cp[ns] + (kc + 1) * 64);
-    }
-    if (new_scale_record<FMT>(kc)) {
+        for (int ns = 0; ns < NS; ++ns) {
+          c[ns] = cring[d][ns];
+          w[ns] = sring[d][ns];
+        }
 #pragma unroll
-      for (int ns = 0; ns < NS; ++ns) sw[ns] = sp[ns][scale_record<FMT>(kc) * 64];
-    }
-    u32x4_t a[MS][4];
+        for (int q = 0; q < 4; ++q) a[q] = aring[d][q];
+        if (kc + D < KC) load_step(d, kc + D);
+        float lo[NS], hi[NS];
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms) {
-      if (ms < nsub) {
+        for (int ns = 0; ns < NS; ++ns) chunk_scales<FMT>(w[ns], kc, lo[ns], hi[ns]);
+        const bool general = general_scales<FMT, NS>(lo, hi);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          a[ms][s] = xv[ms] ? xp[ms][kc * 16 + s] : u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-    float lo[NS], hi[NS];
+        for (int s = 0; s < 4; ++s) {
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) chunk_scales<FMT>(sw[ns], kc, lo[ns], hi[ns]);
-    const bool general = general_scales<FMT, NS>(lo, hi);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4_t b[NS];
-#pragma unroll
-      for (int ns = 0; ns < NS; ++ns) b[ns] = decode_step<FMT>(c[ns][s], s < 2 ? lo[ns] : hi[ns], general);
-#pragma unroll
-      for (int ms = 0; ms < MS; ++ms) {
-        if (ms < nsub) {
-#pragma unroll
-          for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = mfma(as_bf16x8(a[ms][s]), as_bf16x8(b[ns]), acc[ms][ns]);
+          for (int ns = 0; ns < NS; ++ns) {
+            const u32x4_t b = decode_step<FMT>(c[ns][s], s < 2 ? lo[ns] : hi[ns], general);
+            acc[ns] = mfma(as_bf16x8(a[s]), as_bf16x8(b), acc[ns]);
+          }
         }
       }
     }
@@ -272,14 +289,8 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(const uint8_t* __restri
 
   const float post = FMT == 1 ? reinterpret_cast<const float*>(packed + L.tscale_off)[tile.e] : 1.0f;
 #pragma unroll
-  for (int ms = 0; ms < MS; ++ms) {
-    if (ms < nsub) {
-#pragma unroll
-      for (int ns = 0; ns < NS; ++ns)
-        store_tile<OBF16>(y, L.N, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + ns * 16 + r,
-                          acc[ms][ns], post);
-    }
-  }
+  for (int ns = 0; ns < NS; ++ns)
+    store_tile<OBF16>(y, L.N, tile.m0, tile.rows, n0 + ns * 16 + r, acc[ns], post);
 }
 
 // ---------------------------------------------------------------------------
@@ -440,21 +451,55 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
 // wave), so the grid is an upper bound: ceil(M / BM) + min(E, M) tiles, and
 // workgroups past the real tile count return at once.
 // ---------------------------------------------------------------------------
-constexpr int ST_MS = 1;
-constexpr int ST_NS = 2;
+// Stream-kernel shape: NS 16-column subtiles per wave and ring depth D.
+// 4x2 measured best on MI355X for the 64-token gate/up and 256-token down
+// projections (fewer, longer waves amortise the tile lookup and activation
+// loads over 64 columns).  MOEGMM_STREAM=<NS>x<D> selects another compiled
+// shape (for sweeps).
+static int stream_shape() {
+  static int v = [] {
+    const char* s = getenv("MOEGMM_STREAM");
+    if (!s) return 42;
+    const int ns = atoi(s);
+    const char* xp = strchr(s, 'x');
+    const int d = xp ? atoi(xp + 1) : 2;
+    return ns * 10 + d;
+  }();
+  return v;
+}
+
+template <int NS, int D, int FMT, bool OBF16>
+static void launch_stream(const uint8_t* packed, const Layout& L, const uint16_t* x, uint32_t x_bytes,
+                          const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
+                          void* y, hipStream_t stream) {
+  const int NB = (int)((L.N + 64 * NS - 1) / (64 * NS));
+  const int64_t em = E < M ? E : M;
+  const int64_t tiles = (M + 15) / 16 + em;
+  hipLaunchKernelGGL((gmm_stream_kernel<NS, D, FMT, OBF16>), dim3((unsigned)(tiles * NB)),
+                     dim3(256), 0, stream, packed, L, x, x_bytes, row_index, goff, E, y, NB);
+}
 
 template <int FMT, bool OBF16>
-static void launch_gmm_t(const uint8_t* packed, const Layout& L, const uint16_t* x,
+static void launch_gmm_t(const uint8_t* packed, const Layout& L, const uint16_t* x, int32_t x_rows,
                          const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
                          void* y, int kernel, hipStream_t stream) {
-  const int64_t em = E < M ? E : M;
+  const uint32_t x_bytes = (uint32_t)((int64_t)x_rows * L.K * 2);
   if (kernel == 1) {
-    constexpr int BM = 16 * ST_MS;
-    const int NB = (int)((L.N + 64 * ST_NS - 1) / (64 * ST_NS));
-    const int64_t tiles = (M + BM - 1) / BM + em;
-    hipLaunchKernelGGL((gmm_stream_kernel<ST_MS, ST_NS, FMT, OBF16>), dim3((unsigned)(tiles * NB)),
-                       dim3(256), 0, stream, packed, L, x, row_index, goff, E, y, NB);
+    // NS * 16 columns per wave must divide N (N is a multiple of 64).
+    int shape = stream_shape();
+    if (L.N % (16 * (shape / 10)) != 0) shape = 42;
+    switch (shape) {
+      case 21: launch_stream<2, 1, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
+      case 24: launch_stream<2, 4, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
+      case 42: launch_stream<4, 2, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
+      case 43: launch_stream<4, 3, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
+      case 12: launch_stream<1, 2, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
+      case 14: launch_stream<1, 4, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
+      case 22: launch_stream<2, 2, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
+      default: launch_stream<4, 2, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
+    }
   } else {
+    const int64_t em = E < M ? E : M;
     const int NB = (int)((L.N + TL_BN - 1) / TL_BN);
     const int64_t tiles = (M + TL_BM - 1) / TL_BM + em;
     hipLaunchKernelGGL((gmm_tiled_kernel<FMT, OBF16>), dim3((unsigned)(tiles * NB)), dim3(256), 0,
@@ -463,15 +508,16 @@ static void launch_gmm_t(const uint8_t* packed, const Layout& L, const uint16_t*
 }
 
 hipError_t launch_gmm(const uint8_t* packed, int fmt, int32_t E, int32_t N, int32_t K,
-                      const uint16_t* x, const int32_t* row_index, const int32_t* group_offsets,
+                      const uint16_t* x, int32_t x_rows, const int32_t* row_index,
+                      const int32_t* group_offsets,
                       int32_t M, void* y, int y_bf16, int kernel, hipStream_t stream) {
   const Layout L = make_layout(fmt, E, N, K);
   if (fmt == 0) {
-    if (y_bf16) launch_gmm_t<0, true>(packed, L, x, row_index, group_offsets, E, M, y, kernel, stream);
-    else launch_gmm_t<0, false>(packed, L, x, row_index, group_offsets, E, M, y, kernel, stream);
+    if (y_bf16) launch_gmm_t<0, true>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, kernel, stream);
+    else launch_gmm_t<0, false>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, kernel, stream);
   } else {
-    if (y_bf16) launch_gmm_t<1, true>(packed, L, x, row_index, group_offsets, E, M, y, kernel, stream);
-    else launch_gmm_t<1, false>(packed, L, x, row_index, group_offsets, E, M, y, kernel, stream);
+    if (y_bf16) launch_gmm_t<1, true>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, kernel, stream);
+    else launch_gmm_t<1, false>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, kernel, stream);
   }
   return hipGetLastError();
 }

@@ -24,7 +24,8 @@ hipError_t launch_mxfp4_to_nvfp4(const uint8_t* scales, int32_t E, int32_t N, in
 
 // kernel: 1 = weight-streaming waves, 2 = LDS-tiled activations.
 hipError_t launch_gmm(const uint8_t* packed, int fmt, int32_t E, int32_t N, int32_t K,
-                      const uint16_t* x, const int32_t* row_index, const int32_t* group_offsets,
+                      const uint16_t* x, int32_t x_rows, const int32_t* row_index,
+                      const int32_t* group_offsets,
                       int32_t M, void* y, int y_bf16, int kernel, hipStream_t stream);
 
 hipError_t launch_combine(const void* y, int y_bf16, const float* w, const int32_t* pair_row,

@@ -80,7 +80,8 @@ def test_encode_validation(lib):
 def test_gmm_validation(lib):
     f = lib.moe_gmm_ex
     args = lambda **kw: [kw.get("packed", FAKE_ALIGNED), kw.get("fmt", 0), kw.get("E", 8),
-                         kw.get("N", 512), kw.get("K", 256), kw.get("x", FAKE_ALIGNED), None,
+                         kw.get("N", 512), kw.get("K", 256), kw.get("x", FAKE_ALIGNED),
+                         kw.get("x_rows", 128), None,
                          kw.get("off", FAKE), kw.get("M", 128), kw.get("y", FAKE),
                          kw.get("dt", 0), kw.get("kernel", 0), None]
     assert f(*args(packed=None)) == ERR_NULL
@@ -95,7 +96,10 @@ def test_gmm_validation(lib):
     assert f(*args(dt=2)) == ERR_FORMAT
     assert f(*args(kernel=3)) == ERR_FORMAT
     assert f(*args(packed=ctypes.c_void_p((1 << 30) + 128))) == ERR_SHAPE
-    assert lib.moe_gmm(None, 0, 8, 512, 256, FAKE, None, FAKE, 128, FAKE, 0, None) == ERR_NULL
+    assert f(*args(x_rows=0)) == ERR_SHAPE
+    assert f(*args(x_rows=127)) == ERR_SHAPE        # band input needs x_rows >= M
+    assert f(*args(x_rows=1 << 22, K=512)) == ERR_SHAPE   # 4 GiB of activations
+    assert lib.moe_gmm(None, 0, 8, 512, 256, FAKE, 128, None, FAKE, 128, FAKE, 0, None) == ERR_NULL
 
 
 def test_combine_validation(lib):
