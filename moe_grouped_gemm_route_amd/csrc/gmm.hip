@@ -325,6 +325,77 @@ __device__ __forceinline__ void stage_chunk(uint8_t* buf, const uint8_t* const (
   }
 }
 
+// The K walk of one tiled workgroup for a tile with NSUB valid 16-row
+// subtiles (a compile-time count, so the inner loops carry no branches and
+// the compiler can batch the LDS fragment reads ahead of the MFMAs).
+//
+// Per 128-deep chunk kc: issue the activation copy of chunk kc+1 (direct to
+// LDS), the codes of chunk kc+1 and the scale words of chunk kc+1, then
+// compute chunk kc from registers and LDS filled one iteration earlier, then
+// one barrier.  Nothing loaded in an iteration is consumed before that
+// iteration's barrier, so no wait inside the compute phase touches the
+// loads in flight.
+template <int NSUB, int FMT>
+__device__ __forceinline__ void tiled_k_walk(uint8_t (*s_a)[TL_BUF_BYTES], const uint8_t* const (&ap)[TL_LOADS],
+                                             const bool (&av)[TL_LOADS], const u32x4_t* const (&cp)[TL_NS],
+                                             const uint32_t* const (&sp)[TL_NS], bool wave_active, int KC,
+                                             int wave, const int (&aoff)[4],
+                                             f32x4_t (&acc)[TL_MS][TL_NS]) {
+  u32x4_t c[TL_NS];
+  uint32_t sw[TL_NS];
+  if (wave_active) {
+#pragma unroll
+    for (int ns = 0; ns < TL_NS; ++ns) {
+      c[ns] = __builtin_nontemporal_load(cp[ns]);
+      sw[ns] = sp[ns][0];
+    }
+  }
+  __syncthreads();
+  for (int kc = 0; kc < KC; ++kc) {
+    const int buf = kc & 1;
+    const bool more = kc + 1 < KC;
+    if (more) stage_chunk(s_a[buf ^ 1], ap, av, kc + 1, wave);
+    u32x4_t cn[TL_NS];
+    uint32_t swn[TL_NS];
+    if (wave_active && more) {
+#pragma unroll
+      for (int ns = 0; ns < TL_NS; ++ns) {
+        cn[ns] = __builtin_nontemporal_load(cp[ns] + (kc + 1) * 64);
+        swn[ns] = sp[ns][scale_record<FMT>(kc + 1) * 64];
+      }
+    }
+    if (wave_active) {
+      float lo[TL_NS], hi[TL_NS];
+#pragma unroll
+      for (int ns = 0; ns < TL_NS; ++ns) chunk_scales<FMT>(sw[ns], kc, lo[ns], hi[ns]);
+      const bool general = general_scales<FMT, TL_NS>(lo, hi);
+      const uint8_t* abase = s_a[buf];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4_t a[NSUB];
+#pragma unroll
+        for (int ms = 0; ms < NSUB; ++ms)
+          a[ms] = *reinterpret_cast<const u32x4_t*>(abase + ms * 16 * TL_ROW_BYTES + aoff[s]);
+        u32x4_t b[TL_NS];
+#pragma unroll
+        for (int ns = 0; ns < TL_NS; ++ns) b[ns] = decode_step<FMT>(c[ns][s], s < 2 ? lo[ns] : hi[ns], general);
+#pragma unroll
+        for (int ms = 0; ms < NSUB; ++ms)
+#pragma unroll
+          for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = mfma(as_bf16x8(a[ms]), as_bf16x8(b[ns]), acc[ms][ns]);
+      }
+    }
+    if (wave_active && more) {
+#pragma unroll
+      for (int ns = 0; ns < TL_NS; ++ns) {
+        c[ns] = cn[ns];
+        sw[ns] = swn[ns];
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <int FMT, bool OBF16>
 __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __restrict__ packed, Layout L,
                                                            const uint16_t* __restrict__ x,
@@ -372,6 +443,10 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
     cp[ns] = reinterpret_cast<const u32x4_t*>(packed + ((et * L.KC) << 10)) + lane;
     sp[ns] = reinterpret_cast<const uint32_t*>(packed + L.scales_off) + et * L.groups * 64 + lane;
   }
+  // fragment read offsets: row ms*16 + r, logical segment g*4 + s
+  int aoff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aoff[s] = r * TL_ROW_BYTES + (((g * 4 + s) ^ r) << 4);
 
   f32x4_t acc[TL_MS][TL_NS];
 #pragma unroll
@@ -379,58 +454,16 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: chunk 0 -> LDS buffer 0, codes of chunk 0 -> registers
   stage_chunk(s_a[0], ap, av, 0, wave);
-  u32x4_t cnext[TL_NS];
-  if (wave_active) {
-#pragma unroll
-    for (int ns = 0; ns < TL_NS; ++ns) cnext[ns] = __builtin_nontemporal_load(cp[ns]);
-  }
-  uint32_t sw[TL_NS];
-  __syncthreads();
-
-  // fragment read offsets: row ms*16 + r, logical segment g*4 + s
-  int aoff[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) aoff[s] = r * TL_ROW_BYTES + (((g * 4 + s) ^ r) << 4);
-
-  for (int kc = 0; kc < KC; ++kc) {
-    const int buf = kc & 1;
-    const bool more = kc + 1 < KC;
-    if (more) stage_chunk(s_a[buf ^ 1], ap, av, kc + 1, wave);
-    if (wave_active) {
-      u32x4_t c[TL_NS];
-#pragma unroll
-      for (int ns = 0; ns < TL_NS; ++ns) c[ns] = cnext[ns];
-      if (more) {
-#pragma unroll
-        for (int ns = 0; ns < TL_NS; ++ns) cnext[ns] = __builtin_nontemporal_load(cp[ns] + (kc + 1) * 64);
-      }
-      if (new_scale_record<FMT>(kc)) {
-#pragma unroll
-        for (int ns = 0; ns < TL_NS; ++ns) sw[ns] = sp[ns][scale_record<FMT>(kc) * 64];
-      }
-      float lo[TL_NS], hi[TL_NS];
-#pragma unroll
-      for (int ns = 0; ns < TL_NS; ++ns) chunk_scales<FMT>(sw[ns], kc, lo[ns], hi[ns]);
-      const bool general = general_scales<FMT, TL_NS>(lo, hi);
-      const uint8_t* abase = s_a[buf];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        u32x4_t b[TL_NS];
-#pragma unroll
-        for (int ns = 0; ns < TL_NS; ++ns) b[ns] = decode_step<FMT>(c[ns][s], s < 2 ? lo[ns] : hi[ns], general);
-#pragma unroll
-        for (int ms = 0; ms < TL_MS; ++ms) {
-          if (ms < nsub) {
-            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(abase + ms * 16 * TL_ROW_BYTES + aoff[s]);
-#pragma unroll
-            for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = mfma(as_bf16x8(a), as_bf16x8(b[ns]), acc[ms][ns]);
-          }
-        }
-      }
-    }
-    __syncthreads();
+  switch (nsub) {
+    case 1: tiled_k_walk<1, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
+    case 2: tiled_k_walk<2, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
+    case 3: tiled_k_walk<3, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
+    case 4: tiled_k_walk<4, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
+    case 5: tiled_k_walk<5, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
+    case 6: tiled_k_walk<6, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
+    case 7: tiled_k_walk<7, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
+    default: tiled_k_walk<8, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
   }
 
   if (!wave_active) return;
@@ -446,11 +479,6 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
   }
 }
 
-// ---------------------------------------------------------------------------
-// Launch.  Tile lists live on the device (built from group_offsets by each
-// wave), so the grid is an upper bound: ceil(M / BM) + min(E, M) tiles, and
-// workgroups past the real tile count return at once.
-// ---------------------------------------------------------------------------
 // Stream-kernel shape: NS 16-column subtiles per wave and ring depth D.
 // 4x2 measured best on MI355X for the 64-token gate/up and 256-token down
 // projections (fewer, longer waves amortise the tile lookup and activation

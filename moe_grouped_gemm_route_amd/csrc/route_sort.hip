@@ -3,93 +3,113 @@
 // that v6e can't hold": tokens sorted by expert, one band of rows per
 // expert).
 //
-// One workgroup of 512 threads (8 wave64s):
-//   1. histogram of expert ids in LDS (integer counts: the order of the LDS
-//      increments cannot change them);
-//   2. exclusive scan of the counts -> band starts (one wave, 16 experts per
-//      lane, then a wavefront scan);
-//   3. stable scatter, 512 pairs per round in pair order.  Inside a wave the
-//      lanes holding the same expert are found with ballots over the id bits;
-//      a lane's rank is the number of such lanes below it.  Per-wave counts
-//      go to LDS, and the waves' offsets are summed in wave order, so every
-//      position comes from counts and scans, not from atomics.
+// G workgroups of 8 wave64s; workgroup g owns the contiguous pair segment
+// [g*S, (g+1)*S) and wave w of it the sub-segment [g*S + w*S8, ... + S8).
+//   1. histograms (integer counts, so the order of the LDS increments cannot
+//      change them): over all M pairs, tot[e]; over the pairs before the
+//      segment, bef[e]; over each wave's sub-segment, cnt[w][e];
+//   2. scan: band starts off[e] = sum of tot over experts < e, and each
+//      wave's cursor cur[w][e] = off[e] + bef[e] + sum over w' < w of
+//      cnt[w'][e];
+//   3. place: each wave walks its sub-segment 64 pairs at a time in pair
+//      order; lanes holding the same expert are found with ballots over the
+//      id bits; a pair's row is cur[w][e] + the number of such lanes below
+//      it, and the lowest such lane advances cur[w][e].
+// Rows are ordered by expert, then by pair index; every position comes from
+// counts, scans and lane order.  Workgroup 0 writes group_offsets, the
+// error count and the -1 rows past the last band.
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
 
-constexpr int RS_THREADS = 512;
-constexpr int RS_WAVES = RS_THREADS / 64;
-constexpr int RS_EMAX = 1024;
+constexpr int RS_WAVES = 8;
+constexpr int RS_THREADS = RS_WAVES * 64;
+constexpr int RS_SEGMENT = 2048;     // pairs placed per workgroup (large M)
+constexpr int RS_MAX_GROUPS = 64;
 
 __global__ __launch_bounds__(RS_THREADS) void route_sort_kernel(
-    const int32_t* __restrict__ ids, int32_t M, int32_t k, int32_t E, int32_t id_bits,
+    const int32_t* __restrict__ ids, int32_t M, int32_t k, int32_t E, int32_t id_bits, int32_t S,
     int32_t* __restrict__ group_offsets, int32_t* __restrict__ sorted_token,
     int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_row,
     int32_t* __restrict__ err_count) {
-  __shared__ int32_t s_base[RS_EMAX];
-  __shared__ int32_t s_wave_cnt[RS_WAVES][RS_EMAX];
+  extern __shared__ int32_t s_mem[];
+  int32_t* s_tot = s_mem;                 // [E]
+  int32_t* s_bef = s_mem + E;             // [E]
+  int32_t* s_cnt = s_mem + 2 * E;         // [RS_WAVES][E], later the cursors
   __shared__ int32_t s_bad;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int seg_begin = min(M, (int)blockIdx.x * S);
+  const int seg_end = min(M, seg_begin + S);
+  const int S8 = (S + RS_WAVES - 1) / RS_WAVES;
+  const int w_begin = min(seg_end, seg_begin + wave * S8);
+  const int w_end = min(seg_end, w_begin + S8);
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
-  for (int e = tid; e < E; e += RS_THREADS) {
-    s_base[e] = 0;
-    for (int w = 0; w < RS_WAVES; ++w) s_wave_cnt[w][e] = 0;
-  }
+  for (int i = tid; i < (2 + RS_WAVES) * E; i += RS_THREADS) s_mem[i] = 0;
   if (tid == 0) s_bad = 0;
   __syncthreads();
 
-  // 1. histogram
+  // 1. histograms
   int bad = 0;
   for (int p = tid; p < M; p += RS_THREADS) {
     const int e = ids[p];
-    if (e >= 0 && e < E) atomicAdd(&s_base[e], 1);
-    else ++bad;
+    if (e >= 0 && e < E) {
+      atomicAdd(&s_tot[e], 1);
+      if (p < seg_begin) atomicAdd(&s_bef[e], 1);
+    } else {
+      ++bad;
+    }
   }
-  if (bad) atomicAdd(&s_bad, bad);
+  int32_t* cnt = s_cnt + wave * E;
+  for (int p = w_begin + lane; p < w_end; p += 64) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  for (int d = 32; d > 0; d >>= 1) bad += __shfl_xor(bad, d, 64);
+  if (lane == 0 && bad) atomicAdd(&s_bad, bad);
   __syncthreads();
 
-  // 2. exclusive scan over experts (wave 0)
+  // 2. scan (wave 0): band starts and per-wave cursors
   if (wave == 0) {
-    constexpr int PER = RS_EMAX / 64;
-    int local[PER];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = lane * PER + i;
-      local[i] = e < E ? s_base[e] : 0;
-      sum += local[i];
+    const int per = (E + 63) >> 6;
+    int mine = 0;
+    for (int i = 0; i < per; ++i) {
+      const int e = lane * per + i;
+      if (e < E) mine += s_tot[e];
     }
-    int incl = sum;
-#pragma unroll
+    int incl = mine;
     for (int d = 1; d < 64; d <<= 1) {
       const int v = __shfl_up(incl, d, 64);
       if (lane >= d) incl += v;
     }
-    int run = incl - sum;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = lane * PER + i;
+    int run = incl - mine;
+    for (int i = 0; i < per; ++i) {
+      const int e = lane * per + i;
       if (e < E) {
-        s_base[e] = run;
-        group_offsets[e] = run;
+        if (blockIdx.x == 0) group_offsets[e] = run;
+        int c = run + s_bef[e];
+        for (int w = 0; w < RS_WAVES; ++w) {
+          const int n = s_cnt[w * E + e];
+          s_cnt[w * E + e] = c;
+          c += n;
+        }
+        run += s_tot[e];
       }
-      run += local[i];
     }
-    if (lane == 63) group_offsets[E] = incl;
+    if (blockIdx.x == 0 && lane == 63) group_offsets[E] = incl;
   }
   __syncthreads();
 
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-
-  // 3. stable scatter, one round of RS_THREADS pairs at a time
-  for (int p0 = 0; p0 < M; p0 += RS_THREADS) {
-    const int p = p0 + tid;
-    const int e = p < M ? ids[p] : -1;
-    const bool valid = e >= 0 && e < E;
+  // 3. place this wave's sub-segment in pair order
+  for (int p0 = w_begin; p0 < w_end; p0 += 64) {
+    const int p = p0 + lane;
+    const bool in_seg = p < w_end;
+    const int e = in_seg ? ids[p] : -1;
+    const bool valid = in_seg && e >= 0 && e < E;
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < id_bits; ++b) {
       const bool bit = valid && ((e >> b) & 1);
@@ -97,41 +117,29 @@ __global__ __launch_bounds__(RS_THREADS) void route_sort_kernel(
       peers &= bit ? m : ~m;
     }
     const int rank = __popcll(peers & lt_mask);
-    const bool leader = valid && rank == 0;
-    if (leader) s_wave_cnt[wave][e] = __popcll(peers);
-    __syncthreads();
-    if (p < M) {
-      if (valid) {
-        int pos = s_base[e] + rank;
-        for (int w = 0; w < wave; ++w) pos += s_wave_cnt[w][e];
-        sorted_token[pos] = p / k;
-        sorted_pair[pos] = p;
-        pair_row[p] = pos;
-      } else {
-        pair_row[p] = -1;
-      }
+    if (valid) {
+      const int pos = cnt[e] + rank;
+      sorted_token[pos] = p / k;
+      sorted_pair[pos] = p;
+      pair_row[p] = pos;
+    } else if (in_seg) {
+      pair_row[p] = -1;
     }
-    __syncthreads();
-    // advance band cursors by this round's counts, clear the per-wave counts
-    for (int x = tid; x < E; x += RS_THREADS) {
-      int add = 0;
-#pragma unroll
-      for (int w = 0; w < RS_WAVES; ++w) {
-        add += s_wave_cnt[w][x];
-        s_wave_cnt[w][x] = 0;
-      }
-      s_base[x] += add;
-    }
-    __syncthreads();
+    // every lane has read its cursor before the leaders advance them
+    __builtin_amdgcn_wave_barrier();
+    if (valid && rank == 0) cnt[e] += __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
   }
 
-  // rows past the last band belong to dropped pairs
-  const int valid_rows = M - s_bad;
-  for (int r = valid_rows + tid; r < M; r += RS_THREADS) {
-    sorted_token[r] = -1;
-    sorted_pair[r] = -1;
+  if (blockIdx.x == 0) {
+    // rows past the last band belong to dropped pairs
+    const int valid_rows = M - s_bad;
+    for (int r = valid_rows + tid; r < M; r += RS_THREADS) {
+      sorted_token[r] = -1;
+      sorted_pair[r] = -1;
+    }
+    if (tid == 0 && err_count) *err_count = s_bad;
   }
-  if (tid == 0 && err_count) *err_count = s_bad;
 }
 
 hipError_t launch_route_sort(const int32_t* ids, int32_t T, int32_t k, int32_t E,
@@ -139,8 +147,14 @@ hipError_t launch_route_sort(const int32_t* ids, int32_t T, int32_t k, int32_t E
                              int32_t* pair_row, int32_t* err_count, hipStream_t stream) {
   int bits = 0;
   while ((1 << bits) < E) ++bits;
-  hipLaunchKernelGGL(route_sort_kernel, dim3(1), dim3(RS_THREADS), 0, stream, ids, T * k, k, E,
-                     bits, group_offsets, sorted_token, sorted_pair, pair_row, err_count);
+  const int32_t M = T * k;
+  int groups = (M + RS_SEGMENT - 1) / RS_SEGMENT;
+  if (groups > RS_MAX_GROUPS) groups = RS_MAX_GROUPS;
+  if (groups < 1) groups = 1;
+  const int32_t S = (M + groups - 1) / groups;
+  const size_t lds = (size_t)(2 + RS_WAVES) * E * sizeof(int32_t);
+  hipLaunchKernelGGL(route_sort_kernel, dim3(groups), dim3(RS_THREADS), lds, stream, ids, M, k, E,
+                     bits, S, group_offsets, sorted_token, sorted_pair, pair_row, err_count);
   return hipGetLastError();
 }
 
