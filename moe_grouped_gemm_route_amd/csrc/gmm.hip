@@ -206,11 +206,17 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(const uint8_t* __restri
                                                          void* __restrict__ y, int NB) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  // Tiles are dealt round-robin to the 8 XCDs (the dispatcher deals
+  // consecutive workgroup ids round-robin), and each XCD walks all NB column
+  // groups of its tile before the next one: one expert's codes stream
+  // through one XCD in order, while the tiles of a popular expert spread
+  // over all XCDs and keep their work balanced.
   const TileScan ts = scan_tiles(goff, E, 16);
-  const int item = work_item(ts.total * NB, false);
-  if (item < 0) return;
-  const int t = item / NB;
-  const int nb = item - t * NB;
+  const int bx = blockIdx.x;
+  const int xcd = bx & 7, kth = bx >> 3;
+  const int t = xcd + 8 * (kth / NB);
+  const int nb = kth - (kth / NB) * NB;
+  if (t >= ts.total) return;
   const Tile tile = locate_tile(goff, E, 16, ts, t);
   const int n0 = (nb * 4 + wave) * NS * 16;
   if (n0 >= L.N) return;
@@ -502,7 +508,7 @@ static void launch_stream(const uint8_t* packed, const Layout& L, const uint16_t
                           void* y, hipStream_t stream) {
   const int NB = (int)((L.N + 64 * NS - 1) / (64 * NS));
   const int64_t em = E < M ? E : M;
-  const int64_t tiles = (M + 15) / 16 + em;
+  const int64_t tiles = ((M + 15) / 16 + em + 7) / 8 * 8;   // whole rounds of 8 tiles
   hipLaunchKernelGGL((gmm_stream_kernel<NS, D, FMT, OBF16>), dim3((unsigned)(tiles * NB)),
                      dim3(256), 0, stream, packed, L, x, x_bytes, row_index, goff, E, y, NB);
 }
