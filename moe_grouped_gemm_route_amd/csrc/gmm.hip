@@ -21,9 +21,6 @@
 //
 // Both kernels below issue, for every output element, the same MFMAs in the
 // same order (chunks ascending, steps 0..3), so they return identical bits.
-#include <stdlib.h>
-#include <string.h>
-
 #include "common.h"
 #include "launch.h"
 
@@ -184,8 +181,10 @@ constexpr uint32_t BUF_OOB = 0x7FFF0000u;  // a lane offset that reads zeros
 
 // ---------------------------------------------------------------------------
 // Weight-streaming kernel, for bands of a few rows (decode).  Each wave owns
-// NS 16-column subtiles and the 16 rows of one tile, walks the whole K, and
-// has no LDS and no barrier.
+// NS 16-column subtiles and up to MS 16-row subtiles of one tile (tiles are
+// MS * 16 rows), walks the whole K, and has no LDS and no barrier.  Every
+// code word loaded feeds one MFMA per row subtile, so a band of up to
+// MS * 16 rows streams its expert's codes once per column group.
 //
 // Pipelining.  A wave's vector loads complete in issue order, so waiting for
 // one load also waits for every load issued before it.  The activations of a
@@ -197,56 +196,27 @@ constexpr uint32_t BUF_OOB = 0x7FFF0000u;  // a lane offset that reads zeros
 // lane offsets); activation rows past the band read zeros from outside the
 // buffer.
 // ---------------------------------------------------------------------------
-template <int NS, int D, int FMT, bool OBF16>
-__global__ __launch_bounds__(256) void gmm_stream_kernel(const uint8_t* __restrict__ packed, Layout L,
-                                                         const uint16_t* __restrict__ x,
-                                                         uint32_t x_bytes,
-                                                         const int32_t* __restrict__ row_index,
-                                                         const int32_t* __restrict__ goff, int E,
-                                                         void* __restrict__ y, int NB) {
+template <int NS, int D, int MSUB, int FMT, bool OBF16>
+__device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, const Layout& L,
+                                            const Tile& tile, int n0, __amdgpu_buffer_rsrc_t xr,
+                                            const uint32_t (&a_voff)[2], __amdgpu_buffer_rsrc_t cr,
+                                            __amdgpu_buffer_rsrc_t sr, void* __restrict__ y) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  // Tiles are dealt round-robin to the 8 XCDs (the dispatcher deals
-  // consecutive workgroup ids round-robin), and each XCD walks all NB column
-  // groups of its tile before the next one: one expert's codes stream
-  // through one XCD in order, while the tiles of a popular expert spread
-  // over all XCDs and keep their work balanced.
-  const TileScan ts = scan_tiles(goff, E, 16);
-  const int bx = blockIdx.x;
-  const int xcd = bx & 7, kth = bx >> 3;
-  const int t = xcd + 8 * (kth / NB);
-  const int nb = kth - (kth / NB) * NB;
-  if (t >= ts.total) return;
-  const Tile tile = locate_tile(goff, E, 16, ts, t);
-  const int n0 = (nb * 4 + wave) * NS * 16;
-  if (n0 >= L.N) return;
-  const int K = (int)L.K;
+  const int r = lane & 15;
   const int KC = (int)L.KC;
   const int groups = (int)L.groups;
-  const int r = lane & 15;
-  const int g = lane >> 4;
-
-  const int64_t et = (int64_t)tile.e * L.NT + (n0 >> 4);
-  const __amdgpu_buffer_rsrc_t cr = buffer_rsrc(packed + ((et * L.KC) << 10), (uint32_t)(NS * KC) << 10);
-  const __amdgpu_buffer_rsrc_t sr =
-      buffer_rsrc(packed + L.scales_off + et * L.groups * 256, (uint32_t)(NS * groups) * 256);
-  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, x_bytes);
   const uint32_t c_voff = lane * 16;
   const uint32_t s_voff = lane * 4;
-  uint32_t a_voff = BUF_OOB;
-  if (r < tile.rows) {
-    const int row = tile.m0 + r;
-    const int64_t src = row_index ? row_index[row] : row;
-    a_voff = (uint32_t)(src * K * 2 + g * 64);
-  }
 
   u32x4_t cring[D][NS];
   uint32_t sring[D][NS];
-  u32x4_t aring[D][4];
+  u32x4_t aring[D][MSUB][4];
   auto load_step = [&](int slot, int kc) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      aring[slot][q] = __builtin_amdgcn_raw_buffer_load_b128(xr, a_voff, kc * 256 + q * 16, 0);
+    for (int ms = 0; ms < MSUB; ++ms)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        aring[slot][ms][q] = __builtin_amdgcn_raw_buffer_load_b128(xr, a_voff[ms], kc * 256 + q * 16, 0);
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
       cring[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, (ns * KC + kc) << 10, BUF_NT);
@@ -255,9 +225,11 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(const uint8_t* __restri
     }
   };
 
-  f32x4_t acc[NS];
+  f32x4_t acc[MSUB][NS];
 #pragma unroll
-  for (int ns = 0; ns < NS; ++ns) acc[ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int ms = 0; ms < MSUB; ++ms)
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int d = 0; d < D; ++d)
     if (d < KC) load_step(d, d);
@@ -267,7 +239,7 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(const uint8_t* __restri
     for (int d = 0; d < D; ++d) {
       const int kc = k0 + d;
       if (kc < KC) {
-        u32x4_t c[NS], a[4];
+        u32x4_t c[NS], a[MSUB][4];
         uint32_t w[NS];
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
@@ -275,7 +247,9 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(const uint8_t* __restri
           w[ns] = sring[d][ns];
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) a[q] = aring[d][q];
+        for (int ms = 0; ms < MSUB; ++ms)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) a[ms][q] = aring[d][ms][q];
         if (kc + D < KC) load_step(d, kc + D);
         float lo[NS], hi[NS];
 #pragma unroll
@@ -286,7 +260,9 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(const uint8_t* __restri
 #pragma unroll
           for (int ns = 0; ns < NS; ++ns) {
             const u32x4_t b = decode_step<FMT>(c[ns][s], s < 2 ? lo[ns] : hi[ns], general);
-            acc[ns] = mfma(as_bf16x8(a[s]), as_bf16x8(b), acc[ns]);
+#pragma unroll
+            for (int ms = 0; ms < MSUB; ++ms)
+              acc[ms][ns] = mfma(as_bf16x8(a[ms][s]), as_bf16x8(b), acc[ms][ns]);
           }
         }
       }
@@ -295,8 +271,59 @@ __global__ __launch_bounds__(256) void gmm_stream_kernel(const uint8_t* __restri
 
   const float post = FMT == 1 ? reinterpret_cast<const float*>(packed + L.tscale_off)[tile.e] : 1.0f;
 #pragma unroll
-  for (int ns = 0; ns < NS; ++ns)
-    store_tile<OBF16>(y, L.N, tile.m0, tile.rows, n0 + ns * 16 + r, acc[ns], post);
+  for (int ms = 0; ms < MSUB; ++ms)
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns)
+      store_tile<OBF16>(y, L.N, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + ns * 16 + r, acc[ms][ns], post);
+}
+
+template <int NS, int D, int MS, int FMT, bool OBF16>
+__global__ __launch_bounds__(256, 3) void gmm_stream_kernel(const uint8_t* __restrict__ packed, Layout L,
+                                                         const uint16_t* __restrict__ x,
+                                                         uint32_t x_bytes,
+                                                         const int32_t* __restrict__ row_index,
+                                                         const int32_t* __restrict__ goff, int E,
+                                                         void* __restrict__ y, int NB) {
+  constexpr int BM = 16 * MS;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Tiles are dealt round-robin to the 8 XCDs (the dispatcher deals
+  // consecutive workgroup ids round-robin), and each XCD walks all NB column
+  // groups of its tile before the next one: one expert's codes stream
+  // through one XCD in order, while the tiles of a popular expert spread
+  // over all XCDs and keep their work balanced.
+  const TileScan ts = scan_tiles(goff, E, BM);
+  const int bx = blockIdx.x;
+  const int xcd = bx & 7, kth = bx >> 3;
+  const int t = xcd + 8 * (kth / NB);
+  const int nb = kth - (kth / NB) * NB;
+  if (t >= ts.total) return;
+  const Tile tile = locate_tile(goff, E, BM, ts, t);
+  const int n0 = (nb * 4 + wave) * NS * 16;
+  if (n0 >= L.N) return;
+  const int K = (int)L.K;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+
+  const int64_t et = (int64_t)tile.e * L.NT + (n0 >> 4);
+  const __amdgpu_buffer_rsrc_t cr = buffer_rsrc(packed + ((et * L.KC) << 10), (uint32_t)(NS * L.KC) << 10);
+  const __amdgpu_buffer_rsrc_t sr =
+      buffer_rsrc(packed + L.scales_off + et * L.groups * 256, (uint32_t)(NS * L.groups) * 256);
+  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, x_bytes);
+  uint32_t a_voff[2] = {BUF_OOB, BUF_OOB};
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) {
+    const int rl = ms * 16 + r;
+    if (rl < tile.rows) {
+      const int row = tile.m0 + rl;
+      const int64_t src = row_index ? row_index[row] : row;
+      a_voff[ms] = (uint32_t)(src * K * 2 + g * 64);
+    }
+  }
+  if (MS == 2 && tile.rows > 16)
+    stream_walk<NS, (D > 1 ? D - 1 : 1), 2, FMT, OBF16>(packed, L, tile, n0, xr, a_voff, cr, sr, y);
+  else
+    stream_walk<NS, D, 1, FMT, OBF16>(packed, L, tile, n0, xr, a_voff, cr, sr, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -485,31 +512,20 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
   }
 }
 
-// Stream-kernel shape: NS 16-column subtiles per wave and ring depth D.
-// 4x2 measured best on MI355X for the 64-token gate/up and 256-token down
-// projections (fewer, longer waves amortise the tile lookup and activation
-// loads over 64 columns).  MOEGMM_STREAM=<NS>x<D> selects another compiled
-// shape (for sweeps).
-static int stream_shape() {
-  static int v = [] {
-    const char* s = getenv("MOEGMM_STREAM");
-    if (!s) return 42;
-    const int ns = atoi(s);
-    const char* xp = strchr(s, 'x');
-    const int d = xp ? atoi(xp + 1) : 2;
-    return ns * 10 + d;
-  }();
-  return v;
-}
-
-template <int NS, int D, int FMT, bool OBF16>
+// Stream-kernel shape: four 16-column subtiles per wave (64 columns, fewer
+// and longer waves amortise the tile lookup and activation loads), a ring two
+// chunks deep, and tiles of up to 32 rows: a popular expert's band streams
+// its codes once per 32 rows instead of once per 16 (the two-subtile walk
+// keeps a one-chunk ring so that both walks fit three workgroups per CU).
+template <int FMT, bool OBF16>
 static void launch_stream(const uint8_t* packed, const Layout& L, const uint16_t* x, uint32_t x_bytes,
                           const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
                           void* y, hipStream_t stream) {
+  constexpr int NS = 4, D = 2, MS = 2, BM = 16 * MS;
   const int NB = (int)((L.N + 64 * NS - 1) / (64 * NS));
   const int64_t em = E < M ? E : M;
-  const int64_t tiles = ((M + 15) / 16 + em + 7) / 8 * 8;   // whole rounds of 8 tiles
-  hipLaunchKernelGGL((gmm_stream_kernel<NS, D, FMT, OBF16>), dim3((unsigned)(tiles * NB)),
+  const int64_t tiles = ((M + BM - 1) / BM + em + 7) / 8 * 8;   // whole rounds of 8 tiles
+  hipLaunchKernelGGL((gmm_stream_kernel<NS, D, MS, FMT, OBF16>), dim3((unsigned)(tiles * NB)),
                      dim3(256), 0, stream, packed, L, x, x_bytes, row_index, goff, E, y, NB);
 }
 
@@ -519,19 +535,7 @@ static void launch_gmm_t(const uint8_t* packed, const Layout& L, const uint16_t*
                          void* y, int kernel, hipStream_t stream) {
   const uint32_t x_bytes = (uint32_t)((int64_t)x_rows * L.K * 2);
   if (kernel == 1) {
-    // NS * 16 columns per wave must divide N (N is a multiple of 64).
-    int shape = stream_shape();
-    if (L.N % (16 * (shape / 10)) != 0) shape = 42;
-    switch (shape) {
-      case 21: launch_stream<2, 1, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
-      case 24: launch_stream<2, 4, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
-      case 42: launch_stream<4, 2, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
-      case 43: launch_stream<4, 3, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
-      case 12: launch_stream<1, 2, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
-      case 14: launch_stream<1, 4, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
-      case 22: launch_stream<2, 2, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
-      default: launch_stream<4, 2, FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream); break;
-    }
+    launch_stream<FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream);
   } else {
     const int64_t em = E < M ? E : M;
     const int NB = (int)((L.N + TL_BN - 1) / TL_BN);
