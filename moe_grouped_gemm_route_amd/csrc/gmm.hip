@@ -21,6 +21,9 @@
 //
 // Both kernels below issue, for every output element, the same MFMAs in the
 // same order (chunks ascending, steps 0..3), so they return identical bits.
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 #include "launch.h"
 
@@ -331,115 +334,183 @@ __global__ __launch_bounds__(256, 3) void gmm_stream_kernel(const uint8_t* __res
 // waves owns a 128-row tile and 256 columns; wave w owns columns 64w..64w+63
 // (four 16-column subtiles) for all 128 rows, so every decoded weight feeds
 // eight MFMAs.  The activation tile of each 128-deep chunk (gathered rows) is
-// copied HBM -> LDS by direct-to-LDS 16-byte loads (no staging registers),
-// double-buffered.  A staged row is 256 bytes with its 16-byte segments
-// XOR-swizzled by (row & 15), so the 16 rows read by one fragment load hit 16
-// different bank groups.  Codes stream into registers one chunk ahead.
-// 16-row subtiles past the band end are skipped.
+// copied HBM -> LDS by direct-to-LDS 16-byte buffer loads (no staging
+// registers), double-buffered.  A staged row is 256 bytes with its 16-byte
+// segments XOR-swizzled by (row & 15), so the 16 rows read by one fragment
+// load hit 16 different bank groups.  Codes and scale words stream into
+// registers one chunk ahead.  The K walk is compiled per number of valid
+// 16-row subtiles, so subtiles past the band end cost nothing.
+//
+// Waits are explicit.  Per chunk kc a wave issues, in this order, its share
+// of activation chunk kc+1 (LOADS direct-to-LDS loads) and the codes and
+// scale words of chunk kc+1 (2 * NS loads), computes chunk kc, then waits
+// until at most 2 * NS vector loads are outstanding: loads complete in
+// issue order, so its share of chunk kc+1 is then in LDS, while the codes
+// may still be in flight.  The barrier that follows makes every wave's share
+// visible and guarantees that every wave has finished reading buffer kc & 1
+// before it is refilled with chunk kc+2.  Every chunk issues the same loads
+// (indices past the last chunk are clamped to it, into the buffer nobody
+// reads any more), so the count is the same at every wait; a final
+// vmcnt(0) drains them before the epilogue.
+//
+// A-fragment reads are ds_read_b128 issued P - 1 fragments ahead of their
+// MFMAs (inline asm, so the compiler cannot sink them next to their use);
+// before fragment f's MFMAs the wave waits until only the reads issued after
+// f are outstanding (LDS reads of a wave complete in order).  The wait is an
+// asm statement that takes the fragment register as an in-out operand, so no
+// MFMA reading that register can be scheduled above it.
 // ---------------------------------------------------------------------------
 constexpr int TL_MS = 8;                    // 16-row subtiles per tile
 constexpr int TL_NS = 4;                    // 16-column subtiles per wave
+constexpr int TL_WAVES = 4;
 constexpr int TL_BM = 16 * TL_MS;           // 128
-constexpr int TL_BN = 4 * 16 * TL_NS;       // 256
+constexpr int TL_BN = TL_WAVES * 16 * TL_NS;   // 256
 constexpr int TL_ROW_BYTES = 128 * 2;       // one staged row of a chunk
 constexpr int TL_BUF_BYTES = TL_BM * TL_ROW_BYTES;
-constexpr int TL_LOADS = TL_BUF_BYTES / 1024 / 4;   // 1 KiB wave loads per wave per chunk
+constexpr int TL_LOADS = TL_BUF_BYTES / 1024 / TL_WAVES;   // 1 KiB loads per wave per chunk
+constexpr int TL_PIPE = 4;                  // A-fragment registers in the read pipeline
 
-// Copies the activation chunk kc into an LDS buffer.  Load j of wave w fills
-// LDS bytes [(8w + j) KiB, +1 KiB): rows 4(8w + j) .. +3, lane l landing at
-// byte 16 l, i.e. row 4(8w + j) + l/16, physical segment l & 15, which holds
-// logical segment (l & 15) ^ (row & 15).
-__device__ __forceinline__ void stage_chunk(uint8_t* buf, const uint8_t* const (&ap)[TL_LOADS],
-                                            const bool (&av)[TL_LOADS], int kc, int wave) {
-#pragma unroll
-  for (int j = 0; j < TL_LOADS; ++j) {
-    if (av[j])
-      __builtin_amdgcn_global_load_lds(ap[j] + kc * 256, buf + (wave * TL_LOADS + j) * 1024, 16, 0, 0);
-  }
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt immediate for gfx9: vmcnt in [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]; a field at its maximum does not wait.
+template <int VM, int LGKM>
+constexpr int waitcnt_imm() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "waitcnt field");
+  return (VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8);
 }
 
-// The K walk of one tiled workgroup for a tile with NSUB valid 16-row
-// subtiles (a compile-time count, so the inner loops carry no branches and
-// the compiler can batch the LDS fragment reads ahead of the MFMAs).
-//
-// Per 128-deep chunk kc: issue the activation copy of chunk kc+1 (direct to
-// LDS), the codes of chunk kc+1 and the scale words of chunk kc+1, then
-// compute chunk kc from registers and LDS filled one iteration earlier, then
-// one barrier.  Nothing loaded in an iteration is consumed before that
-// iteration's barrier, so no wait inside the compute phase touches the
-// loads in flight.
+// Waits until at most VM vector loads of this wave are outstanding and all
+// its LDS operations are done, then joins the workgroup barrier.
+template <int VM>
+__device__ __forceinline__ void vm_wait_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm<VM, 0>());
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void lds_read_wait(u32x4_t& r) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
+}
+
+template <int OFF>
+__device__ __forceinline__ u32x4_t lds_read16(uint32_t addr) {
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+
+// Fragment f of a chunk (step s = f / NSUB, row subtile ms = f % NSUB) of
+// the LDS buffer BUF: decode the step's weights at its first fragment, wait
+// for the fragment's read, issue its NS MFMAs, then issue the read of
+// fragment f + P - 1 into the register of fragment f - 1 (whose MFMAs were
+// issued one fragment earlier).
+template <int NSUB, int P, int BUF, int FMT, int F>
+__device__ __forceinline__ void tiled_fragment(u32x4_t (&ar)[P], const uint32_t (&va)[4],
+                                               u32x4_t (&b)[TL_NS], const u32x4_t (&cw)[TL_NS],
+                                               const float (&lo)[TL_NS], const float (&hi)[TL_NS],
+                                               bool general, f32x4_t (&acc)[TL_MS][TL_NS]) {
+  constexpr int FT = 4 * NSUB;
+  constexpr int s = F / NSUB, ms = F % NSUB;
+  if constexpr (ms == 0) {
+#pragma unroll
+    for (int ns = 0; ns < TL_NS; ++ns) b[ns] = decode_step<FMT>(cw[ns][s], s < 2 ? lo[ns] : hi[ns], general);
+  }
+  constexpr int newest = (F + P - 2 < FT - 1) ? F + P - 2 : FT - 1;
+  lds_read_wait<newest - F>(ar[F % P]);
+#pragma unroll
+  for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = mfma(as_bf16x8(ar[F % P]), as_bf16x8(b[ns]), acc[ms][ns]);
+  constexpr int NF = F + P - 1;
+  if constexpr (NF < FT)
+    ar[NF % P] = lds_read16<(NF % NSUB) * 16 * TL_ROW_BYTES + BUF * TL_BUF_BYTES>(va[NF / NSUB]);
+}
+
+template <int NSUB, int P, int BUF, int FMT, size_t... Fs>
+__device__ __forceinline__ void tiled_chunk(std::index_sequence<Fs...>, u32x4_t (&ar)[P], const uint32_t (&va)[4],
+                                            u32x4_t (&b)[TL_NS], const u32x4_t (&cw)[TL_NS],
+                                            const float (&lo)[TL_NS], const float (&hi)[TL_NS], bool general,
+                                            f32x4_t (&acc)[TL_MS][TL_NS]) {
+  (tiled_fragment<NSUB, P, BUF, FMT, (int)Fs>(ar, va, b, cw, lo, hi, general, acc), ...);
+}
+
+template <int NSUB, int P, int BUF, size_t... Is>
+__device__ __forceinline__ void tiled_prologue(std::index_sequence<Is...>, u32x4_t (&ar)[P], const uint32_t (&va)[4]) {
+  ((ar[Is] = lds_read16<((int)Is % NSUB) * 16 * TL_ROW_BYTES + BUF * TL_BUF_BYTES>(va[Is / NSUB])), ...);
+}
+
+// The K walk of one wave for a tile with NSUB valid 16-row subtiles.
 template <int NSUB, int FMT>
-__device__ __forceinline__ void tiled_k_walk(uint8_t (*s_a)[TL_BUF_BYTES], const uint8_t* const (&ap)[TL_LOADS],
-                                             const bool (&av)[TL_LOADS], const u32x4_t* const (&cp)[TL_NS],
-                                             const uint32_t* const (&sp)[TL_NS], bool wave_active, int KC,
-                                             int wave, const int (&aoff)[4],
-                                             f32x4_t (&acc)[TL_MS][TL_NS]) {
-  u32x4_t c[TL_NS];
-  uint32_t sw[TL_NS];
-  if (wave_active) {
+__device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_t xr,
+                                             const uint32_t (&avo)[TL_LOADS], __amdgpu_buffer_rsrc_t cr,
+                                             __amdgpu_buffer_rsrc_t sr, int KC, int groups, int wave,
+                                             const uint32_t (&va)[4], f32x4_t (&acc)[TL_MS][TL_NS]) {
+  constexpr int P = TL_PIPE;
+  constexpr int FT = 4 * NSUB;
+  constexpr int PRO = (P - 1 < FT) ? P - 1 : FT;
+  const int lane = threadIdx.x & 63;
+  const uint32_t c_voff = lane * 16, s_voff = lane * 4;
+  u32x4_t cs[2][TL_NS];
+  uint32_t ws[2][TL_NS];
+  // Load j of wave w fills LDS bytes [(LOADS w + j) KiB, +1 KiB) of the
+  // buffer: rows 4(LOADS w + j) .. +3, lane l landing at byte 16 l, i.e. row
+  // 4(LOADS w + j) + l/16, physical segment l & 15, which holds logical
+  // segment (l & 15) ^ (row & 15) (avo carries the source offsets).
+  auto stage = [&](int kc) {
+    uint8_t* buf = s_a + (kc & 1) * TL_BUF_BYTES + wave * TL_LOADS * 1024;
+#pragma unroll
+    for (int j = 0; j < TL_LOADS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(buf + j * 1024), 16, avo[j], kc * 256, 0, 0);
+  };
+  auto load_codes = [&](int slot, int kc) {
+    const int rec = scale_record<FMT>(kc);
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) {
-      c[ns] = __builtin_nontemporal_load(cp[ns]);
-      sw[ns] = sp[ns][0];
+      cs[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, (ns * KC + kc) << 10, BUF_NT);
+      ws[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (ns * groups + rec) * 256, 0);
     }
+  };
+  auto chunk = [&](auto bc, int kc) {
+    constexpr int d = decltype(bc)::value;   // kc & 1: LDS buffer and code slot
+    stage(min(kc + 1, KC - 1));
+    __builtin_amdgcn_sched_barrier(0);       // the activation loads go first
+    load_codes(d ^ 1, min(kc + 1, KC - 1));
+    float lo[TL_NS], hi[TL_NS];
+#pragma unroll
+    for (int ns = 0; ns < TL_NS; ++ns) chunk_scales<FMT>(ws[d][ns], kc, lo[ns], hi[ns]);
+    const bool general = general_scales<FMT, TL_NS>(lo, hi);
+    u32x4_t ar[P];
+    u32x4_t b[TL_NS];
+    tiled_prologue<NSUB, P, d>(std::make_index_sequence<PRO>{}, ar, va);
+    tiled_chunk<NSUB, P, d, FMT>(std::make_index_sequence<FT>{}, ar, va, b, cs[d], lo, hi, general, acc);
+    vm_wait_barrier<2 * TL_NS>();
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  stage(0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_codes(0, 0);
+  vm_wait_barrier<0>();
+  int k0 = 0;
+  for (; k0 + 2 <= KC; k0 += 2) {
+    chunk(B0{}, k0);
+    chunk(B1{}, k0 + 1);
   }
-  __syncthreads();
-  for (int kc = 0; kc < KC; ++kc) {
-    const int buf = kc & 1;
-    const bool more = kc + 1 < KC;
-    if (more) stage_chunk(s_a[buf ^ 1], ap, av, kc + 1, wave);
-    u32x4_t cn[TL_NS];
-    uint32_t swn[TL_NS];
-    if (wave_active && more) {
-#pragma unroll
-      for (int ns = 0; ns < TL_NS; ++ns) {
-        cn[ns] = __builtin_nontemporal_load(cp[ns] + (kc + 1) * 64);
-        swn[ns] = sp[ns][scale_record<FMT>(kc + 1) * 64];
-      }
-    }
-    if (wave_active) {
-      float lo[TL_NS], hi[TL_NS];
-#pragma unroll
-      for (int ns = 0; ns < TL_NS; ++ns) chunk_scales<FMT>(sw[ns], kc, lo[ns], hi[ns]);
-      const bool general = general_scales<FMT, TL_NS>(lo, hi);
-      const uint8_t* abase = s_a[buf];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        u32x4_t a[NSUB];
-#pragma unroll
-        for (int ms = 0; ms < NSUB; ++ms)
-          a[ms] = *reinterpret_cast<const u32x4_t*>(abase + ms * 16 * TL_ROW_BYTES + aoff[s]);
-        u32x4_t b[TL_NS];
-#pragma unroll
-        for (int ns = 0; ns < TL_NS; ++ns) b[ns] = decode_step<FMT>(c[ns][s], s < 2 ? lo[ns] : hi[ns], general);
-#pragma unroll
-        for (int ms = 0; ms < NSUB; ++ms)
-#pragma unroll
-          for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = mfma(as_bf16x8(a[ms]), as_bf16x8(b[ns]), acc[ms][ns]);
-      }
-    }
-    if (wave_active && more) {
-#pragma unroll
-      for (int ns = 0; ns < TL_NS; ++ns) {
-        c[ns] = cn[ns];
-        sw[ns] = swn[ns];
-      }
-    }
-    __syncthreads();
-  }
+  if (k0 < KC) chunk(B0{}, k0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>());
 }
 
 template <int FMT, bool OBF16>
 __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __restrict__ packed, Layout L,
-                                                           const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ x, uint32_t x_bytes,
                                                            const int32_t* __restrict__ row_index,
                                                            const int32_t* __restrict__ goff, int E,
                                                            void* __restrict__ y, int NB) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_a[2][TL_BUF_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a[2 * TL_BUF_BYTES];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const TileScan ts = scan_tiles(goff, E, TL_BM);
   const int item = work_item(ts.total * NB, true);
   if (item < 0) return;
@@ -448,38 +519,40 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
   const Tile tile = locate_tile(goff, E, TL_BM, ts, t);
   const int K = (int)L.K;
   const int KC = (int)L.KC;
+  const int groups = (int)L.groups;
   const int n0 = nb * TL_BN + wave * 16 * TL_NS;
+  // A wave past the last column still stages its share of the activations
+  // and joins every barrier; its code loads read zeros and it stores nothing.
   const bool wave_active = n0 < L.N;
   const int r = lane & 15;
   const int g = lane >> 4;
   const int nsub = (tile.rows + 15) >> 4;
 
-  // Source of each of this lane's staging loads (rows past the band are not
-  // loaded: their LDS rows only feed accumulator rows that are never stored).
-  const uint8_t* ap[TL_LOADS];
-  bool av[TL_LOADS];
+  // Source offsets of this lane's staging loads; rows past the band read
+  // zeros (their accumulator rows are never stored).
+  uint32_t avo[TL_LOADS];
 #pragma unroll
   for (int j = 0; j < TL_LOADS; ++j) {
     const int rl = 4 * (wave * TL_LOADS + j) + (lane >> 4);
-    av[j] = rl < tile.rows;
-    const int row = tile.m0 + (av[j] ? rl : 0);
-    const int64_t src = row_index ? row_index[row] : row;
-    const int logical_seg = (lane & 15) ^ (rl & 15);
-    ap[j] = reinterpret_cast<const uint8_t*>(x + src * K) + logical_seg * 16;
+    avo[j] = BUF_OOB;
+    if (rl < tile.rows) {
+      const int row = tile.m0 + rl;
+      const int64_t src = row_index ? row_index[row] : row;
+      avo[j] = (uint32_t)(src * K * 2 + (((lane & 15) ^ (rl & 15)) << 4));
+    }
   }
-  const u32x4_t* cp[TL_NS];
-  const uint32_t* sp[TL_NS];
+  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, x_bytes);
+  const int64_t et = (int64_t)tile.e * L.NT + (wave_active ? (n0 >> 4) : 0);
+  const __amdgpu_buffer_rsrc_t cr =
+      buffer_rsrc(packed + ((et * L.KC) << 10), wave_active ? (uint32_t)(TL_NS * KC) << 10 : 0u);
+  const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(packed + L.scales_off + et * L.groups * 256,
+                                                wave_active ? (uint32_t)(TL_NS * groups) * 256 : 0u);
+  // LDS address of this lane's fragment row for step s: row r of the
+  // subtile, logical segment g*4 + s
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)s_a;
+  uint32_t va[4];
 #pragma unroll
-  for (int ns = 0; ns < TL_NS; ++ns) {
-    const int64_t nt = wave_active ? (n0 >> 4) + ns : 0;
-    const int64_t et = (int64_t)tile.e * L.NT + nt;
-    cp[ns] = reinterpret_cast<const u32x4_t*>(packed + ((et * L.KC) << 10)) + lane;
-    sp[ns] = reinterpret_cast<const uint32_t*>(packed + L.scales_off) + et * L.groups * 64 + lane;
-  }
-  // fragment read offsets: row ms*16 + r, logical segment g*4 + s
-  int aoff[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) aoff[s] = r * TL_ROW_BYTES + (((g * 4 + s) ^ r) << 4);
+  for (int s = 0; s < 4; ++s) va[s] = lds0 + r * TL_ROW_BYTES + (((g * 4 + s) ^ r) << 4);
 
   f32x4_t acc[TL_MS][TL_NS];
 #pragma unroll
@@ -487,16 +560,15 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  stage_chunk(s_a[0], ap, av, 0, wave);
   switch (nsub) {
-    case 1: tiled_k_walk<1, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
-    case 2: tiled_k_walk<2, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
-    case 3: tiled_k_walk<3, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
-    case 4: tiled_k_walk<4, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
-    case 5: tiled_k_walk<5, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
-    case 6: tiled_k_walk<6, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
-    case 7: tiled_k_walk<7, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
-    default: tiled_k_walk<8, FMT>(s_a, ap, av, cp, sp, wave_active, KC, wave, aoff, acc); break;
+    case 1: tiled_k_walk<1, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
+    case 2: tiled_k_walk<2, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
+    case 3: tiled_k_walk<3, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
+    case 4: tiled_k_walk<4, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
+    case 5: tiled_k_walk<5, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
+    case 6: tiled_k_walk<6, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
+    case 7: tiled_k_walk<7, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
+    default: tiled_k_walk<8, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
   }
 
   if (!wave_active) return;
@@ -540,8 +612,8 @@ static void launch_gmm_t(const uint8_t* packed, const Layout& L, const uint16_t*
     const int64_t em = E < M ? E : M;
     const int NB = (int)((L.N + TL_BN - 1) / TL_BN);
     const int64_t tiles = (M + TL_BM - 1) / TL_BM + em;
-    hipLaunchKernelGGL((gmm_tiled_kernel<FMT, OBF16>), dim3((unsigned)(tiles * NB)), dim3(256), 0,
-                       stream, packed, L, x, row_index, goff, E, y, NB);
+    hipLaunchKernelGGL((gmm_tiled_kernel<FMT, OBF16>), dim3((unsigned)(tiles * NB)), dim3(64 * TL_WAVES), 0,
+                       stream, packed, L, x, x_bytes, row_index, goff, E, y, NB);
   }
 }
 
