@@ -148,6 +148,39 @@ def test_gmm_kernels_agree_bitwise_and_bf16_output(case):
     assert np.all(np.abs(got - ref) <= bf16_ulp(ref))
 
 
+# Band sizes that reach every specialised walk: the stream kernel's one- and
+# two-subtile tiles (1..16, 17..32 rows, several 32-row tiles) and the tiled
+# kernel's 1..8 valid 16-row subtiles, whole and ragged 128-row tiles, and an
+# empty expert.  N = 320 leaves three of the four waves of the last tiled
+# column block without columns.
+BANDS = [1, 15, 16, 17, 31, 32, 33, 48, 0, 64, 80, 96, 112, 127, 128, 129, 200, 5]
+
+
+def _banded_problem(seed, fmt_scales=(-6, -2)):
+    E = len(BANDS)
+    p = make_problem(T=sum(BANDS), k=1, E=E, K=256, N=320, seed=seed, exp_range=fmt_scales)
+    rng = np.random.default_rng(seed + 1)
+    ids = np.repeat(np.arange(E, dtype=np.int32), BANDS)
+    rng.shuffle(ids)
+    p["topk_ids"] = ids.reshape(-1, 1)
+    return p
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_gmm_every_band_shape(fmt):
+    p = _banded_problem(260)
+    w, packed = weights_for(p, fmt)
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    assert np.array_equal(np.diff(ref_r["group_offsets"]), BANDS)
+    ref = oracle.gmm(p["x"], ref_r["sorted_token"], ref_r["group_offsets"], w)
+    ys = []
+    for kernel in KERNELS:
+        _, y = run_gpu(p, packed, fmt, kernel=kernel)
+        assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
+        ys.append(y)
+    assert torch.equal(ys[0], ys[1])
+
+
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_gmm_nvfp4_general_e4m3_scales(kernel):
     # NVFP4 weights whose per-16 scales are arbitrary E4M3 values (not only
