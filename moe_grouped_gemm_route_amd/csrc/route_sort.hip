@@ -27,6 +27,7 @@ constexpr int RS_WAVES = 8;
 constexpr int RS_THREADS = RS_WAVES * 64;
 constexpr int RS_SEGMENT = 2048;     // pairs placed per workgroup (large M)
 constexpr int RS_MAX_GROUPS = 64;
+constexpr int RS_UNROLL = 8;         // id loads in flight per thread
 
 __global__ __launch_bounds__(RS_THREADS) void route_sort_kernel(
     const int32_t* __restrict__ ids, int32_t M, int32_t k, int32_t E, int32_t id_bits, int32_t S,
@@ -53,21 +54,40 @@ __global__ __launch_bounds__(RS_THREADS) void route_sort_kernel(
   if (tid == 0) s_bad = 0;
   __syncthreads();
 
-  // 1. histograms
+  // 1. histograms (ids are loaded RS_UNROLL at a time, so that one wait
+  // covers several loads)
   int bad = 0;
-  for (int p = tid; p < M; p += RS_THREADS) {
-    const int e = ids[p];
-    if (e >= 0 && e < E) {
-      atomicAdd(&s_tot[e], 1);
-      if (p < seg_begin) atomicAdd(&s_bef[e], 1);
-    } else {
-      ++bad;
+  for (int p0 = 0; p0 < M; p0 += RS_THREADS * RS_UNROLL) {
+    int ev[RS_UNROLL];
+#pragma unroll
+    for (int u = 0; u < RS_UNROLL; ++u) {
+      const int p = p0 + u * RS_THREADS + tid;
+      ev[u] = p < M ? ids[p] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < RS_UNROLL; ++u) {
+      const int p = p0 + u * RS_THREADS + tid;
+      const int e = ev[u];
+      if (p >= M) break;
+      if (e >= 0 && e < E) {
+        atomicAdd(&s_tot[e], 1);
+        if (p < seg_begin) atomicAdd(&s_bef[e], 1);
+      } else {
+        ++bad;
+      }
     }
   }
   int32_t* cnt = s_cnt + wave * E;
-  for (int p = w_begin + lane; p < w_end; p += 64) {
-    const int e = ids[p];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  for (int p0 = w_begin; p0 < w_end; p0 += 64 * RS_UNROLL) {
+    int ev[RS_UNROLL];
+#pragma unroll
+    for (int u = 0; u < RS_UNROLL; ++u) {
+      const int p = p0 + u * 64 + lane;
+      ev[u] = p < w_end ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < RS_UNROLL; ++u)
+      if (ev[u] >= 0 && ev[u] < E) atomicAdd(&cnt[ev[u]], 1);
   }
   for (int d = 32; d > 0; d >>= 1) bad += __shfl_xor(bad, d, 64);
   if (lane == 0 && bad) atomicAdd(&s_bad, bad);
@@ -104,11 +124,14 @@ __global__ __launch_bounds__(RS_THREADS) void route_sort_kernel(
   }
   __syncthreads();
 
-  // 3. place this wave's sub-segment in pair order
+  // 3. place this wave's sub-segment in pair order (the ids of the next
+  // round are loaded while this one is placed)
+  int e_next = (w_begin + lane < w_end) ? ids[w_begin + lane] : -1;
   for (int p0 = w_begin; p0 < w_end; p0 += 64) {
     const int p = p0 + lane;
     const bool in_seg = p < w_end;
-    const int e = in_seg ? ids[p] : -1;
+    const int e = e_next;
+    e_next = (p + 64 < w_end) ? ids[p + 64] : -1;
     const bool valid = in_seg && e >= 0 && e < E;
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < id_bits; ++b) {
