@@ -16,8 +16,9 @@ One JSON line is printed.  value is the whole step's throughput in the
 algorithmic bytes of the matmul (codes + scales of the experts that received
 tokens, plus the activations read) per second; roofline.achieved is the same
 bytes over the grouped-matmul kernel's own average duration, timed with HIP
-events on the stream it runs on.  The CPU baseline times the float64 oracle on
-a bounded sample of the same workload on the host cores.
+events on the stream it runs on (gmm_us; the median and minimum are reported
+beside it).  The CPU baseline times the float64 oracle on a bounded sample of
+the same workload on the host cores; gpu_over_cpu is value over its value.
 """
 
 import argparse
@@ -106,10 +107,20 @@ def cpu_baseline(p, fmt, unit, target_s=15.0):
     return {
         "value": round(value, 6), "unit": unit, "cores": int(threads),
         "kind": "oracle",
-        "sample": "float64 numpy oracle: route-sort of all %d pairs + grouped matmul of the "
-                  "first %d of %d active experts' bands (%d rows), %.1f s"
-                  % (p["T"] * p["k"], done, len(active), rows_done, elapsed),
+        "sample": "float64 numpy oracle on %s: route-sort of all %d pairs + grouped matmul of "
+                  "the first %d of %d active experts' bands (%d rows), %.1f s"
+                  % (cpu_model(), p["T"] * p["k"], done, len(active), rows_done, elapsed),
     }
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def main():
@@ -204,6 +215,8 @@ def main():
 
     gmm_ms = [a.elapsed_time(b) for a, b in ev]
     gmm_avg_s = float(np.mean(gmm_ms)) / 1e3
+    gmm_med_s = float(np.median(gmm_ms)) / 1e3
+    gmm_min_s = float(np.min(gmm_ms)) / 1e3
     nbytes, active = algorithmic_bytes(p, fmt)
     flops = 2.0 * M * K * N
     step_s = wall / args.steps
@@ -247,6 +260,8 @@ def main():
                    "output": out_dtype, "kernel": args.kernel,
                    "step": "route_sort + moe_gmm" + (" + moe_combine" if combine else "")},
         "gmm_us": round(gmm_avg_s * 1e6, 2),
+        "gmm_us_median": round(gmm_med_s * 1e6, 2),
+        "gmm_us_min": round(gmm_min_s * 1e6, 2),
         "gmm_tflops": round(flops / gmm_avg_s / 1e12, 2),
         "gmm_gbs": round(nbytes / gmm_avg_s / 1e9, 1),
         "active_experts": active,
@@ -255,6 +270,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, fmt, unit)
+        out["gpu_over_cpu"] = round(value / out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
 
 
