@@ -8,9 +8,9 @@
 //   1. histograms (integer counts, so the order of the LDS increments cannot
 //      change them): over all M pairs, tot[e]; over the pairs before the
 //      segment, bef[e]; over each wave's sub-segment, cnt[w][e];
-//   2. scan: band starts off[e] = sum of tot over experts < e, and each
-//      wave's cursor cur[w][e] = off[e] + bef[e] + sum over w' < w of
-//      cnt[w'][e];
+//   2. scan (all threads): band starts off[e] = sum of tot over experts
+//      < e, and each wave's cursor cur[w][e] = off[e] + bef[e] + sum over
+//      w' < w of cnt[w'][e];
 //   3. place: each wave walks its sub-segment 64 pairs at a time in pair
 //      order; lanes holding the same expert are found with ballots over the
 //      id bits; a pair's row is cur[w][e] + the number of such lanes below
@@ -39,6 +39,7 @@ __global__ __launch_bounds__(RS_THREADS) void route_sort_kernel(
   int32_t* s_bef = s_mem + E;             // [E]
   int32_t* s_cnt = s_mem + 2 * E;         // [RS_WAVES][E], later the cursors
   __shared__ int32_t s_bad;
+  __shared__ int32_t s_wsum[RS_WAVES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -93,34 +94,43 @@ __global__ __launch_bounds__(RS_THREADS) void route_sort_kernel(
   if (lane == 0 && bad) atomicAdd(&s_bad, bad);
   __syncthreads();
 
-  // 2. scan (wave 0): band starts and per-wave cursors
-  if (wave == 0) {
-    const int per = (E + 63) >> 6;
+  // 2. scan (all threads): thread t covers experts [t*per, t*per + per);
+  // an exclusive block scan of their totals gives the band starts, and each
+  // expert's per-wave cursors follow from its before-segment count and the
+  // per-wave counts
+  {
+    const int per = (E + RS_THREADS - 1) / RS_THREADS;
+    const int e0 = tid * per;
     int mine = 0;
-    for (int i = 0; i < per; ++i) {
-      const int e = lane * per + i;
-      if (e < E) mine += s_tot[e];
-    }
+    for (int i = 0; i < per; ++i)
+      if (e0 + i < E) mine += s_tot[e0 + i];
     int incl = mine;
     for (int d = 1; d < 64; d <<= 1) {
       const int v = __shfl_up(incl, d, 64);
       if (lane >= d) incl += v;
     }
-    int run = incl - mine;
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += s_wsum[w];
+    int run = base + incl - mine;
     for (int i = 0; i < per; ++i) {
-      const int e = lane * per + i;
+      const int e = e0 + i;
       if (e < E) {
         if (blockIdx.x == 0) group_offsets[e] = run;
+        int n[RS_WAVES];
+#pragma unroll
+        for (int w = 0; w < RS_WAVES; ++w) n[w] = s_cnt[w * E + e];
         int c = run + s_bef[e];
+#pragma unroll
         for (int w = 0; w < RS_WAVES; ++w) {
-          const int n = s_cnt[w * E + e];
           s_cnt[w * E + e] = c;
-          c += n;
+          c += n[w];
         }
         run += s_tot[e];
       }
     }
-    if (blockIdx.x == 0 && lane == 63) group_offsets[E] = incl;
+    if (blockIdx.x == 0 && tid == RS_THREADS - 1) group_offsets[E] = base + incl;
   }
   __syncthreads();
 
