@@ -15,6 +15,8 @@ routed-expert path computes, written from these pages:
   "Verification": the -0 -> +0 canonicalisation note.
 * "DeepSeek-V4-Flash" (PocketLLM docs), section "Correctness and precision":
   the expert reduction is deterministic (fixed order, no atomics).
+* The gate/up activation after the fused w13 matmul, which the pages name but
+  do not define: the SiLU-gated product of the two column halves (act.py).
 
 It shares no code with the HIP path and imports nothing from it.
 """
@@ -33,3 +35,4 @@ from .formats import (  # noqa: F401
 from .route import route_sort  # noqa: F401
 from .gmm import gmm, gmm_sampled, dense_weights  # noqa: F401
 from .combine import combine  # noqa: F401
+from .act import silu, silu_mul  # noqa: F401
