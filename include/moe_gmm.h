@@ -46,6 +46,12 @@ typedef enum {
 typedef enum { MOE_W_MXFP4 = 0, MOE_W_NVFP4 = 1 } moe_wfmt_t;
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
+/* Epilogue of moe_gmm_act. */
+typedef enum {
+  MOE_ACT_NONE = 0,     /* y = the [M, N] matmul output                        */
+  MOE_ACT_SILU_MUL = 1  /* y = [M, N/2] silu(out[:, :N/2]) * out[:, N/2:]      */
+} moe_act_t;
+
 /* Kernel configuration of moe_gmm_ex.  AUTO picks from the problem shape. */
 typedef enum {
   MOE_GMM_AUTO = 0,
@@ -153,6 +159,32 @@ int moe_gmm_ex(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
                const uint16_t* x, int32_t x_rows, const int32_t* row_index,
                const int32_t* group_offsets, int32_t M, void* y, int y_dtype,
                int kernel, void* stream);
+
+/*
+ * moe_gmm_act - moe_gmm_ex with the gate/up activation fused into the
+ * epilogue.
+ *
+ * Source: "Running DeepSeek V4 Flash on TPU v6", section "Grouped matmul
+ * performance vs bf16", names the gate/up activation that follows the fused
+ * gate+up (w13) matmul; the "DeepSeek-V4-Flash-0731-NVFP4" model card,
+ * section "The lossless weight cast", calls that matmul the fused w1/w3
+ * GEMM1.  Neither page writes the activation out; this library takes the
+ * SiLU-gated product of the two column halves (gate = w1 = the first N/2
+ * weight rows, up = w3 = the last N/2).
+ *
+ * act = MOE_ACT_NONE: exactly moe_gmm_ex.
+ * act = MOE_ACT_SILU_MUL: y is [M, N/2] (f32 or bf16, row stride N/2) with
+ *   y[r, j] = silu(g) * u,  g = out[r, j],  u = out[r, N/2 + j],
+ *   silu(g) = g / (1 + e^-g), out the f32 matmul sums of moe_gmm (times the
+ *   NVFP4 tensor scale), evaluated in f32; the [M, N] sums are never written.
+ *   Requires N % 128 == 0 and (N/32 + 2) * (K/128) KiB < 4 GiB.
+ * Every kernel configuration returns bitwise identical y.  Other arguments,
+ * limits and errors as moe_gmm; an unknown act returns MOE_ERR_FORMAT.
+ */
+int moe_gmm_act(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
+                const uint16_t* x, int32_t x_rows, const int32_t* row_index,
+                const int32_t* group_offsets, int32_t M, void* y, int y_dtype,
+                int act, int kernel, void* stream);
 
 /*
  * moe_combine - top-k weighted unpermute back to token order.

@@ -14,7 +14,7 @@ import os
 import torch
 
 __all__ = [
-    "MXFP4", "NVFP4", "F32", "BF16", "GMM_AUTO", "GMM_STREAM", "GMM_TILED",
+    "MXFP4", "NVFP4", "F32", "BF16", "GMM_AUTO", "GMM_STREAM", "GMM_TILED", "ACT_NONE", "ACT_SILU_MUL",
     "MoeGmmError", "library", "route_sort", "packed_weight_bytes", "mxfp4_encode",
     "moe_gmm", "moe_combine", "mxfp4_to_nvfp4", "debug_decode",
 ]
@@ -22,6 +22,7 @@ __all__ = [
 MXFP4, NVFP4 = 0, 1
 F32, BF16 = 0, 1
 GMM_AUTO, GMM_STREAM, GMM_TILED = 0, 1, 2
+ACT_NONE, ACT_SILU_MUL = 0, 1
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoegmm.so")
 _lib = None
@@ -36,6 +37,8 @@ _SIGNATURES = {
                                _vp, ctypes.c_int, _vp]),
     "moe_gmm_ex": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32,
                                   _vp, ctypes.c_int, ctypes.c_int, _vp]),
+    "moe_gmm_act": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32,
+                                   _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp]),
     "moe_combine": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _i32, _i32, _i32, _vp,
                                    ctypes.c_int, _vp]),
     "moe_mxfp4_to_nvfp4": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
@@ -147,9 +150,10 @@ def mxfp4_encode(codes, scales, tensor_scale=None, fmt=MXFP4):
 
 
 def moe_gmm(packed, fmt, E, N, K, x, group_offsets, M, row_index=None, out_dtype=F32,
-            kernel=GMM_AUTO, out=None):
-    """moe_gmm_ex.  x: bf16 [T, K] (gathered through row_index) or [M, K].
-    Returns y [M, N] float32 or bfloat16."""
+            kernel=GMM_AUTO, out=None, act=ACT_NONE):
+    """moe_gmm_act.  x: bf16 [T, K] (gathered through row_index) or [M, K].
+    Returns y [M, N] (act=ACT_NONE) or [M, N/2] (act=ACT_SILU_MUL), float32 or
+    bfloat16."""
     _dev(packed, torch.uint8, "packed", 1)
     xb = _bits16(x, "x")
     _dev(group_offsets, torch.int32, "group_offsets", 1)
@@ -167,14 +171,16 @@ def moe_gmm(packed, fmt, E, N, K, x, group_offsets, M, row_index=None, out_dtype
     if packed.numel() < packed_weight_bytes(fmt, E, N, K):
         raise MoeGmmError("packed buffer too small")
     dt = torch.float32 if out_dtype == F32 else torch.bfloat16
+    cols = N // 2 if act == ACT_SILU_MUL else N
     if out is None:
-        out = torch.empty((M, N), dtype=dt, device=packed.device)
+        out = torch.empty((M, cols), dtype=dt, device=packed.device)
     else:
         _dev(out, dt, "out", 2)
-        if tuple(out.shape) != (M, N):
-            raise MoeGmmError("out must be [M, N]")
-    _check(library().moe_gmm_ex(_ptr(packed), fmt, E, N, K, _ptr(xb), xb.shape[0], _ptr(row_index),
-                                _ptr(group_offsets), M, _ptr(out), out_dtype, kernel, _stream()))
+        if tuple(out.shape) != (M, cols):
+            raise MoeGmmError("out must be [M, %d]" % cols)
+    _check(library().moe_gmm_act(_ptr(packed), fmt, E, N, K, _ptr(xb), xb.shape[0], _ptr(row_index),
+                                 _ptr(group_offsets), M, _ptr(out), out_dtype, act, kernel,
+                                 _stream()))
     return out
 
 

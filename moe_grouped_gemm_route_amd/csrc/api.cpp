@@ -72,27 +72,41 @@ int mxfp4_encode(int fmt, const uint8_t* codes, const uint8_t* scales, const flo
                                        static_cast<hipStream_t>(stream)));
 }
 
-int moe_gmm_ex(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint16_t* x,
-               int32_t x_rows, const int32_t* row_index, const int32_t* group_offsets, int32_t M, void* y,
-               int y_dtype, int kernel, void* stream) {
+int moe_gmm_act(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint16_t* x,
+                int32_t x_rows, const int32_t* row_index, const int32_t* group_offsets, int32_t M, void* y,
+                int y_dtype, int act, int kernel, void* stream) {
   const int st = check_weight_shape(fmt, E, N, K);
   if (st != MOE_OK) return st;
   if (!dtype_ok(y_dtype)) return MOE_ERR_FORMAT;
   if (kernel < MOE_GMM_AUTO || kernel > MOE_GMM_TILED) return MOE_ERR_FORMAT;
+  if (act != MOE_ACT_NONE && act != MOE_ACT_SILU_MUL) return MOE_ERR_FORMAT;
   if (!packed || !x || !group_offsets || !y) return MOE_ERR_NULL;
   if (M < 1 || M > kMaxRows) return MOE_ERR_SHAPE;
   if (x_rows < 1 || x_rows > kMaxRows || (!row_index && x_rows < M)) return MOE_ERR_SHAPE;
   // activation rows are addressed with 32-bit byte offsets
   if ((int64_t)x_rows * K * 2 >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
   if (((uintptr_t)packed & 255) || ((uintptr_t)x & 15)) return MOE_ERR_SHAPE;
+  if (act == MOE_ACT_SILU_MUL) {
+    // gate and up halves of 64-column multiples; one wave's code range spans
+    // both halves of an expert and is addressed with 32-bit offsets
+    if (N % 128 != 0) return MOE_ERR_SHAPE;
+    if ((int64_t)(N / 32 + 2) * (K / 128) * 1024 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
+  }
   if (kernel == MOE_GMM_AUTO) {
     // Bands averaging 32 rows or more keep the matrix cores busy enough for
     // the LDS-tiled kernel; thinner bands are pure weight streaming.
     kernel = ((int64_t)M >= 32 * (int64_t)E) ? MOE_GMM_TILED : MOE_GMM_STREAM;
   }
   return hip_status(moe::launch_gmm(static_cast<const uint8_t*>(packed), fmt, E, N, K, x, x_rows,
-                                    row_index, group_offsets, M, y, y_dtype == MOE_BF16, kernel,
+                                    row_index, group_offsets, M, y, y_dtype == MOE_BF16, act, kernel,
                                     static_cast<hipStream_t>(stream)));
+}
+
+int moe_gmm_ex(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint16_t* x,
+               int32_t x_rows, const int32_t* row_index, const int32_t* group_offsets, int32_t M, void* y,
+               int y_dtype, int kernel, void* stream) {
+  return moe_gmm_act(packed, fmt, E, N, K, x, x_rows, row_index, group_offsets, M, y, y_dtype,
+                     MOE_ACT_NONE, kernel, stream);
 }
 
 int moe_gmm(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint16_t* x,

@@ -174,6 +174,37 @@ __device__ __forceinline__ void store_tile(void* y, int64_t N, int row0, int row
   }
 }
 
+// Columns a wave multiplies.  Plain output (ACT 0): NS contiguous 16-column
+// subtiles from column n0.  SiLU-gated gate/up output (ACT 1, four
+// subtiles): subtiles 0 and 1 are the gate columns n0 .. n0+31, subtiles 2
+// and 3 the up columns N/2 + n0 .. +31, and the wave writes columns
+// n0 .. n0+31 of the [M, N/2] activation.  col_sub is a subtile's 16-column
+// index relative to the wave's first subtile (h16 = N/32).
+template <int ACT>
+__device__ __forceinline__ int col_sub(int ns, int h16) {
+  return (ACT == 1 && ns >= 2) ? ns - 2 + h16 : ns;
+}
+
+// The gate/up activation of one 16x16 tile pair: silu(gate) * up, with
+// silu(z) = z / (1 + e^-z) in f32 (the NVFP4 tensor scale applies to both
+// halves first); the layout and masking follow store_tile.
+template <bool OBF16>
+__device__ __forceinline__ void store_tile_silu_mul(void* y, int64_t ldy, int row0, int rows_valid,
+                                                    int col, f32x4_t gate, f32x4_t up, float post) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = 4 * g + i;
+    if (rl < rows_valid) {
+      const float gv = gate[i] * post;
+      const float v = gv / (1.0f + __expf(-gv)) * (up[i] * post);
+      const int64_t off = (int64_t)(row0 + rl) * ldy + col;
+      if (OBF16) reinterpret_cast<uint16_t*>(y)[off] = f32_to_bf16_rne(v);
+      else reinterpret_cast<float*>(y)[off] = v;
+    }
+  }
+}
+
 // Raw buffer resource over [base, base + bytes): loads past the end return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
@@ -199,9 +230,9 @@ constexpr uint32_t BUF_OOB = 0x7FFF0000u;  // a lane offset that reads zeros
 // lane offsets); activation rows past the band read zeros from outside the
 // buffer.
 // ---------------------------------------------------------------------------
-template <int NS, int D, int MSUB, int FMT, bool OBF16>
+template <int NS, int D, int MSUB, int FMT, bool OBF16, int ACT>
 __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, const Layout& L,
-                                            const Tile& tile, int n0, __amdgpu_buffer_rsrc_t xr,
+                                            const Tile& tile, int n0, int h16, __amdgpu_buffer_rsrc_t xr,
                                             const uint32_t (&a_voff)[2], __amdgpu_buffer_rsrc_t cr,
                                             __amdgpu_buffer_rsrc_t sr, void* __restrict__ y) {
   const int lane = threadIdx.x & 63;
@@ -222,9 +253,10 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
         aring[slot][ms][q] = __builtin_amdgcn_raw_buffer_load_b128(xr, a_voff[ms], kc * 256 + q * 16, 0);
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
-      cring[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, (ns * KC + kc) << 10, BUF_NT);
+      const int sub = col_sub<ACT>(ns, h16);
+      cring[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, (sub * KC + kc) << 10, BUF_NT);
       const int rec = FMT == 0 ? (kc >> 2) : (kc >> 1);
-      sring[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (ns * groups + rec) * 256, 0);
+      sring[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (sub * groups + rec) * 256, 0);
     }
   };
 
@@ -274,13 +306,22 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
 
   const float post = FMT == 1 ? reinterpret_cast<const float*>(packed + L.tscale_off)[tile.e] : 1.0f;
 #pragma unroll
-  for (int ms = 0; ms < MSUB; ++ms)
+  for (int ms = 0; ms < MSUB; ++ms) {
+    if (ACT == 1) {
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns)
-      store_tile<OBF16>(y, L.N, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + ns * 16 + r, acc[ms][ns], post);
+      for (int j = 0; j < 2; ++j)
+        store_tile_silu_mul<OBF16>(y, L.N / 2, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + j * 16 + r,
+                                   acc[ms][j], acc[ms][j + 2], post);
+    } else {
+#pragma unroll
+      for (int ns = 0; ns < NS; ++ns)
+        store_tile<OBF16>(y, L.N, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + ns * 16 + r, acc[ms][ns],
+                          post);
+    }
+  }
 }
 
-template <int NS, int D, int MS, int FMT, bool OBF16>
+template <int NS, int D, int MS, int FMT, bool OBF16, int ACT>
 __global__ __launch_bounds__(256, 3) void gmm_stream_kernel(const uint8_t* __restrict__ packed, Layout L,
                                                          const uint16_t* __restrict__ x,
                                                          uint32_t x_bytes,
@@ -301,17 +342,21 @@ __global__ __launch_bounds__(256, 3) void gmm_stream_kernel(const uint8_t* __res
   const int t = xcd + 8 * (kth / NB);
   const int nb = kth - (kth / NB) * NB;
   if (t >= ts.total) return;
+  static_assert(ACT == 0 || NS == 4, "the gate/up activation pairs two gate and two up subtiles");
   const Tile tile = locate_tile(goff, E, BM, ts, t);
-  const int n0 = (nb * 4 + wave) * NS * 16;
-  if (n0 >= L.N) return;
+  // first column (ACT 0) or first gate column (ACT 1) of this wave
+  const int n0 = (nb * 4 + wave) * (ACT == 1 ? 32 : NS * 16);
+  if (n0 >= (ACT == 1 ? L.N / 2 : L.N)) return;
+  const int h16 = ACT == 1 ? (int)(L.N / 32) : 0;
+  const int span = ACT == 1 ? h16 + 2 : NS;   // 16-column subtiles the buffer ranges cover
   const int K = (int)L.K;
   const int r = lane & 15;
   const int g = lane >> 4;
 
   const int64_t et = (int64_t)tile.e * L.NT + (n0 >> 4);
-  const __amdgpu_buffer_rsrc_t cr = buffer_rsrc(packed + ((et * L.KC) << 10), (uint32_t)(NS * L.KC) << 10);
+  const __amdgpu_buffer_rsrc_t cr = buffer_rsrc(packed + ((et * L.KC) << 10), (uint32_t)(span * L.KC) << 10);
   const __amdgpu_buffer_rsrc_t sr =
-      buffer_rsrc(packed + L.scales_off + et * L.groups * 256, (uint32_t)(NS * L.groups) * 256);
+      buffer_rsrc(packed + L.scales_off + et * L.groups * 256, (uint32_t)(span * L.groups) * 256);
   const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, x_bytes);
   uint32_t a_voff[2] = {BUF_OOB, BUF_OOB};
 #pragma unroll
@@ -324,9 +369,9 @@ __global__ __launch_bounds__(256, 3) void gmm_stream_kernel(const uint8_t* __res
     }
   }
   if (MS == 2 && tile.rows > 16)
-    stream_walk<NS, (D > 1 ? D - 1 : 1), 2, FMT, OBF16>(packed, L, tile, n0, xr, a_voff, cr, sr, y);
+    stream_walk<NS, (D > 1 ? D - 1 : 1), 2, FMT, OBF16, ACT>(packed, L, tile, n0, h16, xr, a_voff, cr, sr, y);
   else
-    stream_walk<NS, D, 1, FMT, OBF16>(packed, L, tile, n0, xr, a_voff, cr, sr, y);
+    stream_walk<NS, D, 1, FMT, OBF16, ACT>(packed, L, tile, n0, h16, xr, a_voff, cr, sr, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -441,10 +486,10 @@ __device__ __forceinline__ void tiled_prologue(std::index_sequence<Is...>, u32x4
 }
 
 // The K walk of one wave for a tile with NSUB valid 16-row subtiles.
-template <int NSUB, int FMT>
+template <int NSUB, int FMT, int ACT>
 __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_t xr,
                                              const uint32_t (&avo)[TL_LOADS], __amdgpu_buffer_rsrc_t cr,
-                                             __amdgpu_buffer_rsrc_t sr, int KC, int groups, int wave,
+                                             __amdgpu_buffer_rsrc_t sr, int KC, int groups, int h16, int wave,
                                              const uint32_t (&va)[4], f32x4_t (&acc)[TL_MS][TL_NS]) {
   constexpr int P = TL_PIPE;
   constexpr int FT = 4 * NSUB;
@@ -467,8 +512,9 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
     const int rec = scale_record<FMT>(kc);
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) {
-      cs[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, (ns * KC + kc) << 10, BUF_NT);
-      ws[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (ns * groups + rec) * 256, 0);
+      const int sub = col_sub<ACT>(ns, h16);
+      cs[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, (sub * KC + kc) << 10, BUF_NT);
+      ws[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (sub * groups + rec) * 256, 0);
     }
   };
   auto chunk = [&](auto bc, int kc) {
@@ -501,7 +547,7 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
   __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>());
 }
 
-template <int FMT, bool OBF16>
+template <int FMT, bool OBF16, int ACT>
 __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __restrict__ packed, Layout L,
                                                            const uint16_t* __restrict__ x, uint32_t x_bytes,
                                                            const int32_t* __restrict__ row_index,
@@ -520,10 +566,13 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
   const int K = (int)L.K;
   const int KC = (int)L.KC;
   const int groups = (int)L.groups;
-  const int n0 = nb * TL_BN + wave * 16 * TL_NS;
+  // first column (ACT 0) or first gate column (ACT 1) of this wave
+  const int n0 = ACT == 1 ? nb * (TL_BN / 2) + wave * 32 : nb * TL_BN + wave * 16 * TL_NS;
   // A wave past the last column still stages its share of the activations
   // and joins every barrier; its code loads read zeros and it stores nothing.
-  const bool wave_active = n0 < L.N;
+  const bool wave_active = n0 < (ACT == 1 ? L.N / 2 : L.N);
+  const int h16 = ACT == 1 ? (int)(L.N / 32) : 0;
+  const int span = ACT == 1 ? h16 + 2 : TL_NS;   // 16-column subtiles the buffer ranges cover
   const int r = lane & 15;
   const int g = lane >> 4;
   const int nsub = (tile.rows + 15) >> 4;
@@ -544,9 +593,9 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
   const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, x_bytes);
   const int64_t et = (int64_t)tile.e * L.NT + (wave_active ? (n0 >> 4) : 0);
   const __amdgpu_buffer_rsrc_t cr =
-      buffer_rsrc(packed + ((et * L.KC) << 10), wave_active ? (uint32_t)(TL_NS * KC) << 10 : 0u);
+      buffer_rsrc(packed + ((et * L.KC) << 10), wave_active ? (uint32_t)(span * KC) << 10 : 0u);
   const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(packed + L.scales_off + et * L.groups * 256,
-                                                wave_active ? (uint32_t)(TL_NS * groups) * 256 : 0u);
+                                                wave_active ? (uint32_t)(span * groups) * 256 : 0u);
   // LDS address of this lane's fragment row for step s: row r of the
   // subtile, logical segment g*4 + s
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)s_a;
@@ -561,14 +610,14 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
     for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   switch (nsub) {
-    case 1: tiled_k_walk<1, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
-    case 2: tiled_k_walk<2, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
-    case 3: tiled_k_walk<3, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
-    case 4: tiled_k_walk<4, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
-    case 5: tiled_k_walk<5, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
-    case 6: tiled_k_walk<6, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
-    case 7: tiled_k_walk<7, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
-    default: tiled_k_walk<8, FMT>(s_a, xr, avo, cr, sr, KC, groups, wave, va, acc); break;
+    case 1: tiled_k_walk<1, FMT, ACT>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc); break;
+    case 2: tiled_k_walk<2, FMT, ACT>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc); break;
+    case 3: tiled_k_walk<3, FMT, ACT>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc); break;
+    case 4: tiled_k_walk<4, FMT, ACT>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc); break;
+    case 5: tiled_k_walk<5, FMT, ACT>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc); break;
+    case 6: tiled_k_walk<6, FMT, ACT>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc); break;
+    case 7: tiled_k_walk<7, FMT, ACT>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc); break;
+    default: tiled_k_walk<8, FMT, ACT>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc); break;
   }
 
   if (!wave_active) return;
@@ -576,10 +625,17 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
 #pragma unroll
   for (int ms = 0; ms < TL_MS; ++ms) {
     if (ms < nsub) {
+      if (ACT == 1) {
 #pragma unroll
-      for (int ns = 0; ns < TL_NS; ++ns)
-        store_tile<OBF16>(y, L.N, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + ns * 16 + r,
-                          acc[ms][ns], post);
+        for (int j = 0; j < 2; ++j)
+          store_tile_silu_mul<OBF16>(y, L.N / 2, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + j * 16 + r,
+                                     acc[ms][j], acc[ms][j + 2], post);
+      } else {
+#pragma unroll
+        for (int ns = 0; ns < TL_NS; ++ns)
+          store_tile<OBF16>(y, L.N, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + ns * 16 + r,
+                            acc[ms][ns], post);
+      }
     }
   }
 }
@@ -589,45 +645,61 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
 // chunks deep, and tiles of up to 32 rows: a popular expert's band streams
 // its codes once per 32 rows instead of once per 16 (the two-subtile walk
 // keeps a one-chunk ring so that both walks fit three workgroups per CU).
-template <int FMT, bool OBF16>
+template <int FMT, bool OBF16, int ACT>
 static void launch_stream(const uint8_t* packed, const Layout& L, const uint16_t* x, uint32_t x_bytes,
                           const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
                           void* y, hipStream_t stream) {
   constexpr int NS = 4, D = 2, MS = 2, BM = 16 * MS;
-  const int NB = (int)((L.N + 64 * NS - 1) / (64 * NS));
+  // a workgroup covers 4 * 64 output columns, or 4 * 32 activation columns
+  const int64_t cols = ACT == 1 ? L.N / 2 : L.N;
+  const int NB = (int)((cols + (ACT == 1 ? 128 : 64 * NS) - 1) / (ACT == 1 ? 128 : 64 * NS));
   const int64_t em = E < M ? E : M;
   const int64_t tiles = ((M + BM - 1) / BM + em + 7) / 8 * 8;   // whole rounds of 8 tiles
-  hipLaunchKernelGGL((gmm_stream_kernel<NS, D, MS, FMT, OBF16>), dim3((unsigned)(tiles * NB)),
+  hipLaunchKernelGGL((gmm_stream_kernel<NS, D, MS, FMT, OBF16, ACT>), dim3((unsigned)(tiles * NB)),
                      dim3(256), 0, stream, packed, L, x, x_bytes, row_index, goff, E, y, NB);
 }
 
-template <int FMT, bool OBF16>
+template <int FMT, bool OBF16, int ACT>
+static void launch_tiled(const uint8_t* packed, const Layout& L, const uint16_t* x, uint32_t x_bytes,
+                         const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
+                         void* y, hipStream_t stream) {
+  const int64_t em = E < M ? E : M;
+  const int64_t cols = ACT == 1 ? L.N / 2 : L.N;
+  const int bn = ACT == 1 ? TL_BN / 2 : TL_BN;
+  const int NB = (int)((cols + bn - 1) / bn);
+  const int64_t tiles = (M + TL_BM - 1) / TL_BM + em;
+  hipLaunchKernelGGL((gmm_tiled_kernel<FMT, OBF16, ACT>), dim3((unsigned)(tiles * NB)), dim3(64 * TL_WAVES), 0,
+                     stream, packed, L, x, x_bytes, row_index, goff, E, y, NB);
+}
+
+template <int FMT, bool OBF16, int ACT>
 static void launch_gmm_t(const uint8_t* packed, const Layout& L, const uint16_t* x, int32_t x_rows,
                          const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
                          void* y, int kernel, hipStream_t stream) {
   const uint32_t x_bytes = (uint32_t)((int64_t)x_rows * L.K * 2);
-  if (kernel == 1) {
-    launch_stream<FMT, OBF16>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream);
-  } else {
-    const int64_t em = E < M ? E : M;
-    const int NB = (int)((L.N + TL_BN - 1) / TL_BN);
-    const int64_t tiles = (M + TL_BM - 1) / TL_BM + em;
-    hipLaunchKernelGGL((gmm_tiled_kernel<FMT, OBF16>), dim3((unsigned)(tiles * NB)), dim3(64 * TL_WAVES), 0,
-                       stream, packed, L, x, x_bytes, row_index, goff, E, y, NB);
-  }
+  if (kernel == 1) launch_stream<FMT, OBF16, ACT>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream);
+  else launch_tiled<FMT, OBF16, ACT>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream);
+}
+
+template <int FMT, bool OBF16>
+static void launch_gmm_a(const uint8_t* packed, const Layout& L, const uint16_t* x, int32_t x_rows,
+                         const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
+                         void* y, int act, int kernel, hipStream_t stream) {
+  if (act == 1) launch_gmm_t<FMT, OBF16, 1>(packed, L, x, x_rows, row_index, goff, E, M, y, kernel, stream);
+  else launch_gmm_t<FMT, OBF16, 0>(packed, L, x, x_rows, row_index, goff, E, M, y, kernel, stream);
 }
 
 hipError_t launch_gmm(const uint8_t* packed, int fmt, int32_t E, int32_t N, int32_t K,
                       const uint16_t* x, int32_t x_rows, const int32_t* row_index,
-                      const int32_t* group_offsets,
-                      int32_t M, void* y, int y_bf16, int kernel, hipStream_t stream) {
+                      const int32_t* group_offsets, int32_t M, void* y, int y_bf16, int act,
+                      int kernel, hipStream_t stream) {
   const Layout L = make_layout(fmt, E, N, K);
   if (fmt == 0) {
-    if (y_bf16) launch_gmm_t<0, true>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, kernel, stream);
-    else launch_gmm_t<0, false>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, kernel, stream);
+    if (y_bf16) launch_gmm_a<0, true>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, act, kernel, stream);
+    else launch_gmm_a<0, false>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, act, kernel, stream);
   } else {
-    if (y_bf16) launch_gmm_t<1, true>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, kernel, stream);
-    else launch_gmm_t<1, false>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, kernel, stream);
+    if (y_bf16) launch_gmm_a<1, true>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, act, kernel, stream);
+    else launch_gmm_a<1, false>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, act, kernel, stream);
   }
   return hipGetLastError();
 }

@@ -23,10 +23,12 @@ hipError_t launch_mxfp4_to_nvfp4(const uint8_t* scales, int32_t E, int32_t N, in
                                  hipStream_t stream);
 
 // kernel: 1 = weight-streaming waves, 2 = LDS-tiled activations.
+// act: 0 = the [M, N] matmul output, 1 = the [M, N/2] SiLU-gated gate/up
+// activation of it.
 hipError_t launch_gmm(const uint8_t* packed, int fmt, int32_t E, int32_t N, int32_t K,
                       const uint16_t* x, int32_t x_rows, const int32_t* row_index,
                       const int32_t* group_offsets,
-                      int32_t M, void* y, int y_bf16, int kernel, hipStream_t stream);
+                      int32_t M, void* y, int y_bf16, int act, int kernel, hipStream_t stream);
 
 hipError_t launch_combine(const void* y, int y_bf16, const float* w, const int32_t* pair_row,
                           int32_t T, int32_t k, int32_t N, void* out, int out_bf16,

@@ -34,7 +34,7 @@ def weights_for(p, fmt):
     return w, packed
 
 
-def run_gpu(p, packed, fmt, kernel=moe.GMM_AUTO, out_dtype=moe.F32, routed=None):
+def run_gpu(p, packed, fmt, kernel=moe.GMM_AUTO, out_dtype=moe.F32, routed=None, act=moe.ACT_NONE):
     """Route-sort on the GPU, then moe_gmm.  Returns (route dict, y tensor)."""
     E, K, N = p["E"], p["K"], p["N"]
     M = p["T"] * p["k"]
@@ -43,7 +43,7 @@ def run_gpu(p, packed, fmt, kernel=moe.GMM_AUTO, out_dtype=moe.F32, routed=None)
     f = moe.MXFP4 if fmt == "mxfp4" else moe.NVFP4
     y = moe.moe_gmm(packed, f, E, N, K, x, r["group_offsets"], M,
                     row_index=r["sorted_token"] if p["gather"] else None,
-                    out_dtype=out_dtype, kernel=kernel)
+                    out_dtype=out_dtype, kernel=kernel, act=act)
     return r, y
 
 

@@ -102,6 +102,18 @@ def test_gmm_validation(lib):
     assert lib.moe_gmm(None, 0, 8, 512, 256, FAKE, 128, None, FAKE, 128, FAKE, 0, None) == ERR_NULL
 
 
+def test_gmm_act_validation(lib):
+    f = lib.moe_gmm_act
+    args = lambda **kw: [kw.get("packed", FAKE_ALIGNED), 0, kw.get("E", 8), kw.get("N", 512),
+                         kw.get("K", 256), FAKE_ALIGNED, 128, None, FAKE, 128, FAKE, 0,
+                         kw.get("act", 1), kw.get("kernel", 0), None]
+    assert f(*args(act=2)) == ERR_FORMAT
+    assert f(*args(act=-1)) == ERR_FORMAT
+    assert f(*args(N=192)) == ERR_SHAPE                 # halves must be 64-column multiples
+    assert f(*args(packed=None)) == ERR_NULL
+    assert f(*args(N=1 << 17, K=1 << 17, E=1)) == ERR_SHAPE   # code range past 32-bit offsets
+
+
 def test_combine_validation(lib):
     f = lib.moe_combine
     assert f(FAKE_ALIGNED, 0, FAKE, FAKE, 4, 2, 6, FAKE_ALIGNED, 0, None) == ERR_SHAPE

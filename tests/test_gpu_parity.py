@@ -198,6 +198,45 @@ def test_gmm_nvfp4_general_e4m3_scales(kernel):
     assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
 
 
+# ---------------------------------------- fused gate/up activation ---
+
+def _act_problems():
+    banded = _banded_problem(270)
+    banded["N"] = 384
+    banded["codes"] = np.ascontiguousarray(
+        np.random.default_rng(271).integers(0, 256, size=(banded["E"], 384, 128), dtype=np.uint8))
+    banded["scales"] = (np.random.default_rng(272).integers(-6, -1, size=(banded["E"], 384, 8))
+                        + 127).astype(np.uint8)
+    gathered = make_problem(T=96, k=4, E=8, K=512, N=512, seed=273, routing="zipf")
+    return [banded, gathered]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("case", [0, 1])
+def test_gmm_silu_mul_full_oracle(case, fmt, kernel):
+    p = _act_problems()[case]
+    w, packed = weights_for(p, fmt)
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    ref = oracle.silu_mul(oracle.gmm(p["x"], ref_r["sorted_token"] if p["gather"] else None,
+                                     ref_r["group_offsets"], w))
+    _, y = run_gpu(p, packed, fmt, kernel=kernel, act=moe.ACT_SILU_MUL)
+    assert tuple(y.shape) == (p["T"] * p["k"], p["N"] // 2)
+    assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
+    _, yb = run_gpu(p, packed, fmt, kernel=kernel, act=moe.ACT_SILU_MUL, out_dtype=moe.BF16)
+    assert torch.equal(yb, y.to(torch.bfloat16))              # bf16 = RNE of the f32 value
+    got = yb.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= bf16_ulp(ref))
+
+
+def test_gmm_silu_mul_kernels_agree_bitwise():
+    for p in _act_problems():
+        _, packed = weights_for(p, "mxfp4")
+        _, ys = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_STREAM, act=moe.ACT_SILU_MUL)
+        _, yt = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_TILED, act=moe.ACT_SILU_MUL)
+        assert torch.equal(ys, yt)
+
+
 def test_gmm_rows_past_bands_untouched_and_canary():
     # dropped pairs leave rows [group_offsets[E], M) unwritten; nothing is
     # written past the end of y
@@ -265,6 +304,22 @@ def test_gmm_config_sampled(cfg):
 
 
 @pytest.mark.slow
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_gmm_silu_mul_config_sampled(cfg):
+    p = make_config(cfg)
+    w, packed = weights_for(p, "mxfp4")
+    r, y = run_gpu(p, packed, "mxfp4", act=moe.ACT_SILU_MUL)
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    M, H = p["T"] * p["k"], p["N"] // 2
+    rows, cols = _sample(M, H, 2000, 450 + cfg)
+    g = oracle.gmm_sampled(p["x"], ref_r["sorted_token"], ref_r["group_offsets"], w, rows, cols)
+    u = oracle.gmm_sampled(p["x"], ref_r["sorted_token"], ref_r["group_offsets"], w, rows, cols + H)
+    ref = oracle.silu(g) * u
+    got = y.cpu().numpy()[rows, cols].astype(np.float64)
+    assert rel_err(got, ref) <= REL_TOL
+
+
 def test_config5_nvfp4_equals_mxfp4_bitwise():
     p = make_config(5)
     _, packed_mx = weights_for(p, "mxfp4")
