@@ -10,7 +10,10 @@ Flash on TPU v6", section "Grouped matmul performance vs bf16", exclude it):
   down-projection workload, whose router weights are given).
 The default workload is the gate/up (w13) decode: 64 tokens, hidden 4096,
 256 experts, top-6 uniform routing, fused gate+up weight K = N = 4096 in
-MXFP4, bf16 output.
+MXFP4, bf16 output.  The layer_decode workload runs one whole routed-expert
+layer on the same tokens: route-sort -> w13 with the SiLU-gated gate/up
+activation fused (bf16 [384, 2048]) -> w2 (K = 2048, N = 4096, f32) ->
+top-k combine.
 
 One JSON line is printed.  value is the whole step's throughput in the
 algorithmic bytes of the matmul (codes + scales of the experts that received
@@ -38,6 +41,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 
 WORKLOADS = {
     "tiny": 1, "w13_decode": 2, "w2_decode": 3, "w13_prefill": 4, "nvfp4_w13": 5,
+    "layer_decode": 0,
 }
 KERNELS = {"auto": 0, "stream": 1, "tiled": 2}
 GMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_route_amd", "csrc", "gmm.hip")
@@ -123,6 +127,137 @@ def cpu_model():
     return "unknown CPU"
 
 
+def layer_cpu_baseline(p, target_s=15.0):
+    """The float64 oracle for one layer on the host: route-sort, then for as
+    many active experts (in expert order) as fit in about target_s seconds,
+    the w13 band matmul, the gate/up activation and the w2 band matmul."""
+    import oracle
+    from moe_grouped_gemm_route_amd.synth import f32_to_bf16_bits
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    r = oracle.route_sort(p["topk_ids"], p["E"])
+    off = r["group_offsets"]
+    active = [e for e in range(p["E"]) if off[e + 1] > off[e]]
+    per13 = p["N"] * p["K"] * (0.5 + 1.0 / 32)
+    per2 = p["K"] * (p["N"] // 2) * (0.5 + 1.0 / 32)
+    done, rows_done, nbytes = 0, 0, 0.0
+    while done < len(active) and time.perf_counter() - t0 < target_s:
+        e = active[done]
+        sub_off = np.array([0, off[e + 1] - off[e]], dtype=np.int32)
+        w13 = {"fmt": "mxfp4", "codes": p["codes"][e:e + 1], "scales": p["scales"][e:e + 1]}
+        w2 = {"fmt": "mxfp4", "codes": p["w2_codes"][e:e + 1], "scales": p["w2_scales"][e:e + 1]}
+        rows = r["sorted_token"][off[e]:off[e + 1]]
+        y13 = oracle.gmm(p["x"], rows, sub_off, w13)
+        h = oracle.silu_mul(y13)
+        oracle.gmm(f32_to_bf16_bits(h.astype(np.float32)), None, sub_off, w2)   # w2 reads bf16
+        nbytes += per13 + per2
+        rows_done += int(off[e + 1] - off[e])
+        done += 1
+    elapsed = time.perf_counter() - t0
+    nbytes += (p["T"] * rows_done / (p["T"] * p["k"])) * p["K"] * 2 + rows_done * (p["N"] // 2) * 2
+    return {
+        "value": round(nbytes / elapsed / 1e9, 6), "unit": "GB/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": "float64 numpy oracle on %s: route-sort of all %d pairs + w13, gate/up "
+                  "activation and w2 of the first %d of %d active experts' bands (%d rows), %.1f s"
+                  % (cpu_model(), p["T"] * p["k"], done, len(active), rows_done, elapsed),
+    }
+
+
+def run_layer(args):
+    """One routed-expert layer at decode (the layer_decode workload)."""
+    import torch
+    import moe_grouped_gemm_route_amd as moe
+    from moe_grouped_gemm_route_amd.synth import make_layer_decode
+
+    p = make_layer_decode()
+    E, K, N, T, k = p["E"], p["K"], p["N"], p["T"], p["k"]
+    M, H = T * k, N // 2
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    ids, x, tw = d(p["topk_ids"]), d(p["x"]), d(p["topk_weights"])
+    codes = d(p["codes"])
+    w13 = moe.mxfp4_encode(codes, d(p["scales"]), None, moe.MXFP4)
+    del codes
+    codes = d(p["w2_codes"])
+    w2 = moe.mxfp4_encode(codes, d(p["w2_scales"]), None, moe.MXFP4)
+    del codes
+    h = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty((M, K), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    ev = []
+
+    def step(timed):
+        r = moe.route_sort(ids, E)
+        if timed:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+        moe.moe_gmm(w13, moe.MXFP4, E, N, K, x, r["group_offsets"], M, row_index=r["sorted_token"],
+                    out_dtype=moe.BF16, act=moe.ACT_SILU_MUL, out=h)
+        if timed:
+            e[1].record()
+        moe.moe_gmm(w2, moe.MXFP4, E, K, H, h, r["group_offsets"], M, out_dtype=moe.F32, out=y2)
+        if timed:
+            e[2].record()
+            ev.append(e)
+        return moe.moe_combine(y2, tw, r["pair_row"])
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    t13 = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) / 1e3
+    t2 = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) / 1e3
+    counts = np.bincount(p["topk_ids"].reshape(-1), minlength=E)
+    active = int(np.count_nonzero(counts))
+    b13 = active * N * K * (0.5 + 1.0 / 32) + T * K * 2
+    b2 = active * K * H * (0.5 + 1.0 / 32) + M * H * 2
+    step_s = wall / args.steps
+    achieved = (b13 + b2) / (t13 + t2) / 1e9
+    out = {
+        "metric": "moe_gmm TFLOP/s and HBM GB/s (% roofline), w13/w2, 256 experts top-6",
+        "value": round((b13 + b2) / step_s / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "layer_decode", "tokens": T, "top_k": k, "experts": E,
+                   "w13": [K, N], "w2": [H, K], "routed_rows": M, "weights": "mxfp4",
+                   "activations": "bf16", "gate_up": "silu(gate) * up fused into the w13 epilogue",
+                   "step": "route_sort + moe_gmm(w13, act) + moe_gmm(w2) + moe_combine"},
+        "w13_us": round(t13 * 1e6, 2),
+        "w2_us": round(t2 * 1e6, 2),
+        "active_experts": active,
+        "algorithmic_bytes": int(b13 + b2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = layer_cpu_baseline(p)
+        out["gpu_over_cpu"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +276,10 @@ def main():
               "(the routed-expert matmul would shard by experts; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "layer_decode" and not args.copy_calibration:
+        run_layer(args)
+        return
 
     import torch
     import moe_grouped_gemm_route_amd as moe

@@ -128,3 +128,18 @@ def make_config(i):
     p["out"] = c["out"]
     p["config"] = i
     return p
+
+
+@lru_cache(maxsize=1)
+def make_layer_decode():
+    """One MoE layer at decode: config 2's tokens, routing, router weights and
+    fused gate+up (w13) weights, plus down-projection (w2) weights of the
+    expert intermediate size (K = 2048, N = 4096) drawn with seed 6 (only
+    their codes and scales are taken from that draw)."""
+    p = dict(make_config(2))
+    w2 = make_problem(T=8, k=6, E=p["E"], K=p["N"] // 2, N=p["K"], seed=6,
+                      exp_range=CONFIGS[2]["exp_range"])
+    p["w2_codes"], p["w2_scales"] = w2["codes"], w2["scales"]
+    p["name"] = "layer_decode"
+    return p
+

@@ -237,6 +237,32 @@ def test_gmm_silu_mul_kernels_agree_bitwise():
         assert torch.equal(ys, yt)
 
 
+def test_layer_chain_small():
+    # route -> w13 with the fused activation (bf16) -> w2 on the band-ordered
+    # activation (f32) -> combine, each stage against the oracle on the
+    # previous GPU stage's output
+    p = make_problem(T=80, k=3, E=8, K=256, N=512, seed=280, routing="zipf")
+    H, D = p["N"] // 2, p["K"]
+    rng = np.random.default_rng(281)
+    w2c = rng.integers(0, 256, size=(p["E"], D, H // 2), dtype=np.uint8)
+    w2s = (rng.integers(-6, -1, size=(p["E"], D, H // 32)) + 127).astype(np.uint8)
+    w13, p13 = weights_for(p, "mxfp4")
+    pk2 = moe.mxfp4_encode(to_dev(w2c), to_dev(w2s), None, moe.MXFP4)
+    r, h = run_gpu(p, p13, "mxfp4", out_dtype=moe.BF16, act=moe.ACT_SILU_MUL)
+    M = p["T"] * p["k"]
+    y2 = moe.moe_gmm(pk2, moe.MXFP4, p["E"], D, H, h, r["group_offsets"], M)
+    out = moe.moe_combine(y2, to_dev(p["topk_weights"]), r["pair_row"])
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    ref_h = oracle.silu_mul(oracle.gmm(p["x"], ref_r["sorted_token"], ref_r["group_offsets"], w13))
+    got_h = h.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got_h - ref_h) <= bf16_ulp(ref_h))
+    h_bits = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref_y2 = oracle.gmm(h_bits, None, ref_r["group_offsets"], {"fmt": "mxfp4", "codes": w2c, "scales": w2s})
+    assert rel_err(y2.cpu().numpy(), ref_y2) <= REL_TOL
+    ref_out = oracle.combine(y2.cpu().numpy(), p["topk_weights"], ref_r["pair_row"])
+    assert rel_err(out.cpu().numpy(), ref_out) <= REL_TOL
+
+
 def test_gmm_rows_past_bands_untouched_and_canary():
     # dropped pairs leave rows [group_offsets[E], M) unwritten; nothing is
     # written past the end of y
