@@ -9,7 +9,8 @@ routed-expert path computes, written from these pages:
   "1. Four bits that v6e can't hold": expert-sorted token bands, the grouped
   matmul loop nest, the e2m1 code semantics and the per-32 block scale applied
   before the matmul; section "Grouped matmul performance vs bf16": the NVFP4
-  variant (e2m1 codes with per-16 E4M3 block scales).
+  variant (e2m1 codes with per-16 E4M3 block scales) and the bf16-weight
+  grouped matmul it is compared with.
 * "DeepSeek-V4-Flash-0731-NVFP4" (model card), section "The lossless weight
   cast": the MXFP4 -> NVFP4 power-of-two scale mapping; section
   "Verification": the -0 -> +0 canonicalisation note.

@@ -27,15 +27,23 @@ def bf16_bits_to_f64(bits):
 def dense_weights(w, e):
     """Dense float64 weight of expert e, laid out [N, K].
 
-    w is a dict with 'fmt' ('mxfp4' or 'nvfp4'), 'codes' [E,N,K/2] and either
-    'scales' [E,N,K/32] (E8M0) or 'block_scales' [E,N,K/16] (E4M3) plus
-    'tensor_scale' [E]."""
+    w is a dict with 'fmt' ('mxfp4', 'nvfp4' or 'bf16'): 'codes' [E,N,K/2] and
+    either 'scales' [E,N,K/32] (E8M0) or 'block_scales' [E,N,K/16] (E4M3) plus
+    'tensor_scale' [E]; or, for the bf16 comparison arm of "Grouped matmul
+    performance vs bf16", 'weights' [E,N,K] bf16 bit patterns."""
     if w["fmt"] == "mxfp4":
         return decode_mxfp4(w["codes"][e], w["scales"][e])
     if w["fmt"] == "nvfp4":
         return decode_nvfp4(w["codes"][e][None], w["block_scales"][e][None],
                             np.asarray(w["tensor_scale"])[e:e + 1])[0]
+    if w["fmt"] == "bf16":
+        return bf16_bits_to_f64(w["weights"][e])
     raise ValueError("unknown weight format %r" % (w["fmt"],))
+
+
+def weight_columns(w):
+    """N of the weight dict w."""
+    return (w["weights"] if w["fmt"] == "bf16" else w["codes"]).shape[1]
 
 
 def gmm(x_bits, row_index, group_offsets, w):
@@ -50,7 +58,7 @@ def gmm(x_bits, row_index, group_offsets, w):
     off = np.asarray(group_offsets, dtype=np.int64)
     E = off.size - 1
     M = len(row_index) if row_index is not None else x.shape[0]
-    N = w["codes"].shape[1]
+    N = weight_columns(w)
     y = np.full((M, N), np.nan)
     for e in range(E):
         lo, hi = int(off[e]), int(off[e + 1])
@@ -65,6 +73,8 @@ def gmm(x_bits, row_index, group_offsets, w):
 
 def _weight_column(w, e, n):
     """Decoded float64 column n of expert e's weight, length K."""
+    if w["fmt"] == "bf16":
+        return bf16_bits_to_f64(w["weights"][e, n])
     if w["fmt"] == "mxfp4":
         codes = w["codes"][e, n]
         v = e2m1_decode(np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(-1))

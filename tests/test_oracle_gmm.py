@@ -184,3 +184,46 @@ def test_gmm_nvfp4_brute_force_random_block_scales():
                             * e4m3[e, n, kk // 16] * float(ts[e]))
                 assert abs(y[row, n] - ref) <= 1e-12 * (1 + abs(ref))
     assert np.allclose(s, y[rows, cols], rtol=1e-14, atol=1e-14)
+
+
+def _bf16_fields(bits):
+    """Value of a bf16 bit pattern from its sign, exponent and mantissa fields."""
+    s, ex, man = bits >> 15, (bits >> 7) & 0xFF, bits & 0x7F
+    assert ex != 0xFF
+    mag = math.ldexp(man / 128.0, -126) if ex == 0 else math.ldexp(1 + man / 128.0, ex - 127)
+    return -mag if s else mag
+
+
+def test_gmm_bf16_weights_brute_force():
+    # the bf16 comparison arm: weights given as bf16 bit patterns
+    p = make_problem(T=5, k=2, E=3, K=64, N=6, seed=13)
+    rng = np.random.default_rng(14)
+    wb = rng.integers(0, 1 << 16, size=(3, 6, 64), dtype=np.uint16)
+    wb[(wb >> 7 & 0xFF) == 0xFF] &= 0x807F                   # no inf / NaN patterns
+    r = oracle.route_sort(p["topk_ids"], p["E"])
+    y = oracle.gmm(p["x"], r["sorted_token"], r["group_offsets"], {"fmt": "bf16", "weights": wb})
+    for t in range(p["T"]):
+        for j in range(p["k"]):
+            e = int(p["topk_ids"][t, j])
+            row = r["pair_row"][t * p["k"] + j]
+            for n in range(6):
+                ref = sum(_x_val(p["x"][t, kk]) * _bf16_fields(int(wb[e, n, kk])) for kk in range(64))
+                assert abs(y[row, n] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_gmm_bf16_of_decoded_mxfp4_equals_mxfp4():
+    # every decoded MXFP4 weight is a bf16 value, so the bf16 arm fed the
+    # decoded weights computes the same sums
+    import struct
+    p = make_problem(T=20, k=2, E=4, K=128, N=16, seed=15, exp_range=(-6, -2))
+    wb = np.zeros((4, 16, 128), dtype=np.uint16)
+    for e in range(4):
+        for n in range(16):
+            for kk in range(128):
+                f = struct.unpack("<I", struct.pack("<f", _w_brute(p, e, n, kk)))[0]
+                assert f & 0xFFFF == 0
+                wb[e, n, kk] = f >> 16
+    r = oracle.route_sort(p["topk_ids"], p["E"])
+    y_mx = oracle.gmm(p["x"], r["sorted_token"], r["group_offsets"], _mx(p))
+    y_bf = oracle.gmm(p["x"], r["sorted_token"], r["group_offsets"], {"fmt": "bf16", "weights": wb})
+    assert np.array_equal(y_mx, y_bf)
