@@ -43,7 +43,11 @@ typedef enum {
   MOE_ERR_HIP = 5          /* the HIP runtime reported a launch error         */
 } moe_status_t;
 
-typedef enum { MOE_W_MXFP4 = 0, MOE_W_NVFP4 = 1 } moe_wfmt_t;
+typedef enum {
+  MOE_W_MXFP4 = 0,  /* e2m1 codes, E8M0 scale per 32 along K                  */
+  MOE_W_NVFP4 = 1,  /* e2m1 codes, E4M3 scale per 16 along K, f32 per expert  */
+  MOE_W_BF16 = 2    /* bf16 weights: the comparison arm (moe_bf16_encode)     */
+} moe_wfmt_t;
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
 /* Epilogue of moe_gmm_act. */
@@ -121,6 +125,26 @@ int mxfp4_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
                  void* packed, void* stream);
 
 /*
+ * moe_bf16_encode - load-time repack of bf16 expert weights for the bf16
+ * comparison arm.
+ *
+ * Source: "Running DeepSeek V4 Flash on TPU v6", section "Grouped matmul
+ * performance vs bf16": the MXFP4 grouped matmul is measured against the same
+ * grouped matmul with bf16 weights.  The packed layout has the chunks and the
+ * K assignment of the 4-bit layout, each 16-bit weight in place of its code,
+ * so moe_gmm with fmt MOE_W_BF16 on the decoded weights of an MXFP4 matrix
+ * issues the same MFMAs on the same operands and returns the same bits.
+ *
+ * weights   [E, N, K] bf16 bit patterns, K contiguous, 16-byte aligned.
+ * packed    out, moe_packed_weight_bytes(MOE_W_BF16, E, N, K) = E*N*K*2
+ *           bytes, 256-aligned.
+ * Limits as mxfp4_encode, and K < 2^26.  (mxfp4_encode rejects MOE_W_BF16
+ * with MOE_ERR_FORMAT.)
+ */
+int moe_bf16_encode(const uint16_t* weights, int32_t E, int32_t N, int32_t K, void* packed,
+                    void* stream);
+
+/*
  * moe_gmm - routed-expert grouped matmul, W4A16 on bf16 MFMA.
  *
  * Source: "Running DeepSeek V4 Flash on TPU v6", section "1. Four bits that
@@ -154,7 +178,9 @@ int moe_gmm(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
 
 /* moe_gmm_ex - moe_gmm with an explicit kernel configuration
  * (moe_gmm_kernel_t).  Every configuration computes the same sums in the same
- * order, so all of them return bitwise identical y. */
+ * order, so all of them return bitwise identical y.  Weights in MOE_W_BF16
+ * run on the weight-streaming kernel only (MOE_GMM_TILED returns
+ * MOE_ERR_UNSUPPORTED). */
 int moe_gmm_ex(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
                const uint16_t* x, int32_t x_rows, const int32_t* row_index,
                const int32_t* group_offsets, int32_t M, void* y, int y_dtype,
@@ -179,7 +205,8 @@ int moe_gmm_ex(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
  *   NVFP4 tensor scale), evaluated in f32; the [M, N] sums are never written.
  *   Requires N % 128 == 0 and (N/32 + 2) * (K/128) KiB < 4 GiB.
  * Every kernel configuration returns bitwise identical y.  Other arguments,
- * limits and errors as moe_gmm; an unknown act returns MOE_ERR_FORMAT.
+ * limits and errors as moe_gmm; an unknown act returns MOE_ERR_FORMAT, and
+ * MOE_ACT_SILU_MUL with MOE_W_BF16 weights MOE_ERR_UNSUPPORTED.
  */
 int moe_gmm_act(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
                 const uint16_t* x, int32_t x_rows, const int32_t* row_index,

@@ -14,12 +14,12 @@ import os
 import torch
 
 __all__ = [
-    "MXFP4", "NVFP4", "F32", "BF16", "GMM_AUTO", "GMM_STREAM", "GMM_TILED", "ACT_NONE", "ACT_SILU_MUL",
+    "MXFP4", "NVFP4", "W_BF16", "F32", "BF16", "GMM_AUTO", "GMM_STREAM", "GMM_TILED", "ACT_NONE", "ACT_SILU_MUL",
     "MoeGmmError", "library", "route_sort", "packed_weight_bytes", "mxfp4_encode",
-    "moe_gmm", "moe_combine", "mxfp4_to_nvfp4", "debug_decode",
+    "moe_gmm", "moe_combine", "mxfp4_to_nvfp4", "debug_decode", "bf16_encode",
 ]
 
-MXFP4, NVFP4 = 0, 1
+MXFP4, NVFP4, W_BF16 = 0, 1, 2
 F32, BF16 = 0, 1
 GMM_AUTO, GMM_STREAM, GMM_TILED = 0, 1, 2
 ACT_NONE, ACT_SILU_MUL = 0, 1
@@ -33,6 +33,7 @@ _SIGNATURES = {
     "moe_route_sort": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_packed_weight_bytes": (_sz, [ctypes.c_int, _i32, _i32, _i32]),
     "mxfp4_encode": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "moe_bf16_encode": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp]),
     "moe_gmm": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32,
                                _vp, ctypes.c_int, _vp]),
     "moe_gmm_ex": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32,
@@ -146,6 +147,18 @@ def mxfp4_encode(codes, scales, tensor_scale=None, fmt=MXFP4):
     packed = torch.empty(packed_weight_bytes(fmt, E, N, K), dtype=torch.uint8, device=codes.device)
     _check(library().mxfp4_encode(fmt, _ptr(codes), _ptr(scales), _ptr(tensor_scale), E, N, K,
                                   _ptr(packed), _stream()))
+    return packed
+
+
+def bf16_encode(weights):
+    """moe_bf16_encode.  weights [E, N, K] bfloat16 (or its int16/uint16 bit
+    view) -> the packed uint8 buffer of the bf16 comparison arm."""
+    wb = _bits16(weights, "weights")
+    if wb.dim() != 3:
+        raise MoeGmmError("weights must be [E, N, K]")
+    E, N, K = wb.shape
+    packed = torch.empty(packed_weight_bytes(W_BF16, E, N, K), dtype=torch.uint8, device=wb.device)
+    _check(library().moe_bf16_encode(_ptr(wb), E, N, K, _ptr(packed), _stream()))
     return packed
 
 

@@ -13,7 +13,7 @@ namespace {
 constexpr int64_t kMaxRows = int64_t(1) << 24;
 constexpr int64_t kMaxCodeBytes = int64_t(1) << 40;
 
-bool fmt_ok(int fmt) { return fmt == MOE_W_MXFP4 || fmt == MOE_W_NVFP4; }
+bool fmt_ok(int fmt) { return fmt == MOE_W_MXFP4 || fmt == MOE_W_NVFP4 || fmt == MOE_W_BF16; }
 bool dtype_ok(int d) { return d == MOE_F32 || d == MOE_BF16; }
 
 // Weight sizes the packed layout and the kernels support.
@@ -22,6 +22,9 @@ int check_weight_shape(int fmt, int32_t E, int32_t N, int32_t K) {
   if (E < 1 || N < 1 || K < 1) return MOE_ERR_SHAPE;
   if (K % 128 != 0 || N % 64 != 0) return MOE_ERR_SHAPE;
   if ((int64_t)E * N * (K / 2) >= kMaxCodeBytes) return MOE_ERR_SHAPE;
+  // bf16 weights: a wave's two 4 KiB-per-chunk subtiles are addressed with
+  // 32-bit offsets
+  if (fmt == MOE_W_BF16 && (int64_t)2 * (K / 128) * 4096 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
@@ -64,12 +67,23 @@ int mxfp4_encode(int fmt, const uint8_t* codes, const uint8_t* scales, const flo
   const int st = check_weight_shape(fmt, E, N, K);
   if (st != MOE_OK) return st;
   if (!codes || !scales || !packed) return MOE_ERR_NULL;
+  if (fmt == MOE_W_BF16) return MOE_ERR_FORMAT;          /* moe_bf16_encode packs those */
   if (fmt == MOE_W_NVFP4 && !tensor_scale) return MOE_ERR_NULL;
   if (fmt == MOE_W_MXFP4 && tensor_scale) return MOE_ERR_FORMAT;
   if (((uintptr_t)codes & 15) || ((uintptr_t)packed & 255)) return MOE_ERR_SHAPE;
   return hip_status(moe::launch_encode(fmt, codes, scales, tensor_scale, E, N, K,
                                        static_cast<uint8_t*>(packed),
                                        static_cast<hipStream_t>(stream)));
+}
+
+int moe_bf16_encode(const uint16_t* weights, int32_t E, int32_t N, int32_t K, void* packed,
+                    void* stream) {
+  const int st = check_weight_shape(MOE_W_BF16, E, N, K);
+  if (st != MOE_OK) return st;
+  if (!weights || !packed) return MOE_ERR_NULL;
+  if (((uintptr_t)weights & 15) || ((uintptr_t)packed & 255)) return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_bf16_encode(weights, E, N, K, static_cast<uint8_t*>(packed),
+                                            static_cast<hipStream_t>(stream)));
 }
 
 int moe_gmm_act(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint16_t* x,
@@ -86,6 +100,11 @@ int moe_gmm_act(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, co
   // activation rows are addressed with 32-bit byte offsets
   if ((int64_t)x_rows * K * 2 >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
   if (((uintptr_t)packed & 255) || ((uintptr_t)x & 15)) return MOE_ERR_SHAPE;
+  if (fmt == MOE_W_BF16) {
+    // the bf16 comparison arm: weight-streaming kernel, plain output
+    if (kernel == MOE_GMM_TILED || act != MOE_ACT_NONE) return MOE_ERR_UNSUPPORTED;
+    kernel = MOE_GMM_STREAM;
+  }
   if (act == MOE_ACT_SILU_MUL) {
     // gate and up halves of 64-column multiples; one wave's code range spans
     // both halves of an expert and is addressed with 32-bit offsets

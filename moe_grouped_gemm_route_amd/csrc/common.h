@@ -44,6 +44,14 @@ __host__ __device__ inline Layout make_layout(int fmt, int64_t E, int64_t N, int
   Layout L;
   L.E = E; L.N = N; L.K = K;
   L.NT = N / 16; L.KC = K / 128; L.KB = K / 32;
+  if (fmt == 2) {
+    // bf16 weights (the comparison arm): 4 KiB chunks, no scales
+    L.groups = 0;
+    L.codes_bytes = E * N * K * 2;
+    L.scales_off = L.tscale_off = L.total_bytes = L.codes_bytes;
+    L.scales_bytes = 0;
+    return L;
+  }
   const int64_t per = fmt == 0 ? 4 : 2;   // chunks per 256-byte scale record
   L.groups = (L.KC + per - 1) / per;
   L.codes_bytes = E * N * K / 2;
@@ -52,6 +60,18 @@ __host__ __device__ inline Layout make_layout(int fmt, int64_t E, int64_t N, int
   L.tscale_off = L.scales_off + L.scales_bytes;
   L.total_bytes = L.tscale_off + (fmt == 0 ? 0 : ((E * 4 + 255) / 256) * 256);
   return L;
+}
+
+// bf16 weights (the comparison arm) use the same chunks and the same K
+// assignment, four times as large: chunk (e, nt, kc) = 4 KiB at
+// ((e*NT + nt)*KC + kc) * 4 KiB, holding for step s (1 KiB at s * 1 KiB)
+// lane l's eight bf16 of column nt*16 + (l & 15), K indices
+// kc*128 + (l >> 4)*32 + s*8 .. +7, at byte 16 l.
+__host__ __device__ inline int64_t bf16_run_offset(const Layout& L, int64_t e, int64_t n, int64_t k8) {
+  const int64_t k = k8 * 8;
+  const int64_t nt = n >> 4, kc = k >> 7, g = (k >> 5) & 3, st = (k >> 3) & 3;
+  const int64_t lane = (g << 4) | (n & 15);
+  return (((e * L.NT + nt) * L.KC + kc) << 12) + (st << 10) + (lane << 4);
 }
 
 // Byte offset of the 16-byte code run of (e, column n, scale block kb).

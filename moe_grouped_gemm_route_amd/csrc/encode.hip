@@ -1,5 +1,6 @@
-// Load-time weight repack (mxfp4_encode), its inverse check
-// (moe_debug_decode) and the lossless MXFP4 -> NVFP4 scale cast.
+// Load-time weight repack (mxfp4_encode, and moe_bf16_encode for the bf16
+// comparison arm), its inverse check (moe_debug_decode) and the lossless
+// MXFP4 -> NVFP4 scale cast.
 //
 // "Running DeepSeek V4 Flash on TPU v6", section "1. Four bits that v6e can't
 // hold": the weights are re-laid-out once at load and stay 4 bits each.  Here
@@ -83,6 +84,43 @@ hipError_t launch_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
   return hipGetLastError();
 }
 
+// bf16 weights [E, N, K] -> packed chunks: one thread per 16-byte run of
+// eight consecutive K indices (canonical order, coalesced reads).
+__global__ __launch_bounds__(256) void encode_bf16_kernel(const u32x4_t* __restrict__ w, Layout L,
+                                                          uint8_t* __restrict__ packed) {
+  const int64_t runs = L.E * L.N * (L.K / 8);
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < runs;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t k8 = i % (L.K / 8);
+    const int64_t n = (i / (L.K / 8)) % L.N;
+    const int64_t e = i / ((L.K / 8) * L.N);
+    *reinterpret_cast<u32x4_t*>(packed + bf16_run_offset(L, e, n, k8)) = w[i];
+  }
+}
+
+hipError_t launch_bf16_encode(const uint16_t* w, int32_t E, int32_t N, int32_t K, uint8_t* packed,
+                              hipStream_t stream) {
+  const Layout L = make_layout(2, E, N, K);
+  const int64_t runs = L.E * L.N * (L.K / 8);
+  const int grid = (int)((runs + 255) / 256 < 65536 ? (runs + 255) / 256 : 65536);
+  hipLaunchKernelGGL(encode_bf16_kernel, dim3(grid), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4_t*>(w), L, packed);
+  return hipGetLastError();
+}
+
+// Dense bf16 [E, N, K] from packed bf16 chunks (the inverse of the above).
+__global__ __launch_bounds__(256) void unpack_bf16_kernel(const uint8_t* __restrict__ packed, Layout L,
+                                                          u32x4_t* __restrict__ w) {
+  const int64_t runs = L.E * L.N * (L.K / 8);
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < runs;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t k8 = i % (L.K / 8);
+    const int64_t n = (i / (L.K / 8)) % L.N;
+    const int64_t e = i / ((L.K / 8) * L.N);
+    w[i] = *reinterpret_cast<const u32x4_t*>(packed + bf16_run_offset(L, e, n, k8));
+  }
+}
+
 // Dense bf16 [E, N, K] from the packed buffer: one thread per code run.
 __global__ __launch_bounds__(256) void debug_decode_kernel(const uint8_t* __restrict__ packed, int fmt,
                                                            Layout L, uint16_t* __restrict__ w) {
@@ -118,6 +156,13 @@ __global__ __launch_bounds__(256) void debug_decode_kernel(const uint8_t* __rest
 hipError_t launch_debug_decode(const uint8_t* packed, int fmt, int32_t E, int32_t N, int32_t K,
                                uint16_t* w, hipStream_t stream) {
   const Layout L = make_layout(fmt, E, N, K);
+  if (fmt == 2) {
+    const int64_t runs = L.E * L.N * (L.K / 8);
+    const int grid = (int)((runs + 255) / 256 < 65536 ? (runs + 255) / 256 : 65536);
+    hipLaunchKernelGGL(unpack_bf16_kernel, dim3(grid), dim3(256), 0, stream, packed, L,
+                       reinterpret_cast<u32x4_t*>(w));
+    return hipGetLastError();
+  }
   const int64_t runs = L.E * L.N * L.KB;
   const int grid = (int)((runs + 255) / 256 < 65536 ? (runs + 255) / 256 : 65536);
   hipLaunchKernelGGL(debug_decode_kernel, dim3(grid), dim3(256), 0, stream, packed, fmt, L, w);

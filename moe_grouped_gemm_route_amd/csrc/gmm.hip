@@ -242,7 +242,10 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
   const uint32_t c_voff = lane * 16;
   const uint32_t s_voff = lane * 4;
 
-  u32x4_t cring[D][NS];
+  // 16-byte weight words per lane per chunk: one word of codes, or (bf16
+  // weights, FMT 2) the four steps' bf16 operands themselves
+  constexpr int CW = FMT == 2 ? 4 : 1;
+  u32x4_t cring[D][NS][CW];
   uint32_t sring[D][NS];
   u32x4_t aring[D][MSUB][4];
   auto load_step = [&](int slot, int kc) {
@@ -254,9 +257,16 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
       const int sub = col_sub<ACT>(ns, h16);
-      cring[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, (sub * KC + kc) << 10, BUF_NT);
-      const int rec = FMT == 0 ? (kc >> 2) : (kc >> 1);
-      sring[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (sub * groups + rec) * 256, 0);
+      if constexpr (FMT == 2) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          cring[slot][ns][s] =
+              __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, ((sub * KC + kc) << 12) + s * 1024, BUF_NT);
+      } else {
+        cring[slot][ns][0] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, (sub * KC + kc) << 10, BUF_NT);
+        const int rec = FMT == 0 ? (kc >> 2) : (kc >> 1);
+        sring[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (sub * groups + rec) * 256, 0);
+      }
     }
   };
 
@@ -274,12 +284,13 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
     for (int d = 0; d < D; ++d) {
       const int kc = k0 + d;
       if (kc < KC) {
-        u32x4_t c[NS], a[MSUB][4];
+        u32x4_t c[NS][CW], a[MSUB][4];
         uint32_t w[NS];
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
-          c[ns] = cring[d][ns];
-          w[ns] = sring[d][ns];
+#pragma unroll
+          for (int i = 0; i < CW; ++i) c[ns][i] = cring[d][ns][i];
+          if (FMT != 2) w[ns] = sring[d][ns];
         }
 #pragma unroll
         for (int ms = 0; ms < MSUB; ++ms)
@@ -287,14 +298,19 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
           for (int q = 0; q < 4; ++q) a[ms][q] = aring[d][ms][q];
         if (kc + D < KC) load_step(d, kc + D);
         float lo[NS], hi[NS];
+        bool general = false;
+        if constexpr (FMT != 2) {
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) chunk_scales<FMT>(w[ns], kc, lo[ns], hi[ns]);
-        const bool general = general_scales<FMT, NS>(lo, hi);
+          for (int ns = 0; ns < NS; ++ns) chunk_scales<FMT>(w[ns], kc, lo[ns], hi[ns]);
+          general = general_scales<FMT, NS>(lo, hi);
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
           for (int ns = 0; ns < NS; ++ns) {
-            const u32x4_t b = decode_step<FMT>(c[ns][s], s < 2 ? lo[ns] : hi[ns], general);
+            u32x4_t b;
+            if constexpr (FMT == 2) b = c[ns][s];
+            else b = decode_step<FMT>(c[ns][0][s], s < 2 ? lo[ns] : hi[ns], general);
 #pragma unroll
             for (int ms = 0; ms < MSUB; ++ms)
               acc[ms][ns] = mfma(as_bf16x8(a[ms][s]), as_bf16x8(b), acc[ms][ns]);
@@ -354,7 +370,8 @@ __global__ __launch_bounds__(256, 3) void gmm_stream_kernel(const uint8_t* __res
   const int g = lane >> 4;
 
   const int64_t et = (int64_t)tile.e * L.NT + (n0 >> 4);
-  const __amdgpu_buffer_rsrc_t cr = buffer_rsrc(packed + ((et * L.KC) << 10), (uint32_t)(span * L.KC) << 10);
+  constexpr int CSH = FMT == 2 ? 12 : 10;   // log2 of a chunk's bytes
+  const __amdgpu_buffer_rsrc_t cr = buffer_rsrc(packed + ((et * L.KC) << CSH), (uint32_t)(span * L.KC) << CSH);
   const __amdgpu_buffer_rsrc_t sr =
       buffer_rsrc(packed + L.scales_off + et * L.groups * 256, (uint32_t)(span * L.groups) * 256);
   const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, x_bytes);
@@ -649,7 +666,9 @@ template <int FMT, bool OBF16, int ACT>
 static void launch_stream(const uint8_t* packed, const Layout& L, const uint16_t* x, uint32_t x_bytes,
                           const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
                           void* y, hipStream_t stream) {
-  constexpr int NS = 4, D = 2, MS = 2, BM = 16 * MS;
+  // bf16 weights (FMT 2) carry four times the bytes per column, so their
+  // waves own two subtiles (32 columns) to keep the same register budget
+  constexpr int NS = FMT == 2 ? 2 : 4, D = 2, MS = 2, BM = 16 * MS;
   // a workgroup covers 4 * 64 output columns, or 4 * 32 activation columns
   const int64_t cols = ACT == 1 ? L.N / 2 : L.N;
   const int NB = (int)((cols + (ACT == 1 ? 128 : 64 * NS) - 1) / (ACT == 1 ? 128 : 64 * NS));
@@ -677,16 +696,25 @@ static void launch_gmm_t(const uint8_t* packed, const Layout& L, const uint16_t*
                          const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
                          void* y, int kernel, hipStream_t stream) {
   const uint32_t x_bytes = (uint32_t)((int64_t)x_rows * L.K * 2);
-  if (kernel == 1) launch_stream<FMT, OBF16, ACT>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream);
-  else launch_tiled<FMT, OBF16, ACT>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream);
+  if constexpr (FMT == 2) {
+    // the bf16 comparison arm has the weight-streaming kernel only
+    launch_stream<FMT, OBF16, ACT>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream);
+  } else {
+    if (kernel == 1) launch_stream<FMT, OBF16, ACT>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream);
+    else launch_tiled<FMT, OBF16, ACT>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream);
+  }
 }
 
 template <int FMT, bool OBF16>
 static void launch_gmm_a(const uint8_t* packed, const Layout& L, const uint16_t* x, int32_t x_rows,
                          const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
                          void* y, int act, int kernel, hipStream_t stream) {
-  if (act == 1) launch_gmm_t<FMT, OBF16, 1>(packed, L, x, x_rows, row_index, goff, E, M, y, kernel, stream);
-  else launch_gmm_t<FMT, OBF16, 0>(packed, L, x, x_rows, row_index, goff, E, M, y, kernel, stream);
+  if constexpr (FMT == 2) {
+    launch_gmm_t<FMT, OBF16, 0>(packed, L, x, x_rows, row_index, goff, E, M, y, kernel, stream);
+  } else {
+    if (act == 1) launch_gmm_t<FMT, OBF16, 1>(packed, L, x, x_rows, row_index, goff, E, M, y, kernel, stream);
+    else launch_gmm_t<FMT, OBF16, 0>(packed, L, x, x_rows, row_index, goff, E, M, y, kernel, stream);
+  }
 }
 
 hipError_t launch_gmm(const uint8_t* packed, int fmt, int32_t E, int32_t N, int32_t K,
@@ -697,9 +725,12 @@ hipError_t launch_gmm(const uint8_t* packed, int fmt, int32_t E, int32_t N, int3
   if (fmt == 0) {
     if (y_bf16) launch_gmm_a<0, true>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, act, kernel, stream);
     else launch_gmm_a<0, false>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, act, kernel, stream);
-  } else {
+  } else if (fmt == 1) {
     if (y_bf16) launch_gmm_a<1, true>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, act, kernel, stream);
     else launch_gmm_a<1, false>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, act, kernel, stream);
+  } else {
+    if (y_bf16) launch_gmm_a<2, true>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, act, kernel, stream);
+    else launch_gmm_a<2, false>(packed, L, x, x_rows, row_index, group_offsets, E, M, y, act, kernel, stream);
   }
   return hipGetLastError();
 }

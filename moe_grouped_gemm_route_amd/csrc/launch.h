@@ -15,6 +15,9 @@ hipError_t launch_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
                          const float* tensor_scale, int32_t E, int32_t N, int32_t K,
                          uint8_t* packed, hipStream_t stream);
 
+hipError_t launch_bf16_encode(const uint16_t* w, int32_t E, int32_t N, int32_t K, uint8_t* packed,
+                              hipStream_t stream);
+
 hipError_t launch_debug_decode(const uint8_t* packed, int fmt, int32_t E, int32_t N, int32_t K,
                                uint16_t* w, hipStream_t stream);
 

@@ -40,7 +40,7 @@ def run_gpu(p, packed, fmt, kernel=moe.GMM_AUTO, out_dtype=moe.F32, routed=None,
     M = p["T"] * p["k"]
     r = routed if routed is not None else moe.route_sort(to_dev(p["topk_ids"]), E)
     x = to_dev(p["x"])
-    f = moe.MXFP4 if fmt == "mxfp4" else moe.NVFP4
+    f = {"mxfp4": moe.MXFP4, "nvfp4": moe.NVFP4, "bf16": moe.W_BF16}[fmt]
     y = moe.moe_gmm(packed, f, E, N, K, x, r["group_offsets"], M,
                     row_index=r["sorted_token"] if p["gather"] else None,
                     out_dtype=out_dtype, kernel=kernel, act=act)

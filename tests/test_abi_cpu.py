@@ -102,6 +102,18 @@ def test_gmm_validation(lib):
     assert lib.moe_gmm(None, 0, 8, 512, 256, FAKE, 128, None, FAKE, 128, FAKE, 0, None) == ERR_NULL
 
 
+def test_bf16_arm_validation(lib):
+    assert lib.moe_packed_weight_bytes(2, 8, 512, 256) == 8 * 512 * 256 * 2
+    assert lib.mxfp4_encode(2, FAKE, FAKE, None, 8, 512, 256, FAKE_ALIGNED, None) == ERR_FORMAT
+    assert lib.moe_bf16_encode(None, 8, 512, 256, FAKE_ALIGNED, None) == ERR_NULL
+    assert lib.moe_bf16_encode(FAKE, 8, 512, 200, FAKE_ALIGNED, None) == ERR_SHAPE
+    assert lib.moe_bf16_encode(FAKE, 8, 512, 256, ctypes.c_void_p((1 << 30) + 16), None) == ERR_SHAPE
+    ex = lib.moe_gmm_ex
+    assert ex(FAKE_ALIGNED, 2, 8, 512, 256, FAKE_ALIGNED, 128, None, FAKE, 128, FAKE, 0, 2, None) == 4
+    act = lib.moe_gmm_act
+    assert act(FAKE_ALIGNED, 2, 8, 512, 256, FAKE_ALIGNED, 128, None, FAKE, 128, FAKE, 0, 1, 0, None) == 4
+
+
 def test_gmm_act_validation(lib):
     f = lib.moe_gmm_act
     args = lambda **kw: [kw.get("packed", FAKE_ALIGNED), 0, kw.get("E", 8), kw.get("N", 512),

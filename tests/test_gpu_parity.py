@@ -263,6 +263,45 @@ def test_layer_chain_small():
     assert rel_err(out.cpu().numpy(), ref_out) <= REL_TOL
 
 
+# ------------------------------------------------ bf16 comparison arm ---
+
+def _bf16_weights(E, N, K, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((E, N, K), dtype=np.float32) * 0.05
+    return (x.view(np.uint32) >> 16).astype(np.uint16)         # truncation: any bf16 will do
+
+
+def test_bf16_encode_round_trip():
+    wb = _bf16_weights(3, 192, 384, 290)
+    packed = moe.bf16_encode(to_dev(wb))
+    back = moe.debug_decode(packed, moe.W_BF16, 3, 192, 384)
+    assert np.array_equal(back.cpu().numpy().view(np.uint16), wb)
+
+
+@pytest.mark.parametrize("case", [0, 1, 2])
+def test_gmm_bf16_weights_full_oracle(case):
+    p = [_banded_problem(291), _small(1), _small(2)][case]
+    wb = _bf16_weights(p["E"], p["N"], p["K"], 292 + case)
+    packed = moe.bf16_encode(to_dev(wb))
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    ref = oracle.gmm(p["x"], ref_r["sorted_token"] if p["gather"] else None, ref_r["group_offsets"],
+                     {"fmt": "bf16", "weights": wb})
+    _, y = run_gpu(p, packed, "bf16")
+    assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
+
+
+def test_gmm_bf16_of_decoded_mxfp4_is_bitwise_mxfp4():
+    # the bf16 arm on the decoded MXFP4 weights issues the same MFMAs on the
+    # same operands: the two outputs are equal bit for bit
+    p = _banded_problem(295)
+    _, packed = weights_for(p, "mxfp4")
+    dec = moe.debug_decode(packed, moe.MXFP4, p["E"], p["N"], p["K"])
+    pb = moe.bf16_encode(dec)
+    _, y4 = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_STREAM)
+    _, y16 = run_gpu(p, pb, "bf16")
+    assert torch.equal(y4, y16)
+
+
 def test_gmm_rows_past_bands_untouched_and_canary():
     # dropped pairs leave rows [group_offsets[E], M) unwritten; nothing is
     # written past the end of y
