@@ -13,7 +13,10 @@ The default workload is the gate/up (w13) decode: 64 tokens, hidden 4096,
 MXFP4, bf16 output.  The layer_decode workload runs one whole routed-expert
 layer on the same tokens: route-sort -> w13 with the SiLU-gated gate/up
 activation fused (bf16 [384, 2048]) -> w2 (K = 2048, N = 4096, f32) ->
-top-k combine.
+top-k combine.  The bf16_w13_decode and bf16_w2_decode workloads time the
+bf16-weight comparison arm on the decoded weights of configs 2 and 3 (the
+same values, four times the bytes) next to the MXFP4 kernel on the same
+inputs, and report the MXFP4 speedup.
 
 One JSON line is printed.  value is the whole step's throughput in the
 algorithmic bytes of the matmul (codes + scales of the experts that received
@@ -41,7 +44,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 
 WORKLOADS = {
     "tiny": 1, "w13_decode": 2, "w2_decode": 3, "w13_prefill": 4, "nvfp4_w13": 5,
-    "layer_decode": 0,
+    "layer_decode": 0, "bf16_w13_decode": 2, "bf16_w2_decode": 3,
 }
 KERNELS = {"auto": 0, "stream": 1, "tiled": 2}
 GMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_route_amd", "csrc", "gmm.hip")
@@ -54,11 +57,12 @@ def gmm_source_hash():
 
 
 def algorithmic_bytes(p, fmt):
-    """Codes + scales of every expert with a non-empty band, plus the
-    activation bytes the matmul reads (unique token rows when gathering)."""
+    """Codes + scales (or bf16 weights) of every expert with a non-empty band,
+    plus the activation bytes the matmul reads (unique token rows when
+    gathering)."""
     counts = np.bincount(p["topk_ids"].reshape(-1), minlength=p["E"])
     active = int(np.count_nonzero(counts))
-    per_weight = 0.5 + (1.0 / 32 if fmt == "mxfp4" else 1.0 / 16)
+    per_weight = {"mxfp4": 0.5 + 1.0 / 32, "nvfp4": 0.5 + 1.0 / 16, "bf16": 2.0}[fmt]
     w_bytes = active * p["N"] * p["K"] * per_weight + (active * 4 if fmt == "nvfp4" else 0)
     x_rows = p["T"] if p["gather"] else p["T"] * p["k"]
     return w_bytes + x_rows * p["K"] * 2, active
@@ -297,6 +301,7 @@ def main():
 
     cfg = WORKLOADS[args.workload]
     p = make_config(cfg)
+    bf16_arm = args.workload.startswith("bf16_")
     fmt = "nvfp4" if cfg == 5 else "mxfp4"
     out_dtype = args.out_dtype or p["out"]
     odt = moe.BF16 if out_dtype == "bf16" else moe.F32
@@ -321,6 +326,13 @@ def main():
         wf = moe.NVFP4
         assert err.item() == 0
     del codes
+    packed_mx = None
+    if bf16_arm:
+        # the comparison arm streams the decoded weights as bf16
+        dense = moe.debug_decode(packed, wf, E, N, K)
+        packed_mx, packed = packed, moe.bf16_encode(dense)
+        del dense
+        fmt, wf = "bf16", moe.W_BF16
     tw = d(p["topk_weights"])
     combine = cfg == 3
     y = torch.empty((M, N), dtype=torch.bfloat16 if odt == moe.BF16 else torch.float32, device=dev)
@@ -351,6 +363,24 @@ def main():
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    mx_ms = None
+    if bf16_arm:
+        # the MXFP4 kernel on the same inputs, for the speedup
+        r = moe.route_sort(ids, E)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        for i in range(args.warmup):
+            moe.moe_gmm(packed_mx, moe.MXFP4, E, N, K, x, r["group_offsets"], M,
+                        row_index=r["sorted_token"] if p["gather"] else None,
+                        out_dtype=odt, kernel=kernel, out=y)
+        e[0].record()
+        for i in range(args.steps):
+            moe.moe_gmm(packed_mx, moe.MXFP4, E, N, K, x, r["group_offsets"], M,
+                        row_index=r["sorted_token"] if p["gather"] else None,
+                        out_dtype=odt, kernel=kernel, out=y)
+            e[i + 1].record()
+        torch.cuda.synchronize()
+        mx_ms = [e[i].elapsed_time(e[i + 1]) for i in range(args.steps)]
 
     gmm_ms = [a.elapsed_time(b) for a, b in ev]
     gmm_avg_s = float(np.mean(gmm_ms)) / 1e3
@@ -395,7 +425,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens": T, "top_k": k, "experts": E, "K": K,
-                   "N": N, "routed_rows": M, "weights": fmt, "activations": "bf16",
+                   "N": N, "routed_rows": M,
+                   "weights": fmt + (" (decoded MXFP4 weights)" if bf16_arm else ""),
+                   "activations": "bf16",
                    "output": out_dtype, "kernel": args.kernel,
                    "step": "route_sort + moe_gmm" + (" + moe_combine" if combine else "")},
         "gmm_us": round(gmm_avg_s * 1e6, 2),
@@ -407,8 +439,12 @@ def main():
         "algorithmic_bytes": int(nbytes),
         "roofline": roof,
     }
+    if mx_ms is not None:
+        mx_s = float(np.mean(mx_ms)) / 1e3
+        out["mxfp4_us"] = round(mx_s * 1e6, 2)
+        out["mxfp4_speedup_over_bf16"] = round(gmm_avg_s / mx_s, 3)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(p, fmt, unit)
+        out["cpu_baseline"] = cpu_baseline(p, "mxfp4" if bf16_arm else fmt, unit)
         out["gpu_over_cpu"] = round(value / out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
 
