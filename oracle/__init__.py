@@ -18,6 +18,9 @@ routed-expert path computes, written from these pages:
   the expert reduction is deterministic (fixed order, no atomics).
 * The gate/up activation after the fused w13 matmul, which the pages name but
   do not define: the SiLU-gated product of the two column halves (act.py).
+* "DeepSeek-V4-Flash-0731-NVFP4": the W4A4 execution with 4-bit activations,
+  here with MXFP4 (power-of-two block scale) activation quantization
+  (quant.py).
 
 It shares no code with the HIP path and imports nothing from it.
 """
@@ -34,6 +37,7 @@ from .formats import (  # noqa: F401
     mxfp4_to_nvfp4,
 )
 from .route import route_sort  # noqa: F401
-from .gmm import gmm, gmm_sampled, dense_weights  # noqa: F401
+from .gmm import gmm, gmm_w4a4, gmm_sampled, dense_weights  # noqa: F401
+from .quant import nearest_e2m1, quantize_mxfp4_rows, dequantize_mxfp4_rows  # noqa: F401
 from .combine import combine  # noqa: F401
 from .act import silu, silu_mul  # noqa: F401

@@ -54,7 +54,19 @@ def gmm(x_bits, row_index, group_offsets, w):
     group_offsets: [E+1] band boundaries.  Rows past group_offsets[E] are NaN
     (they belong to no band and are never written by the kernel).
     Returns Y [M, N] float64, M = len(row_index) or x rows."""
-    x = bf16_bits_to_f64(x_bits)
+    return gmm_dense_x(bf16_bits_to_f64(x_bits), row_index, group_offsets, w)
+
+
+def gmm_w4a4(xq_codes, xq_scales, row_index, group_offsets, w):
+    """The W4A4 variant: the activations are given MXFP4-quantized (codes
+    [rows, K/2], E8M0 scales [rows, K/32], see quant.py) and enter the same
+    grouped matmul with their dequantized values."""
+    from .formats import decode_mxfp4
+    return gmm_dense_x(decode_mxfp4(xq_codes, xq_scales), row_index, group_offsets, w)
+
+
+def gmm_dense_x(x, row_index, group_offsets, w):
+    """gmm() on float64 activation rows x."""
     off = np.asarray(group_offsets, dtype=np.int64)
     E = off.size - 1
     M = len(row_index) if row_index is not None else x.shape[0]
