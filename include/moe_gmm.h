@@ -214,6 +214,51 @@ int moe_gmm_act(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
                 int act, int kernel, void* stream);
 
 /*
+ * moe_mxfp4_quantize - MXFP4 quantization of bf16 activation rows, for the
+ * W4A4 variant.
+ *
+ * Source: "DeepSeek-V4-Flash-0731-NVFP4" (model card) runs the routed experts
+ * W4A4 (its table row for the routed experts and its "Performance"
+ * discussion: activations quantized to 4-bit floats too).  That card uses
+ * NVFP4 with calibrated per-tensor scales; gfx950's scaled matrix
+ * instructions take power-of-two block scales, so this library quantizes to
+ * MXFP4: for each block of 32 consecutive K values of a row,
+ *   X = floor(log2(max |v|)) - 2, scale byte = X + 127 clamped to [0, 254]
+ *   (an all-zero block: byte 0), code = the e2m1 value nearest to v / 2^X
+ *   (a tie to the even mantissa bit, magnitudes past 6 to 6), sign kept.
+ *
+ * x        bf16 [R, K], K contiguous, 16-byte aligned; finite values.
+ * codes    out [R, K/2] uint8, the even K index in the low nibble, 16-byte aligned.
+ * scales   out [R, K/32] uint8 E8M0.
+ * Limits: K % 32 == 0, R * K < 2^40.
+ */
+int moe_mxfp4_quantize(const uint16_t* x, int32_t R, int32_t K, uint8_t* codes, uint8_t* scales,
+                       void* stream);
+
+/*
+ * moe_gmm_w4a4 - the grouped matmul with MXFP4 weights and MXFP4-quantized
+ * activations, on the scaled FP4 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4).
+ *
+ * Source: the grouped matmul of moe_gmm ("Running DeepSeek V4 Flash on TPU
+ * v6", section "1. Four bits that v6e can't hold") with the W4A4 execution of
+ * "DeepSeek-V4-Flash-0731-NVFP4" (see moe_mxfp4_quantize).
+ *
+ * For every row r of band e:  y[r, n] = sum_k A[src(r), k] * W_e[n, k] with
+ * A = e2m1(code) * 2^(scale - 127) of the quantized activations; the products
+ * are exact, the sums f32 (the matrix unit adds each 128-deep chunk, then
+ * the running sum).  act as moe_gmm_act.
+ *
+ * packed         mxfp4_encode output for (MOE_W_MXFP4, E, N, K).
+ * xq_codes       [x_rows, K/2] from moe_mxfp4_quantize, 16-byte aligned.
+ * xq_scales      [x_rows, K/32].
+ * Other arguments, limits and errors as moe_gmm_act, with
+ * x_rows * K/2 < 2^31.  LDS-tiled kernel (meant for prefill bands).
+ */
+int moe_gmm_w4a4(const void* packed, int32_t E, int32_t N, int32_t K, const uint8_t* xq_codes,
+                 const uint8_t* xq_scales, int32_t x_rows, const int32_t* row_index,
+                 const int32_t* group_offsets, int32_t M, void* y, int y_dtype, int act, void* stream);
+
+/*
  * moe_combine - top-k weighted unpermute back to token order.
  *
  * Source: the band layout of "Running DeepSeek V4 Flash on TPU v6", section

@@ -17,6 +17,7 @@ __all__ = [
     "MXFP4", "NVFP4", "W_BF16", "F32", "BF16", "GMM_AUTO", "GMM_STREAM", "GMM_TILED", "ACT_NONE", "ACT_SILU_MUL",
     "MoeGmmError", "library", "route_sort", "packed_weight_bytes", "mxfp4_encode",
     "moe_gmm", "moe_combine", "mxfp4_to_nvfp4", "debug_decode", "bf16_encode",
+    "mxfp4_quantize", "moe_gmm_w4a4",
 ]
 
 MXFP4, NVFP4, W_BF16 = 0, 1, 2
@@ -34,6 +35,9 @@ _SIGNATURES = {
     "moe_packed_weight_bytes": (_sz, [ctypes.c_int, _i32, _i32, _i32]),
     "mxfp4_encode": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "moe_bf16_encode": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp]),
+    "moe_mxfp4_quantize": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
+    "moe_gmm_w4a4": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp,
+                                    ctypes.c_int, ctypes.c_int, _vp]),
     "moe_gmm": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32,
                                _vp, ctypes.c_int, _vp]),
     "moe_gmm_ex": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32,
@@ -194,6 +198,55 @@ def moe_gmm(packed, fmt, E, N, K, x, group_offsets, M, row_index=None, out_dtype
     _check(library().moe_gmm_act(_ptr(packed), fmt, E, N, K, _ptr(xb), xb.shape[0], _ptr(row_index),
                                  _ptr(group_offsets), M, _ptr(out), out_dtype, act, kernel,
                                  _stream()))
+    return out
+
+
+def mxfp4_quantize(x):
+    """moe_mxfp4_quantize.  x bf16 [R, K] -> (codes [R, K/2] uint8, scales
+    [R, K/32] uint8)."""
+    xb = _bits16(x, "x")
+    if xb.dim() != 2 or xb.shape[1] % 32:
+        raise MoeGmmError("x must be [R, K] with K a multiple of 32")
+    R, K = xb.shape
+    codes = torch.empty((R, K // 2), dtype=torch.uint8, device=xb.device)
+    scales = torch.empty((R, K // 32), dtype=torch.uint8, device=xb.device)
+    _check(library().moe_mxfp4_quantize(_ptr(xb), R, K, _ptr(codes), _ptr(scales), _stream()))
+    return codes, scales
+
+
+def moe_gmm_w4a4(packed, E, N, K, xq_codes, xq_scales, group_offsets, M, row_index=None,
+                 out_dtype=F32, act=ACT_NONE, out=None):
+    """moe_gmm_w4a4.  xq_codes [rows, K/2], xq_scales [rows, K/32] from
+    mxfp4_quantize; packed MXFP4 weights.  Returns y [M, N] or [M, N/2]."""
+    _dev(packed, torch.uint8, "packed", 1)
+    _dev(xq_codes, torch.uint8, "xq_codes", 2)
+    _dev(xq_scales, torch.uint8, "xq_scales", 2)
+    _dev(group_offsets, torch.int32, "group_offsets", 1)
+    rows = xq_codes.shape[0]
+    if tuple(xq_codes.shape) != (rows, K // 2) or tuple(xq_scales.shape) != (rows, K // 32):
+        raise MoeGmmError("xq_codes must be [rows, K/2] and xq_scales [rows, K/32]")
+    if group_offsets.numel() != E + 1:
+        raise MoeGmmError("group_offsets must have E+1 entries")
+    if row_index is None:
+        if rows < M:
+            raise MoeGmmError("the activations must have M rows when row_index is None")
+    else:
+        _dev(row_index, torch.int32, "row_index", 1)
+        if row_index.numel() < M:
+            raise MoeGmmError("row_index must have M entries")
+    if packed.numel() < packed_weight_bytes(MXFP4, E, N, K):
+        raise MoeGmmError("packed buffer too small")
+    dt = torch.float32 if out_dtype == F32 else torch.bfloat16
+    cols = N // 2 if act == ACT_SILU_MUL else N
+    if out is None:
+        out = torch.empty((M, cols), dtype=dt, device=packed.device)
+    else:
+        _dev(out, dt, "out", 2)
+        if tuple(out.shape) != (M, cols):
+            raise MoeGmmError("out must be [M, %d]" % cols)
+    _check(library().moe_gmm_w4a4(_ptr(packed), E, N, K, _ptr(xq_codes), _ptr(xq_scales), rows,
+                                  _ptr(row_index), _ptr(group_offsets), M, _ptr(out), out_dtype, act,
+                                  _stream()))
     return out
 
 

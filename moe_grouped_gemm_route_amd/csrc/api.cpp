@@ -128,6 +128,36 @@ int moe_gmm_ex(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, con
                      MOE_ACT_NONE, kernel, stream);
 }
 
+int moe_mxfp4_quantize(const uint16_t* x, int32_t R, int32_t K, uint8_t* codes, uint8_t* scales,
+                       void* stream) {
+  if (!x || !codes || !scales) return MOE_ERR_NULL;
+  if (R < 1 || K < 32 || K % 32 != 0 || (int64_t)R * K >= (int64_t(1) << 40)) return MOE_ERR_SHAPE;
+  if (((uintptr_t)x & 15) || ((uintptr_t)codes & 15)) return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_quantize_mxfp4(x, R, K, codes, scales, static_cast<hipStream_t>(stream)));
+}
+
+int moe_gmm_w4a4(const void* packed, int32_t E, int32_t N, int32_t K, const uint8_t* xq_codes,
+                 const uint8_t* xq_scales, int32_t x_rows, const int32_t* row_index,
+                 const int32_t* group_offsets, int32_t M, void* y, int y_dtype, int act, void* stream) {
+  const int st = check_weight_shape(MOE_W_MXFP4, E, N, K);
+  if (st != MOE_OK) return st;
+  if (!dtype_ok(y_dtype)) return MOE_ERR_FORMAT;
+  if (act != MOE_ACT_NONE && act != MOE_ACT_SILU_MUL) return MOE_ERR_FORMAT;
+  if (!packed || !xq_codes || !xq_scales || !group_offsets || !y) return MOE_ERR_NULL;
+  if (M < 1 || M > kMaxRows) return MOE_ERR_SHAPE;
+  if (x_rows < 1 || x_rows > kMaxRows || (!row_index && x_rows < M)) return MOE_ERR_SHAPE;
+  // activation codes are addressed with 32-bit byte offsets
+  if ((int64_t)x_rows * (K / 2) >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  if (((uintptr_t)packed & 255) || ((uintptr_t)xq_codes & 15)) return MOE_ERR_SHAPE;
+  if (act == MOE_ACT_SILU_MUL) {
+    if (N % 128 != 0) return MOE_ERR_SHAPE;
+    if ((int64_t)(N / 32 + 2) * (K / 128) * 1024 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
+  }
+  return hip_status(moe::launch_gmm_w4a4(static_cast<const uint8_t*>(packed), E, N, K, xq_codes, xq_scales,
+                                         x_rows, row_index, group_offsets, M, y, y_dtype == MOE_BF16, act,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int moe_gmm(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint16_t* x,
             int32_t x_rows, const int32_t* row_index, const int32_t* group_offsets, int32_t M,
             void* y, int y_dtype, void* stream) {

@@ -169,6 +169,77 @@ hipError_t launch_debug_decode(const uint8_t* packed, int fmt, int32_t E, int32_
   return hipGetLastError();
 }
 
+// MXFP4 quantization of bf16 activation rows (the W4A4 variant): one thread
+// per block of 32 K values.  Scale exponent X = floor(log2(max |v|)) - 2 from
+// the bf16 bits of the block maximum (magnitudes of finite bf16 values order
+// like their 15-bit patterns); each value goes to the nearest e2m1 value of
+// v / 2^X, a tie to the even mantissa bit and magnitudes past 6 to 6, with its
+// sign.  v / 2^X is exact in f32 (a power-of-two product) and so is every
+// comparison with the rounding thresholds.
+__device__ __forceinline__ uint32_t e2m1_nearest_code(float a) {
+  // thresholds between neighbouring e2m1 magnitudes; an equal value is a tie
+  // and goes to the even code
+  return a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+       : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+}
+
+__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const u32x4_t* __restrict__ x, int64_t blocks,
+                                                             u32x4_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+  for (int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; b < blocks;
+       b += (int64_t)gridDim.x * blockDim.x) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = x[b * 4 + i];
+    uint32_t amax = 0;   // largest 15-bit magnitude pattern
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = v[i][j] & 0x7FFFu, hi = (v[i][j] >> 16) & 0x7FFFu;
+        amax = amax > lo ? amax : lo;
+        amax = amax > hi ? amax : hi;
+      }
+    int byte = 0;
+    if (amax != 0) {
+      const int ef = (int)(amax >> 7);
+      // floor(log2 amax): the exponent of a normal value; for a subnormal,
+      // -133 + the position of the leading mantissa bit
+      const int fl = ef != 0 ? ef - 127 : -133 + (31 - __builtin_clz(amax & 0x7Fu));
+      const int X = fl - 2;
+      byte = X + 127 < 0 ? 0 : (X + 127 > 254 ? 254 : X + 127);
+    }
+    // 2^-X with X = byte - 127: the f32 with exponent field 254 - byte.  A
+    // finite bf16 maximum gives byte <= 252 (its exponent is at most 127),
+    // so the field lies in [2, 254] and the value is a normal power of two.
+    const float inv = __builtin_bit_cast(float, (uint32_t)(254 - (byte > 252 ? 252 : byte)) << 23);
+    u32x4_t out = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t bits = (v[i][j] >> (16 * h)) & 0xFFFFu;
+          const float a = __builtin_bit_cast(float, (bits & 0x7FFFu) << 16) * inv;
+          const uint32_t code = e2m1_nearest_code(a) | ((bits >> 12) & 8u);
+          const int k = (i * 4 + j) * 2 + h;          // 0..31 within the block
+          out[k >> 3] |= code << (4 * (k & 7));
+        }
+    codes[b] = out;
+    scales[b] = (uint8_t)byte;
+  }
+}
+
+hipError_t launch_quantize_mxfp4(const uint16_t* x, int32_t R, int32_t K, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t stream) {
+  const int64_t blocks = (int64_t)R * (K / 32);
+  const int grid = (int)((blocks + 255) / 256 < 65536 ? (blocks + 255) / 256 : 65536);
+  hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3(grid), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4_t*>(x), blocks, reinterpret_cast<u32x4_t*>(codes), scales);
+  return hipGetLastError();
+}
+
 // Clears a small int32 counter with a kernel (kept out of memset nodes so the
 // call stays safe to record into a HIP graph).
 __global__ void zero_i32_kernel(int32_t* p, int n) {

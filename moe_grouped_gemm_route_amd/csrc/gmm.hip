@@ -657,6 +657,222 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
   }
 }
 
+// ---------------------------------------------------------------------------
+// W4A4 kernel (prefill): MXFP4 weights times MXFP4-quantized activations on
+// gfx950's scaled FP4 MFMA, v_mfma_scale_f32_16x16x128_f8f6f4 (e2m1 A and B).
+// Its operands match the packed weights exactly: lane l supplies the 32 codes
+// (16 bytes, low nibble first) of column (l & 15), K block (l >> 4) of a
+// 128-deep chunk and that block's E8M0 scale (byte 0 of the scale operand);
+// A is the same for row (l & 15) of the activations, and the f32 result has
+// the layout of the bf16 MFMA's.  One MFMA covers a whole chunk of a 16 x 16
+// tile.
+//
+// Same workgroup shape, schedule and waits as the tiled kernel: 4 waves,
+// 128 rows x 256 columns, the activation chunk staged in LDS by direct-to-LDS
+// loads and double-buffered, the weight codes and scale words one chunk
+// ahead.  A staged chunk holds the 128 rows' codes (64 bytes per row, rows
+// contiguous: 8 KiB) and their scale dwords (wave w loads rows 32w .. 32w+31
+// into its own 256-byte slot; lanes 32..63 read past the buffer and write
+// zeros into the slot's unused half).
+// ---------------------------------------------------------------------------
+constexpr int Q_CODE_BYTES = TL_BM * 64;                     // 8 KiB
+constexpr int Q_SCALE_BYTES = TL_WAVES * 256;
+constexpr int Q_STAGE_BYTES = Q_CODE_BYTES + Q_SCALE_BYTES;
+constexpr int Q_LOADS = Q_CODE_BYTES / 1024 / TL_WAVES;      // 1 KiB code loads per wave per chunk
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4_t mfma_fp4(u32x4_t a, uint32_t sa, u32x4_t b, uint32_t sb, f32x4_t c) {
+  const i32x8_t A = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  const i32x8_t B = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  // cbsz = blgp = 4: e2m1 operands; op_sel 0: byte 0 of each scale operand
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
+template <int NSUB, int ACT>
+__device__ __forceinline__ void w4a4_k_walk(uint8_t* s_q, __amdgpu_buffer_rsrc_t qcr, __amdgpu_buffer_rsrc_t qsr,
+                                            const uint32_t (&cvo)[Q_LOADS], uint32_t svo,
+                                            __amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t sr, int KC,
+                                            int groups, int h16, int wave, f32x4_t (&acc)[TL_MS][TL_NS]) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const uint32_t c_voff = lane * 16, s_voff = lane * 4;
+  u32x4_t cs[2][TL_NS];
+  uint32_t ws[2][TL_NS];
+  auto stage = [&](int kc) {
+    uint8_t* buf = s_q + (kc & 1) * Q_STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < Q_LOADS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qcr, (lds_ptr_t)(buf + (wave * Q_LOADS + j) * 1024), 16, cvo[j],
+                                               kc * 64, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(qsr, (lds_ptr_t)(buf + Q_CODE_BYTES + wave * 256), 4, svo, kc * 4, 0, 0);
+  };
+  auto load_codes = [&](int slot, int kc) {
+    const int rec = scale_record<0>(kc);
+#pragma unroll
+    for (int ns = 0; ns < TL_NS; ++ns) {
+      const int sub = col_sub<ACT>(ns, h16);
+      cs[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, (sub * KC + kc) << 10, BUF_NT);
+      ws[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (sub * groups + rec) * 256, 0);
+    }
+  };
+  auto chunk = [&](auto bc, int kc) {
+    constexpr int d = decltype(bc)::value;   // kc & 1: LDS buffer and code slot
+    stage(min(kc + 1, KC - 1));
+    __builtin_amdgcn_sched_barrier(0);       // the activation loads go first
+    load_codes(d ^ 1, min(kc + 1, KC - 1));
+    const uint8_t* buf = s_q + d * Q_STAGE_BYTES;
+    uint32_t sb[TL_NS];
+#pragma unroll
+    for (int ns = 0; ns < TL_NS; ++ns) sb[ns] = (ws[d][ns] >> (8 * (kc & 3))) & 0xFFu;
+#pragma unroll
+    for (int ms = 0; ms < NSUB; ++ms) {
+      const int row = ms * 16 + r;
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(buf + row * 64 + g * 16);
+      const uint32_t sdw = *reinterpret_cast<const uint32_t*>(buf + Q_CODE_BYTES + (row >> 5) * 256 + (row & 31) * 4);
+      const uint32_t sa = (sdw >> (8 * g)) & 0xFFu;
+#pragma unroll
+      for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = mfma_fp4(a, sa, cs[d][ns], sb[ns], acc[ms][ns]);
+    }
+    vm_wait_barrier<2 * TL_NS>();
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  stage(0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_codes(0, 0);
+  vm_wait_barrier<0>();
+  int k0 = 0;
+  for (; k0 + 2 <= KC; k0 += 2) {
+    chunk(B0{}, k0);
+    chunk(B1{}, k0 + 1);
+  }
+  if (k0 < KC) chunk(B0{}, k0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>());
+}
+
+template <bool OBF16, int ACT>
+__global__ __launch_bounds__(256, 2) void gmm_w4a4_kernel(const uint8_t* __restrict__ packed, Layout L,
+                                                          const uint8_t* __restrict__ qcodes,
+                                                          const uint8_t* __restrict__ qscales, int32_t x_rows,
+                                                          const int32_t* __restrict__ row_index,
+                                                          const int32_t* __restrict__ goff, int E,
+                                                          void* __restrict__ y, int NB) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_q[2 * Q_STAGE_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const TileScan ts = scan_tiles(goff, E, TL_BM);
+  const int item = work_item(ts.total * NB, true);
+  if (item < 0) return;
+  const int t = item / NB;
+  const int nb = item - t * NB;
+  const Tile tile = locate_tile(goff, E, TL_BM, ts, t);
+  const int K = (int)L.K;
+  const int KC = (int)L.KC;
+  const int groups = (int)L.groups;
+  const int n0 = ACT == 1 ? nb * (TL_BN / 2) + wave * 32 : nb * TL_BN + wave * 16 * TL_NS;
+  const bool wave_active = n0 < (ACT == 1 ? L.N / 2 : L.N);
+  const int h16 = ACT == 1 ? (int)(L.N / 32) : 0;
+  const int span = ACT == 1 ? h16 + 2 : TL_NS;
+  const int r = lane & 15;
+  const int nsub = (tile.rows + 15) >> 4;
+
+  // Staging sources: code load j of wave w covers rows 16(Q_LOADS w + j) + l/4,
+  // 16-byte segment l & 3 of the row's 64 code bytes per chunk; the scale load
+  // of wave w covers rows 32w + l for lanes l < 32.  Rows past the band read
+  // zeros (their accumulator rows are never stored).
+  uint32_t cvo[Q_LOADS];
+#pragma unroll
+  for (int j = 0; j < Q_LOADS; ++j) {
+    const int rl = 16 * (wave * Q_LOADS + j) + (lane >> 2);
+    cvo[j] = BUF_OOB;
+    if (rl < tile.rows) {
+      const int64_t src = row_index ? row_index[tile.m0 + rl] : tile.m0 + rl;
+      cvo[j] = (uint32_t)(src * (K / 2) + (lane & 3) * 16);
+    }
+  }
+  uint32_t svo = BUF_OOB;
+  {
+    const int rl = 32 * wave + lane;
+    if (lane < 32 && rl < tile.rows) {
+      const int64_t src = row_index ? row_index[tile.m0 + rl] : tile.m0 + rl;
+      svo = (uint32_t)(src * (K / 32));
+    }
+  }
+  const __amdgpu_buffer_rsrc_t qcr = buffer_rsrc(qcodes, (uint32_t)((int64_t)x_rows * (K / 2)));
+  const __amdgpu_buffer_rsrc_t qsr = buffer_rsrc(qscales, (uint32_t)((int64_t)x_rows * (K / 32)));
+  const int64_t et = (int64_t)tile.e * L.NT + (wave_active ? (n0 >> 4) : 0);
+  const __amdgpu_buffer_rsrc_t cr =
+      buffer_rsrc(packed + ((et * L.KC) << 10), wave_active ? (uint32_t)(span * KC) << 10 : 0u);
+  const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(packed + L.scales_off + et * L.groups * 256,
+                                                wave_active ? (uint32_t)(span * groups) * 256 : 0u);
+
+  f32x4_t acc[TL_MS][TL_NS];
+#pragma unroll
+  for (int ms = 0; ms < TL_MS; ++ms)
+#pragma unroll
+    for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  switch (nsub) {
+    case 1: w4a4_k_walk<1, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
+    case 2: w4a4_k_walk<2, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
+    case 3: w4a4_k_walk<3, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
+    case 4: w4a4_k_walk<4, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
+    case 5: w4a4_k_walk<5, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
+    case 6: w4a4_k_walk<6, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
+    case 7: w4a4_k_walk<7, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
+    default: w4a4_k_walk<8, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
+  }
+
+  if (!wave_active) return;
+#pragma unroll
+  for (int ms = 0; ms < TL_MS; ++ms) {
+    if (ms < nsub) {
+      if (ACT == 1) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          store_tile_silu_mul<OBF16>(y, L.N / 2, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + j * 16 + r,
+                                     acc[ms][j], acc[ms][j + 2], 1.0f);
+      } else {
+#pragma unroll
+        for (int ns = 0; ns < TL_NS; ++ns)
+          store_tile<OBF16>(y, L.N, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + ns * 16 + r,
+                            acc[ms][ns], 1.0f);
+      }
+    }
+  }
+}
+
+template <bool OBF16, int ACT>
+static void launch_w4a4_t(const uint8_t* packed, const Layout& L, const uint8_t* qcodes, const uint8_t* qscales,
+                          int32_t x_rows, const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
+                          void* y, hipStream_t stream) {
+  const int64_t em = E < M ? E : M;
+  const int64_t cols = ACT == 1 ? L.N / 2 : L.N;
+  const int bn = ACT == 1 ? TL_BN / 2 : TL_BN;
+  const int NB = (int)((cols + bn - 1) / bn);
+  const int64_t tiles = (M + TL_BM - 1) / TL_BM + em;
+  hipLaunchKernelGGL((gmm_w4a4_kernel<OBF16, ACT>), dim3((unsigned)(tiles * NB)), dim3(64 * TL_WAVES), 0,
+                     stream, packed, L, qcodes, qscales, x_rows, row_index, goff, E, y, NB);
+}
+
+hipError_t launch_gmm_w4a4(const uint8_t* packed, int32_t E, int32_t N, int32_t K, const uint8_t* qcodes,
+                           const uint8_t* qscales, int32_t x_rows, const int32_t* row_index,
+                           const int32_t* group_offsets, int32_t M, void* y, int y_bf16, int act,
+                           hipStream_t stream) {
+  const Layout L = make_layout(0, E, N, K);
+  if (act == 1) {
+    if (y_bf16) launch_w4a4_t<true, 1>(packed, L, qcodes, qscales, x_rows, row_index, group_offsets, E, M, y, stream);
+    else launch_w4a4_t<false, 1>(packed, L, qcodes, qscales, x_rows, row_index, group_offsets, E, M, y, stream);
+  } else {
+    if (y_bf16) launch_w4a4_t<true, 0>(packed, L, qcodes, qscales, x_rows, row_index, group_offsets, E, M, y, stream);
+    else launch_w4a4_t<false, 0>(packed, L, qcodes, qscales, x_rows, row_index, group_offsets, E, M, y, stream);
+  }
+  return hipGetLastError();
+}
+
 // Stream-kernel shape: four 16-column subtiles per wave (64 columns, fewer
 // and longer waves amortise the tile lookup and activation loads), a ring two
 // chunks deep, and tiles of up to 32 rows: a popular expert's band streams

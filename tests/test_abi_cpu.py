@@ -114,6 +114,26 @@ def test_bf16_arm_validation(lib):
     assert act(FAKE_ALIGNED, 2, 8, 512, 256, FAKE_ALIGNED, 128, None, FAKE, 128, FAKE, 0, 1, 0, None) == 4
 
 
+def test_w4a4_validation(lib):
+    q = lib.moe_mxfp4_quantize
+    assert q(None, 4, 64, FAKE_ALIGNED, FAKE, None) == ERR_NULL
+    assert q(FAKE_ALIGNED, 4, 48, FAKE_ALIGNED, FAKE, None) == ERR_SHAPE
+    assert q(FAKE_ALIGNED, 0, 64, FAKE_ALIGNED, FAKE, None) == ERR_SHAPE
+    assert q(ctypes.c_void_p((1 << 30) + 2), 4, 64, FAKE_ALIGNED, FAKE, None) == ERR_SHAPE
+    g = lib.moe_gmm_w4a4
+    args = lambda **kw: [kw.get("packed", FAKE_ALIGNED), 8, kw.get("N", 512), kw.get("K", 256),
+                         kw.get("qc", FAKE_ALIGNED), FAKE, kw.get("rows", 128), None, FAKE, 128,
+                         FAKE, kw.get("dt", 0), kw.get("act", 0), None]
+    assert g(*args(packed=None)) == ERR_NULL
+    assert g(*args(qc=None)) == ERR_NULL
+    assert g(*args(K=200)) == ERR_SHAPE
+    assert g(*args(rows=100)) == ERR_SHAPE          # band input needs M rows
+    assert g(*args(act=3)) == ERR_FORMAT
+    assert g(*args(dt=5)) == ERR_FORMAT
+    assert g(*args(N=192, act=1)) == ERR_SHAPE
+    assert g(*args(qc=ctypes.c_void_p((1 << 30) + 8))) == ERR_SHAPE
+
+
 def test_gmm_act_validation(lib):
     f = lib.moe_gmm_act
     args = lambda **kw: [kw.get("packed", FAKE_ALIGNED), 0, kw.get("E", 8), kw.get("N", 512),

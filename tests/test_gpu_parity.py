@@ -302,6 +302,72 @@ def test_gmm_bf16_of_decoded_mxfp4_is_bitwise_mxfp4():
     assert torch.equal(y4, y16)
 
 
+# --------------------------------------------------------------- W4A4 ---
+
+def _special_rows():
+    # blocks that exercise every rounding tie, saturation, zero and -0
+    # blocks, bf16 subnormals and the largest finite magnitudes
+    from moe_grouped_gemm_route_amd.synth import f32_to_bf16_bits
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 0.3, -0.25, -5.0, 4.0, 0.0]
+    rows = np.zeros((6, 64), dtype=np.float32)
+    rows[0, :len(ties)] = ties
+    rows[1, :len(ties)] = np.array(ties) * 2.0 ** -20
+    rows[2, 1] = -0.0
+    rows[2, 33] = 3.0e38
+    rows[2, 34] = -1.0e38
+    rows[3, :8] = np.float32(2.0 ** -130) * np.arange(1, 9)      # bf16 subnormals
+    rows[4] = np.random.default_rng(300).standard_normal(64) * 1e-3
+    rows[5, 32:] = -np.abs(np.random.default_rng(301).standard_normal(32))
+    return f32_to_bf16_bits(rows)
+
+
+@pytest.mark.parametrize("which", ["special", "random"])
+def test_mxfp4_quantize_matches_oracle(which):
+    if which == "special":
+        bits = _special_rows()
+    else:
+        p = make_problem(T=300, k=1, E=1, K=512, N=64, seed=302)
+        bits = p["x"]
+    codes, scales = moe.mxfp4_quantize(to_dev(bits))
+    rc, rs = oracle.quantize_mxfp4_rows(bits)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def _w4a4_ref(p, w):
+    qc, qs = oracle.quantize_mxfp4_rows(p["x"])
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    return oracle.gmm_w4a4(qc, qs, ref_r["sorted_token"] if p["gather"] else None,
+                           ref_r["group_offsets"], w)
+
+
+def _run_w4a4(p, packed, out_dtype=moe.F32, act=moe.ACT_NONE):
+    r = moe.route_sort(to_dev(p["topk_ids"]), p["E"])
+    qc, qs = moe.mxfp4_quantize(to_dev(p["x"]))
+    return moe.moe_gmm_w4a4(packed, p["E"], p["N"], p["K"], qc, qs, r["group_offsets"], p["T"] * p["k"],
+                            row_index=r["sorted_token"] if p["gather"] else None,
+                            out_dtype=out_dtype, act=act)
+
+
+@pytest.mark.parametrize("case", ["banded", "gathered", "band_input"])
+def test_gmm_w4a4_full_oracle(case):
+    if case == "banded":
+        p = _banded_problem(310)
+    elif case == "gathered":
+        p = make_problem(T=96, k=4, E=8, K=512, N=512, seed=311, routing="zipf")
+    else:
+        p = _small(2)
+    w, packed = weights_for(p, "mxfp4")
+    ref = _w4a4_ref(p, w)
+    y = _run_w4a4(p, packed)
+    assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
+    yb = _run_w4a4(p, packed, out_dtype=moe.BF16)
+    assert torch.equal(yb, y.to(torch.bfloat16))
+    if p["N"] % 128 == 0:
+        ya = _run_w4a4(p, packed, act=moe.ACT_SILU_MUL)
+        assert rel_err(ya.cpu().numpy(), oracle.silu_mul(ref)) <= REL_TOL
+
+
 def test_gmm_rows_past_bands_untouched_and_canary():
     # dropped pairs leave rows [group_offsets[E], M) unwritten; nothing is
     # written past the end of y
@@ -382,6 +448,27 @@ def test_gmm_silu_mul_config_sampled(cfg):
     u = oracle.gmm_sampled(p["x"], ref_r["sorted_token"], ref_r["group_offsets"], w, rows, cols + H)
     ref = oracle.silu(g) * u
     got = y.cpu().numpy()[rows, cols].astype(np.float64)
+    assert rel_err(got, ref) <= REL_TOL
+
+
+@pytest.mark.slow
+def test_gmm_w4a4_config4_sampled():
+    p = make_config(4)
+    w, packed = weights_for(p, "mxfp4")
+    y = _run_w4a4(p, packed)
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    M = p["T"] * p["k"]
+    rows, cols = _sample(M, p["N"], 2000, 460)
+    # only the token rows the samples read are quantized by the oracle
+    toks = np.unique(ref_r["sorted_token"][rows])
+    qc, qs = oracle.quantize_mxfp4_rows(p["x"][toks])
+    xq = np.zeros((p["T"], p["K"]))
+    xq[toks] = oracle.dequantize_mxfp4_rows(qc, qs)
+    ref = np.array([float(np.dot(xq[ref_r["sorted_token"][r]],
+                                 oracle.dense_weights(w, int(np.searchsorted(ref_r["group_offsets"], r,
+                                                                              side="right") - 1))[c]))
+                    for r, c in zip(rows[:200], cols[:200])])
+    got = y.cpu().numpy()[rows[:200], cols[:200]].astype(np.float64)
     assert rel_err(got, ref) <= REL_TOL
 
 
