@@ -16,7 +16,9 @@ activation fused (bf16 [384, 2048]) -> w2 (K = 2048, N = 4096, f32) ->
 top-k combine.  The bf16_w13_decode and bf16_w2_decode workloads time the
 bf16-weight comparison arm on the decoded weights of configs 2 and 3 (the
 same values, four times the bytes) next to the MXFP4 kernel on the same
-inputs, and report the MXFP4 speedup.
+inputs, and report the MXFP4 speedup.  The w4a4_w13_prefill workload runs
+the 4,096-token w13 prefill W4A4: the activations are quantized to MXFP4
+inside the step and the matmul runs on the scaled FP4 matrix instructions.
 
 One JSON line is printed.  value is the whole step's throughput in the
 algorithmic bytes of the matmul (codes + scales of the experts that received
@@ -41,10 +43,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 MFMA, published
 
 WORKLOADS = {
     "tiny": 1, "w13_decode": 2, "w2_decode": 3, "w13_prefill": 4, "nvfp4_w13": 5,
-    "layer_decode": 0, "bf16_w13_decode": 2, "bf16_w2_decode": 3,
+    "layer_decode": 0, "bf16_w13_decode": 2, "bf16_w2_decode": 3, "w4a4_w13_prefill": 4,
 }
 KERNELS = {"auto": 0, "stream": 1, "tiled": 2}
 GMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_route_amd", "csrc", "gmm.hip")
@@ -262,6 +265,87 @@ def run_layer(args):
     print(json.dumps(out), flush=True)
 
 
+def run_w4a4(args):
+    """The W4A4 prefill workload: route-sort, MXFP4 activation quantization and
+    the grouped matmul on the scaled FP4 MFMA, over config 4's problem."""
+    import torch
+    import moe_grouped_gemm_route_amd as moe
+    from moe_grouped_gemm_route_amd.synth import make_config
+
+    p = make_config(4)
+    E, K, N, T, k = p["E"], p["K"], p["N"], p["T"], p["k"]
+    M = T * k
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    ids, x = d(p["topk_ids"]), d(p["x"])
+    codes = d(p["codes"])
+    packed = moe.mxfp4_encode(codes, d(p["scales"]), None, moe.MXFP4)
+    del codes
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    ev = []
+
+    def step(timed):
+        r = moe.route_sort(ids, E)
+        qc, qs = moe.mxfp4_quantize(x)
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        moe.moe_gmm_w4a4(packed, E, N, K, qc, qs, r["group_offsets"], M, row_index=r["sorted_token"], out=y)
+        if timed:
+            e1.record()
+            ev.append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gmm_ms = [a.elapsed_time(b) for a, b in ev]
+    gmm_s = float(np.mean(gmm_ms)) / 1e3
+    flops = 2.0 * M * K * N
+    counts = np.bincount(p["topk_ids"].reshape(-1), minlength=E)
+    active = int(np.count_nonzero(counts))
+    nbytes = active * N * K * (0.5 + 1.0 / 32) + T * (K // 2 + K // 32)
+    achieved = nbytes / gmm_s / 1e9
+    step_s = wall / args.steps
+    out = {
+        "metric": "moe_gmm TFLOP/s and HBM GB/s (% roofline), w13/w2, 256 experts top-6",
+        "value": round(flops / step_s / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4",
+        "data": "synthetic",
+        "config": {"workload": "w4a4_w13_prefill", "tokens": T, "top_k": k, "experts": E, "K": K,
+                   "N": N, "routed_rows": M, "weights": "mxfp4", "activations": "mxfp4 (quantized in the step)",
+                   "output": "f32", "step": "route_sort + mxfp4_quantize + moe_gmm_w4a4"},
+        "gmm_us": round(gmm_s * 1e6, 2),
+        "gmm_us_median": round(float(np.median(gmm_ms)) * 1e3, 2),
+        "gmm_us_min": round(float(np.min(gmm_ms)) * 1e3, 2),
+        "gmm_tflops": round(flops / gmm_s / 1e12, 2),
+        "active_experts": active,
+        "algorithmic_bytes": int(nbytes),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "fp4_mfma_frac": round(flops / gmm_s / 1e12 / FP4_PEAK_TFLOPS, 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +367,9 @@ def main():
 
     if args.workload == "layer_decode" and not args.copy_calibration:
         run_layer(args)
+        return
+    if args.workload == "w4a4_w13_prefill" and not args.copy_calibration:
+        run_w4a4(args)
         return
 
     import torch
