@@ -801,8 +801,13 @@ __global__ __launch_bounds__(256, 2) void gmm_w4a4_kernel(const uint8_t* __restr
       svo = (uint32_t)(src * (K / 32));
     }
   }
-  const __amdgpu_buffer_rsrc_t qcr = buffer_rsrc(qcodes, (uint32_t)((int64_t)x_rows * (K / 2)));
-  const __amdgpu_buffer_rsrc_t qsr = buffer_rsrc(qscales, (uint32_t)((int64_t)x_rows * (K / 32)));
+  // The sizes go through readfirstlane: K / 32 also feeds the divergent svo
+  // above, and the compiler would otherwise build the descriptor in vector
+  // registers and wrap every load through it in a waterfall loop.
+  const __amdgpu_buffer_rsrc_t qcr =
+      buffer_rsrc(qcodes, (uint32_t)__builtin_amdgcn_readfirstlane((int)((int64_t)x_rows * (K / 2))));
+  const __amdgpu_buffer_rsrc_t qsr =
+      buffer_rsrc(qscales, (uint32_t)__builtin_amdgcn_readfirstlane((int)((int64_t)x_rows * (K / 32))));
   const int64_t et = (int64_t)tile.e * L.NT + (wave_active ? (n0 >> 4) : 0);
   const __amdgpu_buffer_rsrc_t cr =
       buffer_rsrc(packed + ((et * L.KC) << 10), wave_active ? (uint32_t)(span * KC) << 10 : 0u);
