@@ -338,7 +338,7 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
 }
 
 template <int NS, int D, int MS, int FMT, bool OBF16, int ACT>
-__global__ __launch_bounds__(256, 3) void gmm_stream_kernel(const uint8_t* __restrict__ packed, Layout L,
+__global__ __launch_bounds__(256, NS > 4 ? 2 : 3) void gmm_stream_kernel(const uint8_t* __restrict__ packed, Layout L,
                                                          const uint16_t* __restrict__ x,
                                                          uint32_t x_bytes,
                                                          const int32_t* __restrict__ row_index,
@@ -890,11 +890,24 @@ static void launch_stream(const uint8_t* packed, const Layout& L, const uint16_t
   // bf16 weights (FMT 2) carry four times the bytes per column, so their
   // waves own two subtiles (32 columns) to keep the same register budget
   constexpr int NS = FMT == 2 ? 2 : 4, D = 2, MS = 2, BM = 16 * MS;
-  // a workgroup covers 4 * 64 output columns, or 4 * 32 activation columns
   const int64_t cols = ACT == 1 ? L.N / 2 : L.N;
-  const int NB = (int)((cols + (ACT == 1 ? 128 : 64 * NS) - 1) / (ACT == 1 ? 128 : 64 * NS));
   const int64_t em = E < M ? E : M;
   const int64_t tiles = ((M + BM - 1) / BM + em + 7) / 8 * 8;   // whole rounds of 8 tiles
+  // With a mean band of 4 rows or more the activation loads (one 16-row
+  // subtile of 16-byte loads per wave and chunk, whatever the weight count)
+  // fetch real rows and cost as much load issue as the codes: eight
+  // subtiles per wave (two waves per SIMD) halve them per weight byte.
+  // Thinner bands keep four subtiles and three waves per SIMD.
+  if constexpr (ACT == 0 && FMT == 0) {
+    if (M >= 4 * (int64_t)E && L.N % 128 == 0) {
+      const int NB = (int)((cols + 512 - 1) / 512);
+      hipLaunchKernelGGL((gmm_stream_kernel<8, D, MS, FMT, OBF16, ACT>), dim3((unsigned)(tiles * NB)),
+                         dim3(256), 0, stream, packed, L, x, x_bytes, row_index, goff, E, y, NB);
+      return;
+    }
+  }
+  // a workgroup covers 4 * 64 output columns, or 4 * 32 activation columns
+  const int NB = (int)((cols + (ACT == 1 ? 128 : 64 * NS) - 1) / (ACT == 1 ? 128 : 64 * NS));
   hipLaunchKernelGGL((gmm_stream_kernel<NS, D, MS, FMT, OBF16, ACT>), dim3((unsigned)(tiles * NB)),
                      dim3(256), 0, stream, packed, L, x, x_bytes, row_index, goff, E, y, NB);
 }
