@@ -265,6 +265,21 @@ def run_layer(args):
     print(json.dumps(out), flush=True)
 
 
+def recorded_traffic(workload):
+    """HBM bytes per launch of the workload's matmul kernel from the committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, calibrated on a copy kernel),
+    or None when there is none or the kernel source has changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        entry = json.load(open(TRAFFIC_FILE)).get(workload, {})
+    except (OSError, ValueError):
+        return None
+    if entry.get("gmm_source_sha256_16") != gmm_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
 def run_w4a4(args):
     """The W4A4 prefill workload: route-sort, MXFP4 activation quantization and
     the grouped matmul on the scaled FP4 MFMA, over config 4's problem."""
@@ -340,7 +355,7 @@ def run_w4a4(args):
         "active_experts": active,
         "algorithmic_bytes": int(nbytes),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(args.workload),
                      "fp4_mfma_frac": round(flops / gmm_s / 1e12 / FP4_PEAK_TFLOPS, 4)},
     }
     print(json.dumps(out), flush=True)
@@ -487,16 +502,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
         value, unit = nbytes / step_s / 1e9, "GB/s"
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            tf = json.load(open(TRAFFIC_FILE))
-            entry = tf.get(args.workload, {})
-            if entry.get("gmm_source_sha256_16") == gmm_source_hash():
-                traffic = entry.get("bytes_per_launch")
-        except Exception:
-            traffic = None
-    roof["traffic"] = traffic
+    roof["traffic"] = recorded_traffic(args.workload)
 
     out = {
         "metric": "moe_gmm TFLOP/s and HBM GB/s (% roofline), w13/w2, 256 experts top-6",
