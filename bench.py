@@ -530,6 +530,9 @@ def main():
         "gmm_gbs": round(nbytes / gmm_avg_s / 1e9, 1),
         "active_experts": active,
         "algorithmic_bytes": int(nbytes),
+        # + the output written and the index arrays read (band offsets, row index)
+        "algorithmic_bytes_all": int(nbytes + M * N * (2 if odt == moe.BF16 else 4)
+                                     + 4 * (E + 1) + (4 * M if p["gather"] else 0)),
         "roofline": roof,
     }
     if mx_ms is not None:

@@ -105,6 +105,10 @@ SMALL = [
     dict(T=37, k=3, E=5, K=384, N=192, routing="uniform", x_rows=111),
     dict(T=300, k=1, E=1, K=128, N=64, routing="uniform"),
     dict(T=1, k=1, E=4, K=128, N=256, routing="uniform"),
+    # mean band >= 4 rows with N a multiple of 128: the stream kernel's
+    # eight-subtile waves, with the last workgroup's waves partly past N
+    dict(T=160, k=4, E=12, K=512, N=384, routing="zipf", empty=(5,)),
+    dict(T=96, k=2, E=16, K=256, N=640, routing="uniform"),
 ]
 
 
@@ -156,9 +160,9 @@ def test_gmm_kernels_agree_bitwise_and_bf16_output(case):
 BANDS = [1, 15, 16, 17, 31, 32, 33, 48, 0, 64, 80, 96, 112, 127, 128, 129, 200, 5]
 
 
-def _banded_problem(seed, fmt_scales=(-6, -2)):
+def _banded_problem(seed, fmt_scales=(-6, -2), N=320):
     E = len(BANDS)
-    p = make_problem(T=sum(BANDS), k=1, E=E, K=256, N=320, seed=seed, exp_range=fmt_scales)
+    p = make_problem(T=sum(BANDS), k=1, E=E, K=256, N=N, seed=seed, exp_range=fmt_scales)
     rng = np.random.default_rng(seed + 1)
     ids = np.repeat(np.arange(E, dtype=np.int32), BANDS)
     rng.shuffle(ids)
@@ -166,9 +170,10 @@ def _banded_problem(seed, fmt_scales=(-6, -2)):
     return p
 
 
-@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
-def test_gmm_every_band_shape(fmt):
-    p = _banded_problem(260)
+@pytest.mark.parametrize("fmt,N", [("mxfp4", 320), ("nvfp4", 320), ("mxfp4", 384)])
+def test_gmm_every_band_shape(fmt, N):
+    # N = 384 sends the MXFP4 stream walk through its eight-subtile waves
+    p = _banded_problem(260, N=N)
     w, packed = weights_for(p, fmt)
     ref_r = oracle.route_sort(p["topk_ids"], p["E"])
     assert np.array_equal(np.diff(ref_r["group_offsets"]), BANDS)
