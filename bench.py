@@ -13,10 +13,10 @@ The default workload is the gate/up (w13) decode: 64 tokens, hidden 4096,
 MXFP4, bf16 output.  The layer_decode workload runs one whole routed-expert
 layer on the same tokens: route-sort -> w13 with the SiLU-gated gate/up
 activation fused (bf16 [384, 2048]) -> w2 (K = 2048, N = 4096, f32) ->
-top-k combine.  The bf16_w13_decode and bf16_w2_decode workloads time the
-bf16-weight comparison arm on the decoded weights of configs 2 and 3 (the
-same values, four times the bytes) next to the MXFP4 kernel on the same
-inputs, and report the MXFP4 speedup.  The w4a4_w13_prefill workload runs
+top-k combine.  The bf16_w13_decode, bf16_w2_decode and bf16_w13_prefill
+workloads time the bf16-weight comparison arm on the decoded weights of
+configs 2, 3 and 4 (the same values, four times the bytes) next to the MXFP4
+kernel on the same inputs, and report the MXFP4 speedup.  The w4a4_w13_prefill workload runs
 the 4,096-token w13 prefill W4A4: the activations are quantized to MXFP4
 inside the step and the matmul runs on the scaled FP4 matrix instructions.
 
@@ -47,7 +47,8 @@ FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 MFMA, published
 
 WORKLOADS = {
     "tiny": 1, "w13_decode": 2, "w2_decode": 3, "w13_prefill": 4, "nvfp4_w13": 5,
-    "layer_decode": 0, "bf16_w13_decode": 2, "bf16_w2_decode": 3, "w4a4_w13_prefill": 4,
+    "layer_decode": 0, "bf16_w13_decode": 2, "bf16_w2_decode": 3, "bf16_w13_prefill": 4,
+    "w4a4_w13_prefill": 4,
 }
 KERNELS = {"auto": 0, "stream": 1, "tiled": 2}
 GMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_route_amd", "csrc", "gmm.hip")
@@ -491,7 +492,9 @@ def main():
     nbytes, active = algorithmic_bytes(p, fmt)
     flops = 2.0 * M * K * N
     step_s = wall / args.steps
-    prefill = cfg == 4
+    # the roof is whichever bound takes longer at peak: the matrix unit for
+    # MXFP4 prefill, HBM for decode and for bf16 weights at prefill
+    prefill = flops / (BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9)
     if prefill:
         achieved = flops / gmm_avg_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,

@@ -138,7 +138,7 @@ int mxfp4_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
  * weights   [E, N, K] bf16 bit patterns, K contiguous, 16-byte aligned.
  * packed    out, moe_packed_weight_bytes(MOE_W_BF16, E, N, K) = E*N*K*2
  *           bytes, 256-aligned.
- * Limits as mxfp4_encode, and K < 2^26.  (mxfp4_encode rejects MOE_W_BF16
+ * Limits as mxfp4_encode, and K < 2^25.  (mxfp4_encode rejects MOE_W_BF16
  * with MOE_ERR_FORMAT.)
  */
 int moe_bf16_encode(const uint16_t* weights, int32_t E, int32_t N, int32_t K, void* packed,
@@ -178,9 +178,8 @@ int moe_gmm(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
 
 /* moe_gmm_ex - moe_gmm with an explicit kernel configuration
  * (moe_gmm_kernel_t).  Every configuration computes the same sums in the same
- * order, so all of them return bitwise identical y.  Weights in MOE_W_BF16
- * run on the weight-streaming kernel only (MOE_GMM_TILED returns
- * MOE_ERR_UNSUPPORTED). */
+ * order, so all of them return bitwise identical y; this holds for
+ * MOE_W_BF16 weights too. */
 int moe_gmm_ex(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
                const uint16_t* x, int32_t x_rows, const int32_t* row_index,
                const int32_t* group_offsets, int32_t M, void* y, int y_dtype,

@@ -22,9 +22,9 @@ int check_weight_shape(int fmt, int32_t E, int32_t N, int32_t K) {
   if (E < 1 || N < 1 || K < 1) return MOE_ERR_SHAPE;
   if (K % 128 != 0 || N % 64 != 0) return MOE_ERR_SHAPE;
   if ((int64_t)E * N * (K / 2) >= kMaxCodeBytes) return MOE_ERR_SHAPE;
-  // bf16 weights: a wave's two 4 KiB-per-chunk subtiles are addressed with
-  // 32-bit offsets
-  if (fmt == MOE_W_BF16 && (int64_t)2 * (K / 128) * 4096 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
+  // bf16 weights: a wave's (up to four) 4 KiB-per-chunk subtiles are
+  // addressed with 32-bit offsets
+  if (fmt == MOE_W_BF16 && (int64_t)4 * (K / 128) * 4096 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
@@ -100,11 +100,8 @@ int moe_gmm_act(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, co
   // activation rows are addressed with 32-bit byte offsets
   if ((int64_t)x_rows * K * 2 >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
   if (((uintptr_t)packed & 255) || ((uintptr_t)x & 15)) return MOE_ERR_SHAPE;
-  if (fmt == MOE_W_BF16) {
-    // the bf16 comparison arm: weight-streaming kernel, plain output
-    if (kernel == MOE_GMM_TILED || act != MOE_ACT_NONE) return MOE_ERR_UNSUPPORTED;
-    kernel = MOE_GMM_STREAM;
-  }
+  // the bf16 comparison arm has no fused activation
+  if (fmt == MOE_W_BF16 && act != MOE_ACT_NONE) return MOE_ERR_UNSUPPORTED;
   if (act == MOE_ACT_SILU_MUL) {
     // gate and up halves of 64-column multiples; one wave's code range spans
     // both halves of an expert and is addressed with 32-bit offsets

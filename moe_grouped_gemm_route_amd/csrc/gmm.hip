@@ -502,6 +502,93 @@ __device__ __forceinline__ void tiled_prologue(std::index_sequence<Is...>, u32x4
   ((ar[Is] = lds_read16<((int)Is % NSUB) * 16 * TL_ROW_BYTES + BUF * TL_BUF_BYTES>(va[Is / NSUB])), ...);
 }
 
+// bf16 weights (FMT 2): the weight words of a step are the MFMA B operands
+// themselves, four times the bytes of the codes, so they stream one step at
+// a time: bw[s] holds step s of the current chunk, and once the last row
+// subtile of step s has issued its MFMAs, bw[s] is refilled with step s of
+// the next chunk.  One chunk of weights stays in flight with 64 registers.
+template <int NSUB, int P, int BUF, int ACT, int F>
+__device__ __forceinline__ void tiled_fragment_bf16(u32x4_t (&ar)[P], const uint32_t (&va)[4],
+                                                    u32x4_t (&bw)[4][TL_NS], __amdgpu_buffer_rsrc_t cr,
+                                                    uint32_t c_voff, int KC, int h16, int kn,
+                                                    f32x4_t (&acc)[TL_MS][TL_NS]) {
+  constexpr int FT = 4 * NSUB;
+  constexpr int s = F / NSUB, ms = F % NSUB;
+  constexpr int newest = (F + P - 2 < FT - 1) ? F + P - 2 : FT - 1;
+  lds_read_wait<newest - F>(ar[F % P]);
+#pragma unroll
+  for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = mfma(as_bf16x8(ar[F % P]), as_bf16x8(bw[s][ns]), acc[ms][ns]);
+  constexpr int NF = F + P - 1;
+  if constexpr (NF < FT)
+    ar[NF % P] = lds_read16<(NF % NSUB) * 16 * TL_ROW_BYTES + BUF * TL_BUF_BYTES>(va[NF / NSUB]);
+  if constexpr (ms == NSUB - 1) {
+#pragma unroll
+    for (int ns = 0; ns < TL_NS; ++ns) {
+      const int sub = col_sub<ACT>(ns, h16);
+      bw[s][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, ((sub * KC + kn) << 12) + s * 1024, BUF_NT);
+    }
+  }
+}
+
+template <int NSUB, int P, int BUF, int ACT, size_t... Fs>
+__device__ __forceinline__ void tiled_chunk_bf16(std::index_sequence<Fs...>, u32x4_t (&ar)[P],
+                                                 const uint32_t (&va)[4], u32x4_t (&bw)[4][TL_NS],
+                                                 __amdgpu_buffer_rsrc_t cr, uint32_t c_voff, int KC, int h16,
+                                                 int kn, f32x4_t (&acc)[TL_MS][TL_NS]) {
+  (tiled_fragment_bf16<NSUB, P, BUF, ACT, (int)Fs>(ar, va, bw, cr, c_voff, KC, h16, kn, acc), ...);
+}
+
+// The K walk with bf16 weights.  Per chunk a wave issues its share of the
+// next activation chunk (LOADS direct-to-LDS loads), then, step by step, the
+// next chunk's weights (4 * NS loads); the wait before the barrier leaves
+// only those weight loads outstanding.
+template <int NSUB, int ACT>
+__device__ __forceinline__ void tiled_k_walk_bf16(uint8_t* s_a, __amdgpu_buffer_rsrc_t xr,
+                                                  const uint32_t (&avo)[TL_LOADS], __amdgpu_buffer_rsrc_t cr,
+                                                  int KC, int h16, int wave, const uint32_t (&va)[4],
+                                                  f32x4_t (&acc)[TL_MS][TL_NS]) {
+  constexpr int P = TL_PIPE;
+  constexpr int FT = 4 * NSUB;
+  constexpr int PRO = (P - 1 < FT) ? P - 1 : FT;
+  const int lane = threadIdx.x & 63;
+  const uint32_t c_voff = lane * 16;
+  u32x4_t bw[4][TL_NS];
+  auto stage = [&](int kc) {
+    uint8_t* buf = s_a + (kc & 1) * TL_BUF_BYTES + wave * TL_LOADS * 1024;
+#pragma unroll
+    for (int j = 0; j < TL_LOADS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(buf + j * 1024), 16, avo[j], kc * 256, 0, 0);
+  };
+  auto chunk = [&](auto bc, int kc) {
+    constexpr int d = decltype(bc)::value;   // kc & 1: LDS buffer
+    const int kn = min(kc + 1, KC - 1);
+    stage(kn);
+    __builtin_amdgcn_sched_barrier(0);       // the activation loads go first
+    u32x4_t ar[P];
+    tiled_prologue<NSUB, P, d>(std::make_index_sequence<PRO>{}, ar, va);
+    tiled_chunk_bf16<NSUB, P, d, ACT>(std::make_index_sequence<FT>{}, ar, va, bw, cr, c_voff, KC, h16, kn, acc);
+    vm_wait_barrier<4 * TL_NS>();
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  stage(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int ns = 0; ns < TL_NS; ++ns)
+      bw[s][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, ((col_sub<ACT>(ns, h16) * KC) << 12) + s * 1024,
+                                                        BUF_NT);
+  vm_wait_barrier<0>();
+  int k0 = 0;
+  for (; k0 + 2 <= KC; k0 += 2) {
+    chunk(B0{}, k0);
+    chunk(B1{}, k0 + 1);
+  }
+  if (k0 < KC) chunk(B0{}, k0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>());
+}
+
 // The K walk of one wave for a tile with NSUB valid 16-row subtiles.
 template <int NSUB, int FMT, int ACT>
 __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_t xr,
@@ -609,8 +696,9 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
   }
   const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(x, x_bytes);
   const int64_t et = (int64_t)tile.e * L.NT + (wave_active ? (n0 >> 4) : 0);
+  constexpr int CSH = FMT == 2 ? 12 : 10;   // log2 of a chunk's bytes
   const __amdgpu_buffer_rsrc_t cr =
-      buffer_rsrc(packed + ((et * L.KC) << 10), wave_active ? (uint32_t)(span * KC) << 10 : 0u);
+      buffer_rsrc(packed + ((et * L.KC) << CSH), wave_active ? (uint32_t)(span * KC) << CSH : 0u);
   const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(packed + L.scales_off + et * L.groups * 256,
                                                 wave_active ? (uint32_t)(span * groups) * 256 : 0u);
   // LDS address of this lane's fragment row for step s: row r of the
@@ -626,7 +714,18 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  switch (nsub) {
+  if constexpr (FMT == 2) {
+    switch (nsub) {
+      case 1: tiled_k_walk_bf16<1, ACT>(s_a, xr, avo, cr, KC, h16, wave, va, acc); break;
+      case 2: tiled_k_walk_bf16<2, ACT>(s_a, xr, avo, cr, KC, h16, wave, va, acc); break;
+      case 3: tiled_k_walk_bf16<3, ACT>(s_a, xr, avo, cr, KC, h16, wave, va, acc); break;
+      case 4: tiled_k_walk_bf16<4, ACT>(s_a, xr, avo, cr, KC, h16, wave, va, acc); break;
+      case 5: tiled_k_walk_bf16<5, ACT>(s_a, xr, avo, cr, KC, h16, wave, va, acc); break;
+      case 6: tiled_k_walk_bf16<6, ACT>(s_a, xr, avo, cr, KC, h16, wave, va, acc); break;
+      case 7: tiled_k_walk_bf16<7, ACT>(s_a, xr, avo, cr, KC, h16, wave, va, acc); break;
+      default: tiled_k_walk_bf16<8, ACT>(s_a, xr, avo, cr, KC, h16, wave, va, acc); break;
+    }
+  } else switch (nsub) {
     case 1: tiled_k_walk<1, FMT, ACT>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc); break;
     case 2: tiled_k_walk<2, FMT, ACT>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc); break;
     case 3: tiled_k_walk<3, FMT, ACT>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc); break;
@@ -930,13 +1029,8 @@ static void launch_gmm_t(const uint8_t* packed, const Layout& L, const uint16_t*
                          const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
                          void* y, int kernel, hipStream_t stream) {
   const uint32_t x_bytes = (uint32_t)((int64_t)x_rows * L.K * 2);
-  if constexpr (FMT == 2) {
-    // the bf16 comparison arm has the weight-streaming kernel only
-    launch_stream<FMT, OBF16, ACT>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream);
-  } else {
-    if (kernel == 1) launch_stream<FMT, OBF16, ACT>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream);
-    else launch_tiled<FMT, OBF16, ACT>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream);
-  }
+  if (kernel == 1) launch_stream<FMT, OBF16, ACT>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream);
+  else launch_tiled<FMT, OBF16, ACT>(packed, L, x, x_bytes, row_index, goff, E, M, y, stream);
 }
 
 template <int FMT, bool OBF16>

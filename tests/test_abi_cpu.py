@@ -108,8 +108,12 @@ def test_bf16_arm_validation(lib):
     assert lib.moe_bf16_encode(None, 8, 512, 256, FAKE_ALIGNED, None) == ERR_NULL
     assert lib.moe_bf16_encode(FAKE, 8, 512, 200, FAKE_ALIGNED, None) == ERR_SHAPE
     assert lib.moe_bf16_encode(FAKE, 8, 512, 256, ctypes.c_void_p((1 << 30) + 16), None) == ERR_SHAPE
+    # both kernels take bf16 weights, whose four-subtile chunk ranges must fit
+    # 32-bit offsets: K = 2^25 is one past the limit (rejected before launch)
+    assert lib.moe_packed_weight_bytes(2, 1, 64, 1 << 25) == 0
+    assert lib.moe_bf16_encode(FAKE, 1, 64, 1 << 25, FAKE_ALIGNED, None) == ERR_SHAPE
     ex = lib.moe_gmm_ex
-    assert ex(FAKE_ALIGNED, 2, 8, 512, 256, FAKE_ALIGNED, 128, None, FAKE, 128, FAKE, 0, 2, None) == 4
+    assert ex(FAKE_ALIGNED, 2, 1, 64, 1 << 25, FAKE_ALIGNED, 1, None, FAKE, 1, FAKE, 0, 2, None) == ERR_SHAPE
     act = lib.moe_gmm_act
     assert act(FAKE_ALIGNED, 2, 8, 512, 256, FAKE_ALIGNED, 128, None, FAKE, 128, FAKE, 0, 1, 0, None) == 4
 

@@ -283,27 +283,34 @@ def test_bf16_encode_round_trip():
     assert np.array_equal(back.cpu().numpy().view(np.uint16), wb)
 
 
-@pytest.mark.parametrize("case", [0, 1, 2])
+@pytest.mark.parametrize("case", [0, 1, 2, 3])
 def test_gmm_bf16_weights_full_oracle(case):
-    p = [_banded_problem(291), _small(1), _small(2)][case]
+    # both kernels on bf16 weights: every band shape (N = 320), a Zipf
+    # problem, band input, and N = 384 with a 512-deep K
+    p = [_banded_problem(291), _small(1), _small(2), _small(5)][case]
     wb = _bf16_weights(p["E"], p["N"], p["K"], 292 + case)
     packed = moe.bf16_encode(to_dev(wb))
     ref_r = oracle.route_sort(p["topk_ids"], p["E"])
     ref = oracle.gmm(p["x"], ref_r["sorted_token"] if p["gather"] else None, ref_r["group_offsets"],
                      {"fmt": "bf16", "weights": wb})
-    _, y = run_gpu(p, packed, "bf16")
-    assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
+    _, ys = run_gpu(p, packed, "bf16", kernel=moe.GMM_STREAM)
+    _, yt = run_gpu(p, packed, "bf16", kernel=moe.GMM_TILED)
+    assert rel_err(ys.cpu().numpy(), ref) <= REL_TOL
+    assert torch.equal(ys, yt)
+    _, yb = run_gpu(p, packed, "bf16", kernel=moe.GMM_TILED, out_dtype=moe.BF16)
+    assert torch.equal(yb, ys.to(torch.bfloat16))
 
 
-def test_gmm_bf16_of_decoded_mxfp4_is_bitwise_mxfp4():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_gmm_bf16_of_decoded_mxfp4_is_bitwise_mxfp4(kernel):
     # the bf16 arm on the decoded MXFP4 weights issues the same MFMAs on the
     # same operands: the two outputs are equal bit for bit
     p = _banded_problem(295)
     _, packed = weights_for(p, "mxfp4")
     dec = moe.debug_decode(packed, moe.MXFP4, p["E"], p["N"], p["K"])
     pb = moe.bf16_encode(dec)
-    _, y4 = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_STREAM)
-    _, y16 = run_gpu(p, pb, "bf16")
+    _, y4 = run_gpu(p, packed, "mxfp4", kernel=kernel)
+    _, y16 = run_gpu(p, pb, "bf16", kernel=kernel)
     assert torch.equal(y4, y16)
 
 
