@@ -42,6 +42,15 @@ def bf16_bits_to_f32(bits):
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
+def random_bf16_bits(rng, shape):
+    """Fast seeded bf16 bit patterns for very large activation matrices:
+    random sign and 7-bit mantissa, exponent uniform over 2^-4 .. 2^3 (so
+    magnitudes in [1/16, 16)).  Two uint16 draws from rng, in this order."""
+    a = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)
+    e = rng.integers(123, 131, size=shape, dtype=np.uint16)
+    return (a & np.uint16(0x807F)) | (e << np.uint16(7))
+
+
 def _topk_desc(keys, k):
     order = np.argsort(-keys, axis=1, kind="stable")
     return order[:, :k].astype(np.int32)

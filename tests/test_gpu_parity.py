@@ -15,7 +15,7 @@ import torch
 
 import moe_grouped_gemm_route_amd as moe
 import oracle
-from moe_grouped_gemm_route_amd.synth import make_config, make_problem
+from moe_grouped_gemm_route_amd.synth import make_config, make_problem, random_bf16_bits
 from gpu_util import (REL_TOL, bf16_bits_to_f64, bf16_ulp, rel_err, run_gpu, to_dev,
                       weights_for)
 
@@ -481,6 +481,31 @@ def test_gmm_w4a4_config4_sampled():
                                                                               side="right") - 1))[c]))
                     for r, c in zip(rows[:200], cols[:200])])
     got = y.cpu().numpy()[rows[:200], cols[:200]].astype(np.float64)
+    assert rel_err(got, ref) <= REL_TOL
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_gmm_largest_activation_matrix(kernel):
+    # the activations at the 32-bit byte-offset limit of the buffer loads:
+    # 262,143 token rows x 4096 bf16 = 2^31 - 8 KiB, every row its own
+    # expert band entry (top-1 of 8); the rows of the last tokens are checked
+    K, N, E = 4096, 256, 8
+    T = ((1 << 31) - 1) // (2 * K)
+    p = make_problem(T=1, k=1, E=E, K=K, N=N, seed=470)
+    rng = np.random.default_rng(471)
+    p["x"] = random_bf16_bits(rng, (T, K))
+    p["topk_ids"] = rng.integers(0, E, size=(T, 1)).astype(np.int32)
+    p["T"] = T
+    w, packed = weights_for(p, "mxfp4")
+    print("largest activation matrix: T=%d K=%d kernel=%d" % (T, K, kernel), flush=True)
+    r, y = run_gpu(p, packed, "mxfp4", kernel=kernel)
+    ref_r = oracle.route_sort(p["topk_ids"], E)
+    assert np.array_equal(r["group_offsets"].cpu().numpy(), ref_r["group_offsets"])
+    rows, cols = _sample(T, N, 1500, 472)
+    rows[8:24] = ref_r["pair_row"][T - 16:]                   # the last 16 tokens' rows
+    ref = oracle.gmm_sampled(p["x"], ref_r["sorted_token"], ref_r["group_offsets"], w, rows, cols)
+    got = y.cpu().numpy()[rows, cols].astype(np.float64)
     assert rel_err(got, ref) <= REL_TOL
 
 

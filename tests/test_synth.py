@@ -58,3 +58,13 @@ def test_code_nibbles_cover_all_16_values_uniformly():
     nib = np.concatenate([p["codes"] & 0xF, p["codes"] >> 4]).reshape(-1)
     cnt = np.bincount(nib, minlength=16)
     assert cnt.min() > 0.8 * cnt.mean()
+
+
+def test_random_bf16_bits_range_and_determinism():
+    from moe_grouped_gemm_route_amd.synth import random_bf16_bits, bf16_bits_to_f32
+    a = random_bf16_bits(np.random.default_rng(5), (300, 64))
+    b = random_bf16_bits(np.random.default_rng(5), (300, 64))
+    assert a.dtype == np.uint16 and np.array_equal(a, b)
+    v = np.abs(bf16_bits_to_f32(a))
+    assert v.min() >= 1.0 / 16 and v.max() < 16.0
+    assert 0.4 < np.mean(a >> 15) < 0.6                        # both signs
