@@ -118,7 +118,7 @@ size_t moe_packed_weight_bytes(int fmt, int32_t E, int32_t N, int32_t K);
  *                NVFP4: [E, N, K/16] E4M3FN bytes.
  * tensor_scale   NVFP4: [E] float, the per-expert scale; MXFP4: must be NULL.
  * packed         out, moe_packed_weight_bytes(fmt, E, N, K) bytes, 256-aligned.
- * Limits: K % 128 == 0, N % 64 == 0, E >= 1, E*N*K/2 < 2^40.
+ * Limits: K % 128 == 0, K < 2^26, N % 64 == 0, E >= 1, E*N*K/2 < 2^40.
  */
 int mxfp4_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
                  const float* tensor_scale, int32_t E, int32_t N, int32_t K,

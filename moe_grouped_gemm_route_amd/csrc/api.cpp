@@ -22,6 +22,9 @@ int check_weight_shape(int fmt, int32_t E, int32_t N, int32_t K) {
   if (E < 1 || N < 1 || K < 1) return MOE_ERR_SHAPE;
   if (K % 128 != 0 || N % 64 != 0) return MOE_ERR_SHAPE;
   if ((int64_t)E * N * (K / 2) >= kMaxCodeBytes) return MOE_ERR_SHAPE;
+  // a wave's code range (up to eight 16-column subtiles of 1 KiB per chunk)
+  // is addressed with 32-bit offsets
+  if ((int64_t)8 * (K / 128) * 1024 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
   // bf16 weights: a wave's (up to four) 4 KiB-per-chunk subtiles are
   // addressed with 32-bit offsets
   if (fmt == MOE_W_BF16 && (int64_t)4 * (K / 128) * 4096 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;

@@ -111,6 +111,9 @@ def test_bf16_arm_validation(lib):
     # both kernels take bf16 weights, whose four-subtile chunk ranges must fit
     # 32-bit offsets: K = 2^25 is one past the limit (rejected before launch)
     assert lib.moe_packed_weight_bytes(2, 1, 64, 1 << 25) == 0
+    # MXFP4 / NVFP4: up to eight subtiles of a wave, K < 2^26
+    assert lib.moe_packed_weight_bytes(0, 1, 128, (1 << 26) - 128) > 0
+    assert lib.moe_packed_weight_bytes(0, 1, 128, 1 << 26) == 0
     assert lib.moe_bf16_encode(FAKE, 1, 64, 1 << 25, FAKE_ALIGNED, None) == ERR_SHAPE
     ex = lib.moe_gmm_ex
     assert ex(FAKE_ALIGNED, 2, 1, 64, 1 << 25, FAKE_ALIGNED, 1, None, FAKE, 1, FAKE, 0, 2, None) == ERR_SHAPE
