@@ -13,7 +13,8 @@ The default workload is the gate/up (w13) decode: 64 tokens, hidden 4096,
 MXFP4, bf16 output.  The layer_decode workload runs one whole routed-expert
 layer on the same tokens: route-sort -> w13 with the SiLU-gated gate/up
 activation fused (bf16 [384, 2048]) -> w2 (K = 2048, N = 4096, f32) ->
-top-k combine.  The bf16_w13_decode, bf16_w2_decode and bf16_w13_prefill
+top-k combine; layer_prefill runs the same layer on config 4's 4,096
+tokens (both matmuls on the LDS-tiled kernel).  The bf16_w13_decode, bf16_w2_decode and bf16_w13_prefill
 workloads time the bf16-weight comparison arm on the decoded weights of
 configs 2, 3 and 4 (the same values, four times the bytes) next to the MXFP4
 kernel on the same inputs, and report the MXFP4 speedup.  The w4a4_w13_prefill workload runs
@@ -47,7 +48,7 @@ FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 MFMA, published
 
 WORKLOADS = {
     "tiny": 1, "w13_decode": 2, "w2_decode": 3, "w13_prefill": 4, "nvfp4_w13": 5,
-    "layer_decode": 0, "bf16_w13_decode": 2, "bf16_w2_decode": 3, "bf16_w13_prefill": 4,
+    "layer_decode": 0, "layer_prefill": 0, "bf16_w13_decode": 2, "bf16_w2_decode": 3, "bf16_w13_prefill": 4,
     "w4a4_w13_prefill": 4,
 }
 KERNELS = {"auto": 0, "stream": 1, "tiled": 2}
@@ -135,7 +136,7 @@ def cpu_model():
     return "unknown CPU"
 
 
-def layer_cpu_baseline(p, target_s=15.0):
+def layer_cpu_baseline(p, unit="GB/s", target_s=15.0):
     """The float64 oracle for one layer on the host: route-sort, then for as
     many active experts (in expert order) as fit in about target_s seconds,
     the w13 band matmul, the gate/up activation and the w2 band matmul."""
@@ -167,8 +168,10 @@ def layer_cpu_baseline(p, target_s=15.0):
         done += 1
     elapsed = time.perf_counter() - t0
     nbytes += (p["T"] * rows_done / (p["T"] * p["k"])) * p["K"] * 2 + rows_done * (p["N"] // 2) * 2
+    flops = 2.0 * rows_done * p["K"] * (p["N"] + p["N"] // 2)
+    rate = flops / elapsed / 1e12 if unit == "TFLOP/s" else nbytes / elapsed / 1e9
     return {
-        "value": round(nbytes / elapsed / 1e9, 6), "unit": "GB/s", "cores": int(threads),
+        "value": round(rate, 6), "unit": unit, "cores": int(threads),
         "kind": "oracle",
         "sample": "float64 numpy oracle on %s: route-sort of all %d pairs + w13, gate/up "
                   "activation and w2 of the first %d of %d active experts' bands (%d rows), %.1f s"
@@ -177,12 +180,12 @@ def layer_cpu_baseline(p, target_s=15.0):
 
 
 def run_layer(args):
-    """One routed-expert layer at decode (the layer_decode workload)."""
+    """One routed-expert layer (the layer_decode and layer_prefill workloads)."""
     import torch
     import moe_grouped_gemm_route_amd as moe
-    from moe_grouped_gemm_route_amd.synth import make_layer_decode
+    from moe_grouped_gemm_route_amd.synth import make_layer_decode, make_layer_prefill
 
-    p = make_layer_decode()
+    p = make_layer_prefill() if args.workload == "layer_prefill" else make_layer_decode()
     E, K, N, T, k = p["E"], p["K"], p["N"], p["T"], p["k"]
     M, H = T * k, N // 2
     dev = torch.device("cuda", 0)
@@ -235,11 +238,23 @@ def run_layer(args):
     b13 = active * N * K * (0.5 + 1.0 / 32) + T * K * 2
     b2 = active * K * H * (0.5 + 1.0 / 32) + M * H * 2
     step_s = wall / args.steps
-    achieved = (b13 + b2) / (t13 + t2) / 1e9
+    flops = 2.0 * M * K * (N + H)
+    # matrix-unit bound when its roof time is the longer one (prefill)
+    mfma_bound = flops / (BF16_PEAK_TFLOPS * 1e12) > (b13 + b2) / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        achieved = flops / (t13 + t2) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+        value, unit = flops / step_s / 1e12, "TFLOP/s"
+    else:
+        achieved = (b13 + b2) / (t13 + t2) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+        value, unit = (b13 + b2) / step_s / 1e9, "GB/s"
     out = {
         "metric": "moe_gmm TFLOP/s and HBM GB/s (% roofline), w13/w2, 256 experts top-6",
-        "value": round((b13 + b2) / step_s / 1e9, 2),
-        "unit": "GB/s",
+        "value": round(value, 2),
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -249,7 +264,7 @@ def run_layer(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "layer_decode", "tokens": T, "top_k": k, "experts": E,
+        "config": {"workload": args.workload, "tokens": T, "top_k": k, "experts": E,
                    "w13": [K, N], "w2": [H, K], "routed_rows": M, "weights": "mxfp4",
                    "activations": "bf16", "gate_up": "silu(gate) * up fused into the w13 epilogue",
                    "step": "route_sort + moe_gmm(w13, act) + moe_gmm(w2) + moe_combine"},
@@ -257,11 +272,11 @@ def run_layer(args):
         "w2_us": round(t2 * 1e6, 2),
         "active_experts": active,
         "algorithmic_bytes": int(b13 + b2),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "layer_tflops": round(flops / (t13 + t2) / 1e12, 2),
+        "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = layer_cpu_baseline(p)
+        out["cpu_baseline"] = layer_cpu_baseline(p, unit)
         out["gpu_over_cpu"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
 
@@ -381,7 +396,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    if args.workload == "layer_decode" and not args.copy_calibration:
+    if args.workload in ("layer_decode", "layer_prefill") and not args.copy_calibration:
         run_layer(args)
         return
     if args.workload == "w4a4_w13_prefill" and not args.copy_calibration:

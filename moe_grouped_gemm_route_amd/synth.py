@@ -145,10 +145,20 @@ def make_layer_decode():
     fused gate+up (w13) weights, plus down-projection (w2) weights of the
     expert intermediate size (K = 2048, N = 4096) drawn with seed 6 (only
     their codes and scales are taken from that draw)."""
-    p = dict(make_config(2))
+    return _layer(2, "layer_decode")
+
+
+def make_layer_prefill():
+    """One MoE layer at prefill: config 4's 4096 tokens, routing, router
+    weights and w13 weights, plus the same w2 weights as make_layer_decode."""
+    return _layer(4, "layer_prefill")
+
+
+def _layer(cfg, name):
+    p = dict(make_config(cfg))
     w2 = make_problem(T=8, k=6, E=p["E"], K=p["N"] // 2, N=p["K"], seed=6,
                       exp_range=CONFIGS[2]["exp_range"])
     p["w2_codes"], p["w2_scales"] = w2["codes"], w2["scales"]
-    p["name"] = "layer_decode"
+    p["name"] = name
     return p
 
