@@ -766,18 +766,22 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
 // the layout of the bf16 MFMA's.  One MFMA covers a whole chunk of a 16 x 16
 // tile.
 //
-// Same workgroup shape, schedule and waits as the tiled kernel: 4 waves,
-// 128 rows x 256 columns, the activation chunk staged in LDS by direct-to-LDS
-// loads and double-buffered, the weight codes and scale words one chunk
-// ahead.  A staged chunk holds the 128 rows' codes (64 bytes per row, rows
-// contiguous: 8 KiB) and their scale dwords (wave w loads rows 32w .. 32w+31
-// into its own 256-byte slot; lanes 32..63 read past the buffer and write
-// zeros into the slot's unused half).
+// Same workgroup shape as the tiled kernel: 4 waves, 128 rows x 256
+// columns, the activation chunk staged in LDS by direct-to-LDS loads.  With a
+// quarter of the matrix work per chunk the kernel is bound by its weight
+// stream, so three chunks are staged (LDS buffers for the activations, a
+// register ring for the weight codes and scale words) and two of them are in
+// flight while the third is computed.  A staged chunk holds the 128 rows'
+// codes (64 bytes per row, rows contiguous: 8 KiB) and their scale dwords
+// (wave w loads rows 32w .. 32w+31 into its own 256-byte slot; lanes 32..63
+// read past the buffer and write zeros into the slot's unused half).
 // ---------------------------------------------------------------------------
 constexpr int Q_CODE_BYTES = TL_BM * 64;                     // 8 KiB
 constexpr int Q_SCALE_BYTES = TL_WAVES * 256;
 constexpr int Q_STAGE_BYTES = Q_CODE_BYTES + Q_SCALE_BYTES;
 constexpr int Q_LOADS = Q_CODE_BYTES / 1024 / TL_WAVES;      // 1 KiB code loads per wave per chunk
+constexpr int Q_STAGES = 3;                                   // chunks staged: two in flight, one computed
+constexpr int Q_ISSUE = Q_LOADS + 1 + 2 * TL_NS;             // vector-memory instructions per chunk
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
@@ -797,17 +801,20 @@ __device__ __forceinline__ void w4a4_k_walk(uint8_t* s_q, __amdgpu_buffer_rsrc_t
   const int r = lane & 15;
   const int g = lane >> 4;
   const uint32_t c_voff = lane * 16, s_voff = lane * 4;
-  u32x4_t cs[2][TL_NS];
-  uint32_t ws[2][TL_NS];
-  auto stage = [&](int kc) {
-    uint8_t* buf = s_q + (kc & 1) * Q_STAGE_BYTES;
+  u32x4_t cs[Q_STAGES][TL_NS];
+  uint32_t ws[Q_STAGES][TL_NS];
+  // all loads of chunk kc into stage `slot`: the activation codes and scales
+  // (direct to LDS, shared by the four waves), then this wave's weight codes
+  // and scale words (registers); Q_ISSUE vector-memory instructions
+  auto issue = [&](auto sc, int kc) {
+    constexpr int slot = decltype(sc)::value;
+    uint8_t* buf = s_q + slot * Q_STAGE_BYTES;
 #pragma unroll
     for (int j = 0; j < Q_LOADS; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(qcr, (lds_ptr_t)(buf + (wave * Q_LOADS + j) * 1024), 16, cvo[j],
                                                kc * 64, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(qsr, (lds_ptr_t)(buf + Q_CODE_BYTES + wave * 256), 4, svo, kc * 4, 0, 0);
-  };
-  auto load_codes = [&](int slot, int kc) {
+    __builtin_amdgcn_sched_barrier(0);       // the activation loads go first
     const int rec = scale_record<0>(kc);
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) {
@@ -816,11 +823,12 @@ __device__ __forceinline__ void w4a4_k_walk(uint8_t* s_q, __amdgpu_buffer_rsrc_t
       ws[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (sub * groups + rec) * 256, 0);
     }
   };
-  auto chunk = [&](auto bc, int kc) {
-    constexpr int d = decltype(bc)::value;   // kc & 1: LDS buffer and code slot
-    stage(min(kc + 1, KC - 1));
-    __builtin_amdgcn_sched_barrier(0);       // the activation loads go first
-    load_codes(d ^ 1, min(kc + 1, KC - 1));
+  // Chunk kc (stage kc % 3) issues chunk kc + 2 into the stage chunk kc - 1
+  // used, computes, then waits until only those loads are outstanding: chunk
+  // kc + 1 has then landed for every wave when the barrier opens.
+  auto chunk = [&](auto sc, int kc) {
+    constexpr int d = decltype(sc)::value;
+    issue(std::integral_constant<int, (d + 2) % Q_STAGES>{}, min(kc + 2, KC - 1));
     const uint8_t* buf = s_q + d * Q_STAGE_BYTES;
     uint32_t sb[TL_NS];
 #pragma unroll
@@ -834,20 +842,23 @@ __device__ __forceinline__ void w4a4_k_walk(uint8_t* s_q, __amdgpu_buffer_rsrc_t
 #pragma unroll
       for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = mfma_fp4(a, sa, cs[d][ns], sb[ns], acc[ms][ns]);
     }
-    vm_wait_barrier<2 * TL_NS>();
+    vm_wait_barrier<Q_ISSUE>();
   };
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-  stage(0);
-  __builtin_amdgcn_sched_barrier(0);
-  load_codes(0, 0);
-  vm_wait_barrier<0>();
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  static_assert(Q_STAGES == 3, "the walk below is unrolled for three stages");
+  issue(S0{}, 0);
+  issue(S1{}, min(1, KC - 1));
+  vm_wait_barrier<Q_ISSUE>();
   int k0 = 0;
-  for (; k0 + 2 <= KC; k0 += 2) {
-    chunk(B0{}, k0);
-    chunk(B1{}, k0 + 1);
+  for (; k0 + 3 <= KC; k0 += 3) {
+    chunk(S0{}, k0);
+    chunk(S1{}, k0 + 1);
+    chunk(S2{}, k0 + 2);
   }
-  if (k0 < KC) chunk(B0{}, k0);
+  if (k0 < KC) chunk(S0{}, k0);
+  if (k0 + 1 < KC) chunk(S1{}, k0 + 1);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>());
 }
 
@@ -858,7 +869,7 @@ __global__ __launch_bounds__(256, 2) void gmm_w4a4_kernel(const uint8_t* __restr
                                                           const int32_t* __restrict__ row_index,
                                                           const int32_t* __restrict__ goff, int E,
                                                           void* __restrict__ y, int NB) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_q[2 * Q_STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_q[Q_STAGES * Q_STAGE_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
