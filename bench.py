@@ -14,7 +14,8 @@ MXFP4, bf16 output.  The layer_decode workload runs one whole routed-expert
 layer on the same tokens: route-sort -> w13 with the SiLU-gated gate/up
 activation fused (bf16 [384, 2048]) -> w2 (K = 2048, N = 4096, f32) ->
 top-k combine; layer_prefill runs the same layer on config 4's 4,096
-tokens (both matmuls on the LDS-tiled kernel).  The bf16_w13_decode, bf16_w2_decode and bf16_w13_prefill
+tokens (both matmuls on the LDS-tiled kernel), and w4a4_layer_prefill runs it
+W4A4 (x and the activation h quantized to MXFP4 inside the step).  The bf16_w13_decode, bf16_w2_decode and bf16_w13_prefill
 workloads time the bf16-weight comparison arm on the decoded weights of
 configs 2, 3 and 4 (the same values, four times the bytes) next to the MXFP4
 kernel on the same inputs, and report the MXFP4 speedup.  The w4a4_w13_prefill workload runs
@@ -48,7 +49,7 @@ FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 MFMA, published
 
 WORKLOADS = {
     "tiny": 1, "w13_decode": 2, "w2_decode": 3, "w13_prefill": 4, "nvfp4_w13": 5,
-    "layer_decode": 0, "layer_prefill": 0, "bf16_w13_decode": 2, "bf16_w2_decode": 3, "bf16_w13_prefill": 4,
+    "layer_decode": 0, "layer_prefill": 0, "w4a4_layer_prefill": 0, "bf16_w13_decode": 2, "bf16_w2_decode": 3, "bf16_w13_prefill": 4,
     "w4a4_w13_prefill": 4,
 }
 KERNELS = {"auto": 0, "stream": 1, "tiled": 2}
@@ -185,7 +186,9 @@ def run_layer(args):
     import moe_grouped_gemm_route_amd as moe
     from moe_grouped_gemm_route_amd.synth import make_layer_decode, make_layer_prefill
 
-    p = make_layer_prefill() if args.workload == "layer_prefill" else make_layer_decode()
+    prefill = args.workload in ("layer_prefill", "w4a4_layer_prefill")
+    w4a4 = args.workload == "w4a4_layer_prefill"
+    p = make_layer_prefill() if prefill else make_layer_decode()
     E, K, N, T, k = p["E"], p["K"], p["N"], p["T"], p["k"]
     M, H = T * k, N // 2
     dev = torch.device("cuda", 0)
@@ -208,17 +211,32 @@ def run_layer(args):
     ev = []
 
     def step(timed):
+        # events around each matmul kernel (the W4A4 quantizations fall between)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
         r = moe.route_sort(ids, E)
+        if w4a4:
+            qc, qs = moe.mxfp4_quantize(x)
+            if timed:
+                e[0].record()
+            moe.moe_gmm_w4a4(w13, E, N, K, qc, qs, r["group_offsets"], M, row_index=r["sorted_token"],
+                             out_dtype=moe.BF16, act=moe.ACT_SILU_MUL, out=h)
+            if timed:
+                e[1].record()
+            qc, qs = moe.mxfp4_quantize(h)
+            if timed:
+                e[2].record()
+            moe.moe_gmm_w4a4(w2, E, K, H, qc, qs, r["group_offsets"], M, out_dtype=moe.F32, out=y2)
+        else:
+            if timed:
+                e[0].record()
+            moe.moe_gmm(w13, moe.MXFP4, E, N, K, x, r["group_offsets"], M, row_index=r["sorted_token"],
+                        out_dtype=moe.BF16, act=moe.ACT_SILU_MUL, out=h)
+            if timed:
+                e[1].record()
+                e[2].record()
+            moe.moe_gmm(w2, moe.MXFP4, E, K, H, h, r["group_offsets"], M, out_dtype=moe.F32, out=y2)
         if timed:
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            e[0].record()
-        moe.moe_gmm(w13, moe.MXFP4, E, N, K, x, r["group_offsets"], M, row_index=r["sorted_token"],
-                    out_dtype=moe.BF16, act=moe.ACT_SILU_MUL, out=h)
-        if timed:
-            e[1].record()
-        moe.moe_gmm(w2, moe.MXFP4, E, K, H, h, r["group_offsets"], M, out_dtype=moe.F32, out=y2)
-        if timed:
-            e[2].record()
+            e[3].record()
             ev.append(e)
         return moe.moe_combine(y2, tw, r["pair_row"])
 
@@ -231,16 +249,21 @@ def run_layer(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    t13 = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) / 1e3
-    t2 = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) / 1e3
+    t13 = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / 1e3
+    t2 = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) / 1e3
     counts = np.bincount(p["topk_ids"].reshape(-1), minlength=E)
     active = int(np.count_nonzero(counts))
     b13 = active * N * K * (0.5 + 1.0 / 32) + T * K * 2
     b2 = active * K * H * (0.5 + 1.0 / 32) + M * H * 2
     step_s = wall / args.steps
     flops = 2.0 * M * K * (N + H)
-    # matrix-unit bound when its roof time is the longer one (prefill)
-    mfma_bound = flops / (BF16_PEAK_TFLOPS * 1e12) > (b13 + b2) / (HBM_PEAK_GBS * 1e9)
+    if w4a4:
+        # quantized activations: K/2 + K/32 bytes per row instead of 2K
+        b13 = active * N * K * (0.5 + 1.0 / 32) + T * (K // 2 + K // 32)
+        b2 = active * K * H * (0.5 + 1.0 / 32) + M * (H // 2 + H // 32)
+    # matrix-unit bound when its roof time is the longer one (bf16 prefill)
+    peak_flops = (FP4_PEAK_TFLOPS if w4a4 else BF16_PEAK_TFLOPS) * 1e12
+    mfma_bound = flops / peak_flops > (b13 + b2) / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:
         achieved = flops / (t13 + t2) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
@@ -251,6 +274,10 @@ def run_layer(args):
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
         value, unit = (b13 + b2) / step_s / 1e9, "GB/s"
+        if prefill:
+            value, unit = flops / step_s / 1e12, "TFLOP/s"
+    if w4a4:
+        roof["fp4_mfma_frac"] = round(flops / (t13 + t2) / peak_flops, 4)
     out = {
         "metric": "moe_gmm TFLOP/s and HBM GB/s (% roofline), w13/w2, 256 experts top-6",
         "value": round(value, 2),
@@ -262,12 +289,15 @@ def run_layer(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp4" if w4a4 else "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens": T, "top_k": k, "experts": E,
                    "w13": [K, N], "w2": [H, K], "routed_rows": M, "weights": "mxfp4",
-                   "activations": "bf16", "gate_up": "silu(gate) * up fused into the w13 epilogue",
-                   "step": "route_sort + moe_gmm(w13, act) + moe_gmm(w2) + moe_combine"},
+                   "activations": "mxfp4 (quantized in the step)" if w4a4 else "bf16",
+                   "gate_up": "silu(gate) * up fused into the w13 epilogue",
+                   "step": ("route_sort + mxfp4_quantize(x) + moe_gmm_w4a4(w13, act) + mxfp4_quantize(h) "
+                            "+ moe_gmm_w4a4(w2) + moe_combine") if w4a4 else
+                           "route_sort + moe_gmm(w13, act) + moe_gmm(w2) + moe_combine"},
         "w13_us": round(t13 * 1e6, 2),
         "w2_us": round(t2 * 1e6, 2),
         "active_experts": active,
@@ -275,7 +305,7 @@ def run_layer(args):
         "layer_tflops": round(flops / (t13 + t2) / 1e12, 2),
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not w4a4:
         out["cpu_baseline"] = layer_cpu_baseline(p, unit)
         out["gpu_over_cpu"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
@@ -396,7 +426,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    if args.workload in ("layer_decode", "layer_prefill") and not args.copy_calibration:
+    if args.workload in ("layer_decode", "layer_prefill", "w4a4_layer_prefill") and not args.copy_calibration:
         run_layer(args)
         return
     if args.workload == "w4a4_w13_prefill" and not args.copy_calibration:

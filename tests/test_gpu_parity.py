@@ -380,6 +380,39 @@ def test_gmm_w4a4_full_oracle(case):
         assert rel_err(ya.cpu().numpy(), oracle.silu_mul(ref)) <= REL_TOL
 
 
+def test_w4a4_layer_chain_small():
+    # the W4A4 layer: route -> quantize x -> w13 with the fused activation
+    # (bf16) -> quantize h -> w2 on the band-ordered activation (f32) ->
+    # combine, each stage against the oracle on the previous GPU stage's output
+    p = make_problem(T=80, k=3, E=8, K=256, N=512, seed=320, routing="zipf")
+    H, D = p["N"] // 2, p["K"]
+    rng = np.random.default_rng(321)
+    w2c = rng.integers(0, 256, size=(p["E"], D, H // 2), dtype=np.uint8)
+    w2s = (rng.integers(-6, -1, size=(p["E"], D, H // 32)) + 127).astype(np.uint8)
+    w13, p13 = weights_for(p, "mxfp4")
+    pk2 = moe.mxfp4_encode(to_dev(w2c), to_dev(w2s), None, moe.MXFP4)
+    M = p["T"] * p["k"]
+    r = moe.route_sort(to_dev(p["topk_ids"]), p["E"])
+    qc, qs = moe.mxfp4_quantize(to_dev(p["x"]))
+    h = moe.moe_gmm_w4a4(p13, p["E"], p["N"], p["K"], qc, qs, r["group_offsets"], M,
+                         row_index=r["sorted_token"], out_dtype=moe.BF16, act=moe.ACT_SILU_MUL)
+    qhc, qhs = moe.mxfp4_quantize(h)
+    y2 = moe.moe_gmm_w4a4(pk2, p["E"], D, H, qhc, qhs, r["group_offsets"], M)
+    out = moe.moe_combine(y2, to_dev(p["topk_weights"]), r["pair_row"])
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    ref_h = oracle.silu_mul(_w4a4_ref(p, w13))
+    got_h = h.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got_h - ref_h) <= bf16_ulp(ref_h))
+    h_bits = h.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref_qc, ref_qs = oracle.quantize_mxfp4_rows(h_bits)
+    assert np.array_equal(qhc.cpu().numpy(), ref_qc) and np.array_equal(qhs.cpu().numpy(), ref_qs)
+    ref_y2 = oracle.gmm_w4a4(ref_qc, ref_qs, None, ref_r["group_offsets"],
+                             {"fmt": "mxfp4", "codes": w2c, "scales": w2s})
+    assert rel_err(y2.cpu().numpy(), ref_y2) <= REL_TOL
+    ref_out = oracle.combine(y2.cpu().numpy(), p["topk_weights"], ref_r["pair_row"])
+    assert rel_err(out.cpu().numpy(), ref_out) <= REL_TOL
+
+
 def test_gmm_rows_past_bands_untouched_and_canary():
     # dropped pairs leave rows [group_offsets[E], M) unwritten; nothing is
     # written past the end of y
