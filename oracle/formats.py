@@ -17,7 +17,7 @@ Sources
   2^(k_max - 8) times a per-16 E4M3 block scale, with k_max shared by the
   fused gate/up pair of an expert.  Every nibble is unchanged.
 
-Readings where the pages are silent (each listed in the design notes):
+Readings where the pages are silent:
 * Two codes per byte, the even K index in the low nibble; codes are stored
   [.., N, K/2] with K contiguous (the checkpoint's [out, in] orientation).
 * E8M0 is the OCP MX scale byte: 2^(b - 127), 0xFF is NaN.
