@@ -210,6 +210,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
+// Byte offset of chunk idx (chunks of 1 << SH bytes) inside a buffer range.
+// The host checks that every range fits 32 bits; the shift is done unsigned
+// so offsets past 2^31 stay well defined.
+template <int SH>
+__device__ __forceinline__ int chunk_off(int idx) {
+  return (int)((uint32_t)idx << SH);
+}
+
 constexpr int BUF_NT = 2;                  // buffer-load cache policy: non-temporal
 constexpr uint32_t BUF_OOB = 0x7FFF0000u;  // a lane offset that reads zeros
 
@@ -261,9 +269,9 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           cring[slot][ns][s] =
-              __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, ((sub * KC + kc) << 12) + s * 1024, BUF_NT);
+              __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, chunk_off<12>(sub * KC + kc) + s * 1024, BUF_NT);
       } else {
-        cring[slot][ns][0] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, (sub * KC + kc) << 10, BUF_NT);
+        cring[slot][ns][0] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, chunk_off<10>(sub * KC + kc), BUF_NT);
         const int rec = FMT == 0 ? (kc >> 2) : (kc >> 1);
         sring[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (sub * groups + rec) * 256, 0);
       }
@@ -525,7 +533,7 @@ __device__ __forceinline__ void tiled_fragment_bf16(u32x4_t (&ar)[P], const uint
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) {
       const int sub = col_sub<ACT>(ns, h16);
-      bw[s][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, ((sub * KC + kn) << 12) + s * 1024, BUF_NT);
+      bw[s][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, chunk_off<12>(sub * KC + kn) + s * 1024, BUF_NT);
     }
   }
 }
@@ -577,7 +585,7 @@ __device__ __forceinline__ void tiled_k_walk_bf16(uint8_t* s_a, __amdgpu_buffer_
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns)
-      bw[s][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, ((col_sub<ACT>(ns, h16) * KC) << 12) + s * 1024,
+      bw[s][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, chunk_off<12>(col_sub<ACT>(ns, h16) * KC) + s * 1024,
                                                         BUF_NT);
   vm_wait_barrier<0>();
   int k0 = 0;
@@ -617,7 +625,7 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) {
       const int sub = col_sub<ACT>(ns, h16);
-      cs[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, (sub * KC + kc) << 10, BUF_NT);
+      cs[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, chunk_off<10>(sub * KC + kc), BUF_NT);
       ws[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (sub * groups + rec) * 256, 0);
     }
   };
@@ -819,7 +827,7 @@ __device__ __forceinline__ void w4a4_k_walk(uint8_t* s_q, __amdgpu_buffer_rsrc_t
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) {
       const int sub = col_sub<ACT>(ns, h16);
-      cs[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, (sub * KC + kc) << 10, BUF_NT);
+      cs[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, chunk_off<10>(sub * KC + kc), BUF_NT);
       ws[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (sub * groups + rec) * 256, 0);
     }
   };
