@@ -278,6 +278,7 @@ def run_layer(args):
             value, unit = flops / step_s / 1e12, "TFLOP/s"
     if w4a4:
         roof["fp4_mfma_frac"] = round(flops / (t13 + t2) / peak_flops, 4)
+    calib = mfma_calibration(roof["achieved"]) if mfma_bound else None
     out = {
         "metric": "moe_gmm TFLOP/s and HBM GB/s (% roofline), w13/w2, 256 experts top-6",
         "value": round(value, 2),
@@ -305,10 +306,49 @@ def run_layer(args):
         "layer_tflops": round(flops / (t13 + t2) / 1e12, 2),
         "roofline": roof,
     }
+    if calib is not None:
+        out["mfma_calibration"] = calib
     if not args.no_cpu_baseline and not w4a4:
         out["cpu_baseline"] = layer_cpu_baseline(p, unit)
         out["gpu_over_cpu"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
     print(json.dumps(out), flush=True)
+
+
+CALIB_BLOCKS, CALIB_ITERS = 512, 12800     # two workgroups per CU, about 25 ms per launch
+
+
+def mfma_calibration(achieved_tflops):
+    """The bf16 matrix-unit rate this part sustains with no memory traffic
+    (moe_calib_mfma_bf16: the tiled kernel's 128 x 64 wave tile of 16x16x32
+    MFMAs on register-resident N(0,1) activations and decoded MXFP4 weights),
+    the median of 3 launches after one warm-up, with the matmul's achieved
+    rate as a fraction of it.  Measured after the timed steps; the roofline
+    fraction stays the one against the published peak."""
+    import torch
+    import moe_grouped_gemm_route_amd as moe
+    from moe_grouped_gemm_route_amd.synth import make_problem
+
+    q = make_problem(T=2048, k=1, E=1, K=4096, N=1024, seed=41)
+    dev = torch.device("cuda", 0)
+    a = torch.from_numpy(q["x"].view(np.int16)).to(dev)
+    packed = moe.mxfp4_encode(torch.from_numpy(q["codes"]).to(dev), torch.from_numpy(q["scales"]).to(dev),
+                              None, moe.MXFP4)
+    b = moe.debug_decode(packed, moe.MXFP4, 1, 1024, 4096)
+    moe.calib_mfma_bf16(a, b, CALIB_BLOCKS, CALIB_ITERS)
+    ms = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        moe.calib_mfma_bf16(a, b, CALIB_BLOCKS, CALIB_ITERS)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    flops = CALIB_BLOCKS * 4.0 * CALIB_ITERS * 128 * 16384
+    sustained = flops / (float(np.median(ms)) / 1e3) / 1e12
+    return {"sustained_tflops": round(sustained, 1),
+            "kernel_frac_of_sustained": round(achieved_tflops / sustained, 4),
+            "loop": "bf16 16x16x32 MFMAs over a 128 x 64 wave tile, operands in registers, "
+                    "%d workgroups of 4 waves, %.1f ms per launch" % (CALIB_BLOCKS, float(np.median(ms)))}
 
 
 def recorded_traffic(workload):
@@ -583,6 +623,8 @@ def main():
                                      + 4 * (E + 1) + (4 * M if p["gather"] else 0)),
         "roofline": roof,
     }
+    if prefill:
+        out["mfma_calibration"] = mfma_calibration(roof["achieved"])
     if mx_ms is not None:
         mx_s = float(np.mean(mx_ms)) / 1e3
         out["mxfp4_us"] = round(mx_s * 1e6, 2)

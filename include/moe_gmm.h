@@ -305,6 +305,27 @@ int moe_mxfp4_to_nvfp4(const uint8_t* scales, int32_t E, int32_t N, int32_t K,
 int moe_debug_decode(const void* packed, int fmt, int32_t E, int32_t N,
                      int32_t K, uint16_t* w_bf16, void* stream);
 
+/*
+ * moe_calib_mfma_bf16 - measurement support: the bf16 matrix-unit rate this
+ * part sustains with no memory traffic.  The published dense bf16 peak
+ * assumes the full shader clock on every cycle; this loop measures what the
+ * matrix cores hold under the part's power limit, for reading the tiled
+ * grouped matmul's MFMA-bound fraction against.
+ *
+ * a    [blocks*256*8] 16-byte A fragments (8 bf16 each), lane-major: lane g
+ *      of the grid holds a[8g .. 8g+7].
+ * b    [blocks*256*4] 16-byte B fragments, b[4g .. 4g+3] for lane g.
+ * out  [blocks*256] f32, out: a sum of each lane's accumulators.
+ * Each wave keeps its fragments in registers and issues iters * 128
+ * v_mfma_f32_16x16x32_bf16 over a 128 x 64 accumulator tile (the tiled
+ * kernel's wave tile), rotating the fragments so that every instruction's
+ * operands differ from the previous one's.  FLOPs per call:
+ * blocks * 4 waves * iters * 128 * 16384.
+ * Limits: 1 <= blocks <= 65535, 1 <= iters <= 2^20; a and b 16-byte aligned.
+ */
+int moe_calib_mfma_bf16(const uint16_t* a, const uint16_t* b, int32_t blocks,
+                        int32_t iters, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,6 +48,7 @@ _SIGNATURES = {
                                    ctypes.c_int, _vp]),
     "moe_mxfp4_to_nvfp4": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "moe_debug_decode": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp]),
+    "moe_calib_mfma_bf16": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
 }
 
 
@@ -290,3 +291,18 @@ def debug_decode(packed, fmt, E, N, K):
     w = torch.empty((E, N, K), dtype=torch.int16, device=packed.device)
     _check(library().moe_debug_decode(_ptr(packed), fmt, E, N, K, _ptr(w), _stream()))
     return w
+
+
+def calib_mfma_bf16(a, b, blocks, iters):
+    """moe_calib_mfma_bf16: blocks workgroups of 4 waves, each wave issuing
+    iters * 128 bf16 MFMAs (16x16x32) on register-resident fragments taken
+    from a ([blocks*256*8*8] bf16 bits) and b ([blocks*256*4*8]).  Returns the
+    [blocks*256] f32 sums; FLOPs = blocks * 4 * iters * 128 * 16384."""
+    a = _bits16(a, "a")
+    b = _bits16(b, "b")
+    lanes = blocks * 256
+    if a.numel() < lanes * 64 or b.numel() < lanes * 32:
+        raise MoeGmmError("calib_mfma_bf16: a needs %d and b %d bf16 values" % (lanes * 64, lanes * 32))
+    out = torch.empty(lanes, dtype=torch.float32, device=a.device)
+    _check(library().moe_calib_mfma_bf16(_ptr(a), _ptr(b), blocks, iters, _ptr(out), _stream()))
+    return out

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoegmm.so")
 
-SOURCES = ["api.cpp", "route_sort.hip", "encode.hip", "gmm.hip", "combine.hip"]
+SOURCES = ["api.cpp", "route_sort.hip", "encode.hip", "gmm.hip", "combine.hip", "calib.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

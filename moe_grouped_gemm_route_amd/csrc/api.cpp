@@ -200,4 +200,12 @@ int moe_debug_decode(const void* packed, int fmt, int32_t E, int32_t N, int32_t 
                                              w_bf16, static_cast<hipStream_t>(stream)));
 }
 
+int moe_calib_mfma_bf16(const uint16_t* a, const uint16_t* b, int32_t blocks, int32_t iters, float* out,
+                        void* stream) {
+  if (!a || !b || !out) return MOE_ERR_NULL;
+  if (blocks < 1 || blocks > 65535 || iters < 1 || iters > (1 << 20)) return MOE_ERR_SHAPE;
+  if (((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)out & 3)) return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_calib_mfma(a, b, blocks, iters, out, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

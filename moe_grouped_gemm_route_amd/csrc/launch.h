@@ -43,6 +43,11 @@ hipError_t launch_gmm_w4a4(const uint8_t* packed, int32_t E, int32_t N, int32_t 
 hipError_t launch_quantize_mxfp4(const uint16_t* x, int32_t R, int32_t K, uint8_t* codes, uint8_t* scales,
                                  hipStream_t stream);
 
+// Matrix-unit calibration: blocks workgroups of 4 waves, each wave issuing
+// iters * 128 bf16 MFMAs on register-resident fragments (a: 8, b: 4 per lane).
+hipError_t launch_calib_mfma(const uint16_t* a, const uint16_t* b, int32_t blocks, int32_t iters, float* out,
+                             hipStream_t stream);
+
 hipError_t launch_combine(const void* y, int y_bf16, const float* w, const int32_t* pair_row,
                           int32_t T, int32_t k, int32_t N, void* out, int out_bf16,
                           hipStream_t stream);

@@ -168,6 +168,17 @@ def test_cast_and_debug_decode_validation(lib):
     assert lib.moe_debug_decode(None, 0, 1, 64, 128, FAKE, None) == ERR_NULL
 
 
+def test_calib_validation(lib):
+    f = lib.moe_calib_mfma_bf16
+    assert f(None, FAKE_ALIGNED, 1, 1, FAKE_ALIGNED, None) == ERR_NULL
+    assert f(FAKE_ALIGNED, FAKE_ALIGNED, 1, 1, None, None) == ERR_NULL
+    assert f(FAKE_ALIGNED, FAKE_ALIGNED, 0, 1, FAKE_ALIGNED, None) == ERR_SHAPE
+    assert f(FAKE_ALIGNED, FAKE_ALIGNED, 65536, 1, FAKE_ALIGNED, None) == ERR_SHAPE
+    assert f(FAKE_ALIGNED, FAKE_ALIGNED, 1, 0, FAKE_ALIGNED, None) == ERR_SHAPE
+    assert f(FAKE_ALIGNED, FAKE_ALIGNED, 1, (1 << 20) + 1, FAKE_ALIGNED, None) == ERR_SHAPE
+    assert f(ctypes.c_void_p((1 << 30) + 8), FAKE_ALIGNED, 1, 1, FAKE_ALIGNED, None) == ERR_SHAPE
+
+
 def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(moe.MoeGmmError):

@@ -608,3 +608,18 @@ def test_config3_w2_then_combine():
         for j in range(k):
             ref[i] += float(p["topk_weights"][t, j]) * yref[i * k + j]
     assert rel_err(out[np.ix_(toks, cols)], ref) <= REL_TOL
+
+
+# ------------------------------------------------------- calibration ---
+def test_calib_mfma_closed_form():
+    # all-ones A with B = 1 or 2: every 16x16x32 MFMA adds 32 * b to each of
+    # a lane's 4 accumulator elements; a lane holds 32 tiles and each
+    # iteration runs 4 rounds, so its sum is 128 * 128 * iters * b (exact)
+    blocks, iters = 3, 5
+    a = torch.full((blocks * 256 * 64,), 1.0, dtype=torch.bfloat16, device="cuda")
+    for bv in (1.0, 2.0):
+        b = torch.full((blocks * 256 * 32,), bv, dtype=torch.bfloat16, device="cuda")
+        out = moe.calib_mfma_bf16(a, b, blocks, iters)
+        torch.cuda.synchronize()
+        assert torch.all(out == 16384.0 * iters * bv)
+
