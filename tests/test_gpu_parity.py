@@ -96,6 +96,18 @@ def test_route_sort_edge_cases():
     _route_check(rng.integers(0, 3, size=(5000, 1)).astype(np.int32), 3)
 
 
+def test_route_sort_max_pairs():
+    # the largest pair count the call accepts (T * k = 2^24): E = 1024 with
+    # uniform ids, and E = 256 with a skewed id mix (a quarter of the pairs on
+    # expert 0), against the oracle's stable sort, bit for bit
+    rng = np.random.default_rng(8)
+    ids = rng.integers(0, 1024, size=(1 << 21, 8), dtype=np.int32)
+    _route_check(ids, 1024)
+    ids = rng.integers(0, 256, size=(1 << 22, 4), dtype=np.int32)
+    ids[rng.random(ids.shape) < 0.25] = 0
+    _route_check(ids, 256)
+
+
 # ------------------------------------------------------------------- gmm ---
 
 SMALL = [
