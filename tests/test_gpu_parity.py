@@ -445,6 +445,36 @@ def test_gmm_rows_past_bands_untouched_and_canary():
         assert rel_err(got[:M - 2], ref[:M - 2]) <= REL_TOL
 
 
+def test_all_pairs_dropped():
+    # every id outside [0, E): every band is empty, so no tile runs and y is
+    # left untouched by both kernels, the fused activation and W4A4; combine
+    # of all-dropped pairs gives zeros
+    p = make_problem(T=40, k=3, E=8, K=256, N=256, seed=330)
+    p["topk_ids"][:] = p["E"]
+    p["topk_ids"][::2, 1] = -5
+    M, N, K, E = p["T"] * p["k"], p["N"], p["K"], p["E"]
+    r = moe.route_sort(to_dev(p["topk_ids"]), E)
+    assert int(r["err_count"].item()) == M
+    assert torch.all(r["group_offsets"] == 0) and torch.all(r["pair_row"] == -1)
+    _, packed = weights_for(p, "mxfp4")
+    x = to_dev(p["x"])
+    for kernel in KERNELS:
+        for act in (moe.ACT_NONE, moe.ACT_SILU_MUL):
+            cols = N // 2 if act == moe.ACT_SILU_MUL else N
+            buf = torch.full((M, cols), 777.0, dtype=torch.float32, device="cuda")
+            moe.moe_gmm(packed, moe.MXFP4, E, N, K, x, r["group_offsets"], M, row_index=r["sorted_token"],
+                        kernel=kernel, act=act, out=buf)
+            torch.cuda.synchronize()
+            assert torch.all(buf == 777.0)
+    qc, qs = moe.mxfp4_quantize(x)
+    buf = torch.full((M, N), 777.0, dtype=torch.float32, device="cuda")
+    moe.moe_gmm_w4a4(packed, E, N, K, qc, qs, r["group_offsets"], M, row_index=r["sorted_token"], out=buf)
+    out = moe.moe_combine(buf, to_dev(p["topk_weights"]), r["pair_row"])
+    torch.cuda.synchronize()
+    assert torch.all(buf == 777.0)
+    assert torch.all(out == 0.0)
+
+
 def test_gmm_deterministic():
     p = _small(1)
     _, packed = weights_for(p, "mxfp4")
