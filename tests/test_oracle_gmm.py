@@ -4,7 +4,8 @@
   decode each weight from its bit fields, without the sort;
 * closed forms: all-ones weights give row sums, all-zero codes give zeros;
 * exactness: sampled outputs against exact rational dot products, within the
-  float64 summation error bound;
+  float64 summation error bound (config 1, and 1,000 samples of each
+  full-size workload with the exact products built from the bit fields);
 * combine: one-hot, uniform and zero router weights.
 """
 
@@ -227,3 +228,89 @@ def test_gmm_bf16_of_decoded_mxfp4_equals_mxfp4():
     y_mx = oracle.gmm(p["x"], r["sorted_token"], r["group_offsets"], _mx(p))
     y_bf = oracle.gmm(p["x"], r["sorted_token"], r["group_offsets"], {"fmt": "bf16", "weights": wb})
     assert np.array_equal(y_mx, y_bf)
+
+
+# ------------------------------------------------------------------------
+# Exact-arithmetic pin of the sampled oracle at the full workload sizes.
+# Every bf16 activation is an integer times a power of two, and so is every
+# decoded weight (e2m1 magnitude in halves x block scale x tensor scale), so a
+# dot product is an exact sum of integers times powers of two.  The decode
+# below works on the raw bit fields and shares nothing with the oracle's.
+
+def _bf16_int(bits):
+    """bf16 bit patterns -> (signed integer mantissa, exponent) with
+    value = mantissa * 2**exponent (normal and subnormal numbers)."""
+    b = np.asarray(bits, dtype=np.int64)
+    s, ex, m = b >> 15, (b >> 7) & 0xFF, b & 0x7F
+    mant = np.where(ex > 0, 128 + m, m)
+    exp = np.where(ex > 0, ex, 1) - 127 - 7
+    return np.where(s == 1, -mant, mant), exp
+
+
+def _e2m1_halves(nib):
+    """e2m1 nibble -> signed magnitude in halves, from its fields."""
+    nib = np.asarray(nib, dtype=np.int64)
+    s, e, m = nib >> 3, (nib >> 1) & 3, nib & 1
+    mag = np.where(e == 0, m, (2 + m) << np.maximum(e - 1, 0))
+    return np.where(s == 1, -mag, mag)
+
+
+def _e4m3_int(b):
+    """E4M3FN bytes (finite, non-negative here) -> (integer, exponent)."""
+    b = np.asarray(b, dtype=np.int64)
+    assert np.all((b & 0x80) == 0) and np.all((b & 0x7F) != 0x7F)
+    ex, m = (b >> 3) & 0xF, b & 7
+    return np.where(ex > 0, 8 + m, m), np.where(ex > 0, ex, 1) - 7 - 3
+
+
+def _exact_sum(mant, exp):
+    """Sum of mant[i] * 2**exp[i] as an exact Fraction (int64 partial sums
+    per exponent, then Python integers)."""
+    total = Fraction(0)
+    for e in np.unique(exp):
+        part = int(mant[exp == e].sum())
+        total += Fraction(part) * (Fraction(2) ** int(e))
+    return total
+
+
+def _pin_sampled(p, w_kind, n_samples, seed):
+    r = oracle.route_sort(p["topk_ids"], p["E"])
+    off = r["group_offsets"]
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, off[-1], size=n_samples)
+    cols = rng.integers(0, p["N"], size=n_samples)
+    row_index = r["sorted_token"] if p["gather"] else None
+    if w_kind == "nvfp4":
+        bs, ts = oracle.mxfp4_to_nvfp4(p["scales"])
+        w = {"fmt": "nvfp4", "codes": p["codes"], "block_scales": bs, "tensor_scale": ts}
+    else:
+        w = _mx(p)
+    got = oracle.gmm_sampled(p["x"], row_index, off, w, rows, cols)
+    K = p["K"]
+    gamma = K * 2.0 ** -53 / (1 - K * 2.0 ** -53)
+    for i, (row, col) in enumerate(zip(rows, cols)):
+        e = int(np.searchsorted(off, row, side="right") - 1)
+        src = int(row_index[row]) if row_index is not None else int(row)
+        xm, xe = _bf16_int(p["x"][src])
+        codes = p["codes"][e, col].astype(np.int64)
+        nib = np.stack([codes & 0xF, codes >> 4], axis=-1).reshape(-1)
+        q = _e2m1_halves(nib)
+        if w_kind == "nvfp4":
+            sm, se = _e4m3_int(np.repeat(bs[e, col], 16))
+            tm, te = np.frexp(np.float64(ts[e]))
+            assert tm == 0.5                      # the cast's tensor scale is a power of two
+            mant, exp = xm * q * sm, xe + se - 1 + (int(te) - 1)
+        else:
+            sc = np.repeat(p["scales"][e, col].astype(np.int64), 32)
+            mant, exp = xm * q, xe + sc - 127 - 1
+        exact = _exact_sum(mant, exp)
+        bound = gamma * float(_exact_sum(np.abs(mant), exp))
+        assert abs(Fraction(float(got[i])) - exact) <= Fraction(bound), (row, col)
+
+
+def test_gmm_sampled_exact_at_full_size():
+    # 1,000 sampled outputs of each full-size workload (w13 decode, w2 decode
+    # on the band input, w13 prefill, NVFP4 by the lossless cast) against the
+    # exact rational dot product, within the float64 summation bound
+    for cfg, kind in ((2, "mxfp4"), (3, "mxfp4"), (4, "mxfp4"), (5, "nvfp4")):
+        _pin_sampled(make_config(cfg), kind, 1000, 40 + cfg)
