@@ -8,7 +8,10 @@
 // section "Correctness and precision") requires.
 //
 // HBM-bound: each thread produces 4 consecutive columns of one token with
-// 16-byte (f32) or 8-byte (bf16) loads per slot.
+// 16-byte (f32) or 8-byte (bf16) loads per slot.  The band rows and router
+// weights of up to CB slots are loaded first and then all of their row
+// loads are issued together, so a thread keeps CB row loads in flight
+// instead of one; the FMAs still run in slot order.
 #include "common.h"
 #include "launch.h"
 
@@ -28,23 +31,42 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   const int64_t t = i / quads;
   const int64_t c = (i - t * quads) << 2;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int32_t row = pair_row[t * k + j];
-    if (row < 0) continue;
-    const float wj = w[t * k + j];
-    float v0, v1, v2, v3;
-    if (YBF16) {
-      const uint2 q = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(y) + (int64_t)row * N + c);
-      v0 = bf16_to_f32(q.x & 0xFFFF); v1 = bf16_to_f32(q.x >> 16);
-      v2 = bf16_to_f32(q.y & 0xFFFF); v3 = bf16_to_f32(q.y >> 16);
-    } else {
-      const float4 q = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(y) + (int64_t)row * N + c);
-      v0 = q.x; v1 = q.y; v2 = q.z; v3 = q.w;
+  constexpr int CB = 8;   // slots whose row loads are in flight together
+  for (int j0 = 0; j0 < k; j0 += CB) {
+    int32_t row[CB];
+    float wj[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int j = j0 + u;
+      row[u] = j < k ? pair_row[t * k + j] : -1;
+      wj[u] = j < k ? w[t * k + j] : 0.f;
     }
-    a0 = fmaf(wj, v0, a0);
-    a1 = fmaf(wj, v1, a1);
-    a2 = fmaf(wj, v2, a2);
-    a3 = fmaf(wj, v3, a3);
+    float v[CB][4];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      v[u][0] = v[u][1] = v[u][2] = v[u][3] = 0.f;
+      if (row[u] >= 0) {
+        if (YBF16) {
+          const uint2 q =
+              *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(y) + (int64_t)row[u] * N + c);
+          v[u][0] = bf16_to_f32(q.x & 0xFFFF); v[u][1] = bf16_to_f32(q.x >> 16);
+          v[u][2] = bf16_to_f32(q.y & 0xFFFF); v[u][3] = bf16_to_f32(q.y >> 16);
+        } else {
+          const float4 q = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(y) + (int64_t)row[u] * N + c);
+          v[u][0] = q.x; v[u][1] = q.y; v[u][2] = q.z; v[u][3] = q.w;
+        }
+      }
+    }
+    // slot order; a dropped pair (row < 0) contributes nothing
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      if (row[u] >= 0) {
+        a0 = fmaf(wj[u], v[u][0], a0);
+        a1 = fmaf(wj[u], v[u][1], a1);
+        a2 = fmaf(wj[u], v[u][2], a2);
+        a3 = fmaf(wj[u], v[u][3], a3);
+      }
+    }
   }
   if (OBF16) {
     uint2 q;
