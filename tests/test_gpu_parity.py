@@ -584,6 +584,40 @@ def test_gmm_largest_activation_matrix(kernel):
     assert rel_err(got, ref) <= REL_TOL
 
 
+def test_gmm_w4a4_largest_activation_codes():
+    # W4A4 at the 32-bit byte-offset limit of its activation-code loads:
+    # 1,048,575 token rows x 2048 code bytes = 2^31 - 2 KiB (random codes and
+    # E8M0 scales), every row its own band entry (top-1 of 8), gathered
+    # through row_index; the rows of the last tokens are among the samples
+    from oracle.formats import decode_mxfp4
+    K, N, E = 4096, 256, 8
+    T = ((1 << 31) - 1) // (K // 2)
+    p = make_problem(T=1, k=1, E=E, K=K, N=N, seed=480)
+    rng = np.random.default_rng(481)
+    qc = rng.integers(0, 256, size=(T, K // 2), dtype=np.uint8)
+    qs = (rng.integers(-4, 1, size=(T, K // 32)) + 127).astype(np.uint8)
+    ids = rng.integers(0, E, size=(T, 1)).astype(np.int32)
+    w, packed = weights_for(p, "mxfp4")
+    print("largest W4A4 activation codes: T=%d K=%d" % (T, K), flush=True)
+    r = moe.route_sort(to_dev(ids), E)
+    y = moe.moe_gmm_w4a4(packed, E, N, K, to_dev(qc), to_dev(qs), r["group_offsets"], T,
+                         row_index=r["sorted_token"])
+    ref_r = oracle.route_sort(ids, E)
+    assert np.array_equal(r["group_offsets"].cpu().numpy(), ref_r["group_offsets"])
+    rows, cols = _sample(T, N, 1500, 482)
+    rows[8:24] = ref_r["pair_row"][T - 16:]                   # the last 16 tokens' rows
+    off = ref_r["group_offsets"]
+    ref = np.empty(len(rows))
+    for i, (row, col) in enumerate(zip(rows, cols)):
+        e = int(np.searchsorted(off, row, side="right") - 1)
+        src = int(ref_r["sorted_token"][row])
+        xa = decode_mxfp4(qc[src], qs[src])
+        wc = decode_mxfp4(p["codes"][e, col], p["scales"][e, col])
+        ref[i] = float(np.dot(xa, wc))
+    got = y.cpu().numpy()[rows, cols].astype(np.float64)
+    assert rel_err(got, ref) <= REL_TOL
+
+
 def test_config5_nvfp4_equals_mxfp4_bitwise():
     p = make_config(5)
     _, packed_mx = weights_for(p, "mxfp4")
