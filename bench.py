@@ -180,6 +180,15 @@ def layer_cpu_baseline(p, unit="GB/s", target_s=15.0):
     }
 
 
+def route_workspace(T, k, E, dev):
+    """The route sort's device workspace, allocated once outside the timed
+    steps (None when the sort needs none)."""
+    import torch
+    import moe_grouped_gemm_route_amd as moe
+    need = moe.route_sort_workspace_bytes(T, k, E)
+    return torch.empty((need + 3) // 4, dtype=torch.int32, device=dev) if need else None
+
+
 def run_layer(args):
     """One routed-expert layer (the layer_decode and layer_prefill workloads)."""
     import torch
@@ -207,13 +216,14 @@ def run_layer(args):
     del codes
     h = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
     y2 = torch.empty((M, K), dtype=torch.float32, device=dev)
+    ws = route_workspace(T, k, E, dev)
     torch.cuda.synchronize()
     ev = []
 
     def step(timed):
         # events around each matmul kernel (the W4A4 quantizations fall between)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
-        r = moe.route_sort(ids, E)
+        r = moe.route_sort(ids, E, ws=ws)
         if w4a4:
             qc, qs = moe.mxfp4_quantize(x)
             if timed:
@@ -388,11 +398,12 @@ def run_w4a4(args):
     packed = moe.mxfp4_encode(codes, d(p["scales"]), None, moe.MXFP4)
     del codes
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws = route_workspace(T, k, E, dev)
     torch.cuda.synchronize()
     ev = []
 
     def step(timed):
-        r = moe.route_sort(ids, E)
+        r = moe.route_sort(ids, E, ws=ws)
         qc, qs = moe.mxfp4_quantize(x)
         if timed:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -525,12 +536,13 @@ def main():
     combine = cfg == 3
     y = torch.empty((M, N), dtype=torch.bfloat16 if odt == moe.BF16 else torch.float32, device=dev)
     kernel = KERNELS[args.kernel]
+    ws = route_workspace(T, k, E, dev)
     torch.cuda.synchronize()
 
     ev = []
 
     def step(timed):
-        r = moe.route_sort(ids, E)
+        r = moe.route_sort(ids, E, ws=ws)
         if timed:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -555,7 +567,7 @@ def main():
     mx_ms = None
     if bf16_arm:
         # the MXFP4 kernel on the same inputs, for the speedup
-        r = moe.route_sort(ids, E)
+        r = moe.route_sort(ids, E, ws=ws)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         for i in range(args.warmup):
             moe.moe_gmm(packed_mx, moe.MXFP4, E, N, K, x, r["group_offsets"], M,

@@ -67,14 +67,23 @@ typedef enum {
 const char* moe_status_string(int status);
 
 /*
+ * moe_route_sort_workspace_bytes - bytes of device workspace moe_route_sort
+ * needs for T tokens of k slots over E experts: 0 when the pairs are sorted
+ * by one workgroup (T*k <= 4096), else 4 * E * G, with G = ceil(T*k / S)
+ * segments of S = max(1024, ceil(T*k / 64) rounded up to 512) pairs
+ * (G <= 64, so at most 256 KiB).  Also 0 for sizes moe_route_sort rejects.
+ */
+size_t moe_route_sort_workspace_bytes(int32_t T, int32_t k, int32_t E);
+
+/*
  * moe_route_sort - counting sort of token-expert pairs into expert bands.
  *
  * Source: "Running DeepSeek V4 Flash on TPU v6", section "1. Four bits that
- * v6e can't hold": tokens are sorted by expert so that each expert's
- * activations form one contiguous band of rows, and the grouped matmul walks
- * the band sizes.  Inside a band, pairs keep ascending flat pair order
- * p = t*k + j (stable), so the result is unique and deterministic; positions
- * are decided by counts and scans, never by atomics.
+ * v6e can't hold": the activations are ordered by expert into one band of
+ * rows each, and the grouped matmul walks the band sizes.  Inside a band,
+ * pairs keep ascending flat pair order p = t*k + j (stable), so the result is
+ * unique and deterministic; positions are decided by counts and scans, never
+ * by atomics.
  *
  * topk_ids       [T, k] int32  expert of slot j of token t.
  * group_offsets  [E+1]  int32  out: band e is rows [off[e], off[e+1]).
@@ -84,12 +93,20 @@ const char* moe_status_string(int status);
  * err_count      [1]    int32  out, may be NULL: number of pairs whose id is
  *                              outside [0, E); they are dropped from every
  *                              band (the device-side data error).
+ * ws, ws_bytes   caller-owned device workspace of at least
+ *                moe_route_sort_workspace_bytes(T, k, E) bytes, 4-byte
+ *                aligned; it holds the per-segment expert counts between
+ *                the count and place kernels, needs no clearing and may be
+ *                reused once the stream has passed this call.  May be NULL
+ *                when that size is 0.
+ * Errors: NULL ws with a non-zero need -> MOE_ERR_NULL; ws_bytes below the
+ * need or ws misaligned -> MOE_ERR_SHAPE.
  * Limits: 1 <= T, 1 <= k, 1 <= E <= 1024, T*k <= 2^24.
  */
 int moe_route_sort(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                    int32_t* group_offsets, int32_t* sorted_token,
                    int32_t* sorted_pair, int32_t* pair_row, int32_t* err_count,
-                   void* stream);
+                   void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_packed_weight_bytes - size in bytes of the packed buffer that
@@ -118,11 +135,21 @@ size_t moe_packed_weight_bytes(int fmt, int32_t E, int32_t N, int32_t K);
  *                NVFP4: [E, N, K/16] E4M3FN bytes.
  * tensor_scale   NVFP4: [E] float, the per-expert scale; MXFP4: must be NULL.
  * packed         out, moe_packed_weight_bytes(fmt, E, N, K) bytes, 256-aligned.
+ * err_count      out [1] int32, may be NULL: the number of scale values
+ *                outside the exact-decode domain (the scale sanity sweep of
+ *                "DeepSeek-V4-Flash-0731-NVFP4", section "Verification"):
+ *                MXFP4 E8M0 bytes other than 2..252 (0 and 1 are below the
+ *                bf16-normal range of the decode, 253 and 254 overflow bf16
+ *                for the larger codes, 255 is NaN), NVFP4 E4M3 NaN bytes
+ *                (0x7F, 0xFF) and non-finite tensor scales.  Such values are
+ *                packed as given; the weights they scale do not decode to the
+ *                format's values, so every output they feed is unspecified.
+ *                A zero count means every packed weight decodes exactly.
  * Limits: K % 128 == 0, K < 2^26, N % 64 == 0, E >= 1, E*N*K/2 < 2^40.
  */
 int mxfp4_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
                  const float* tensor_scale, int32_t E, int32_t N, int32_t K,
-                 void* packed, void* stream);
+                 void* packed, int32_t* err_count, void* stream);
 
 /*
  * moe_bf16_encode - load-time repack of bf16 expert weights for the bf16
@@ -287,7 +314,7 @@ int moe_combine(const void* y, int y_dtype, const float* topk_weights,
  *
  * scales         [E, N, K/32] E8M0 bytes of one expert tensor per expert.
  * block_scales   out [E, N, K/16] E4M3FN bytes.
- * tensor_scale   out [E] float.
+ * tensor_scale   out [E] float (a subnormal f32 when k_max < -118; exact).
  * err_count      out [1] int32, may be NULL: blocks that cannot be held
  *                exactly (k_j < k_max - 17, or a NaN byte 0xFF); such a
  *                block's bytes are written as 0.

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "MXFP4", "NVFP4", "W_BF16", "F32", "BF16", "GMM_AUTO", "GMM_STREAM", "GMM_TILED", "ACT_NONE", "ACT_SILU_MUL",
-    "MoeGmmError", "library", "route_sort", "packed_weight_bytes", "mxfp4_encode",
+    "MoeGmmError", "library", "route_sort", "route_sort_workspace_bytes", "packed_weight_bytes", "mxfp4_encode",
     "moe_gmm", "moe_combine", "mxfp4_to_nvfp4", "debug_decode", "bf16_encode",
     "mxfp4_quantize", "moe_gmm_w4a4",
 ]
@@ -31,9 +31,10 @@ _lib = None
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 _SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
-    "moe_route_sort": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_route_sort_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "moe_route_sort": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_packed_weight_bytes": (_sz, [ctypes.c_int, _i32, _i32, _i32]),
-    "mxfp4_encode": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "mxfp4_encode": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "moe_bf16_encode": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp]),
     "moe_mxfp4_quantize": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "moe_gmm_w4a4": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp,
@@ -109,10 +110,17 @@ def _bits16(t, name):
     return _dev(t, torch.int16, name)
 
 
-def route_sort(topk_ids, E):
+def route_sort_workspace_bytes(T, k, E):
+    """moe_route_sort_workspace_bytes: device workspace bytes of a route sort
+    of T tokens x k slots over E experts (0 when none is needed)."""
+    return int(library().moe_route_sort_workspace_bytes(T, k, E))
+
+
+def route_sort(topk_ids, E, ws=None):
     """moe_route_sort.  topk_ids [T, k] int32 -> dict of int32 tensors
     group_offsets [E+1], sorted_token, sorted_pair, pair_row [T*k] and
-    err_count [1]."""
+    err_count [1].  ws: a device tensor of at least
+    route_sort_workspace_bytes(T, k, E) bytes, or None to allocate one."""
     _dev(topk_ids, torch.int32, "topk_ids", 2)
     T, k = topk_ids.shape
     dev = topk_ids.device
@@ -123,9 +131,17 @@ def route_sort(topk_ids, E):
         "pair_row": torch.empty(T * k, dtype=torch.int32, device=dev),
         "err_count": torch.empty(1, dtype=torch.int32, device=dev),
     }
+    need = route_sort_workspace_bytes(T, k, E)
+    if ws is None and need > 0:
+        ws = torch.empty((need + 3) // 4, dtype=torch.int32, device=dev)
+    if ws is not None:
+        if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+            raise MoeGmmError("ws must be a contiguous CUDA (HIP) tensor")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(library().moe_route_sort(
         _ptr(topk_ids), T, k, E, _ptr(out["group_offsets"]), _ptr(out["sorted_token"]),
-        _ptr(out["sorted_pair"]), _ptr(out["pair_row"]), _ptr(out["err_count"]), _stream()))
+        _ptr(out["sorted_pair"]), _ptr(out["pair_row"]), _ptr(out["err_count"]), _ptr(ws), ws_bytes,
+        _stream()))
     return out
 
 
@@ -136,10 +152,12 @@ def packed_weight_bytes(fmt, E, N, K):
     return n
 
 
-def mxfp4_encode(codes, scales, tensor_scale=None, fmt=MXFP4):
+def mxfp4_encode(codes, scales, tensor_scale=None, fmt=MXFP4, err_count=None):
     """mxfp4_encode.  codes [E, N, K/2] uint8, scales [E, N, K/32] (MXFP4) or
     [E, N, K/16] (NVFP4) uint8, tensor_scale [E] float32 (NVFP4 only).
-    Returns the packed uint8 buffer."""
+    Returns the packed uint8 buffer.  err_count: an optional [1] int32 device
+    tensor that receives the number of scale values outside the exact-decode
+    domain."""
     _dev(codes, torch.uint8, "codes", 3)
     _dev(scales, torch.uint8, "scales", 3)
     E, N, K2 = codes.shape
@@ -150,8 +168,10 @@ def mxfp4_encode(codes, scales, tensor_scale=None, fmt=MXFP4):
     if fmt == NVFP4:
         _dev(tensor_scale, torch.float32, "tensor_scale", 1)
     packed = torch.empty(packed_weight_bytes(fmt, E, N, K), dtype=torch.uint8, device=codes.device)
+    if err_count is not None:
+        _dev(err_count, torch.int32, "err_count", 1)
     _check(library().mxfp4_encode(fmt, _ptr(codes), _ptr(scales), _ptr(tensor_scale), E, N, K,
-                                  _ptr(packed), _stream()))
+                                  _ptr(packed), _ptr(err_count), _stream()))
     return packed
 
 

@@ -33,6 +33,14 @@ int check_weight_shape(int fmt, int32_t E, int32_t N, int32_t K) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Route-sort sizes: ids fit the 10 id bits the placement ballots, and every
+// pair and row index fits int32.
+int route_sort_shape(int32_t T, int32_t k, int32_t E) {
+  if (T < 1 || k < 1 || E < 1 || E > 1024) return MOE_ERR_SHAPE;
+  if ((int64_t)T * k > kMaxRows) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -49,14 +57,24 @@ const char* moe_status_string(int status) {
   }
 }
 
+size_t moe_route_sort_workspace_bytes(int32_t T, int32_t k, int32_t E) {
+  if (route_sort_shape(T, k, E) != MOE_OK) return 0;
+  return moe::route_plan((int64_t)T * k, E).ws_bytes;
+}
+
 int moe_route_sort(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                    int32_t* group_offsets, int32_t* sorted_token, int32_t* sorted_pair,
-                   int32_t* pair_row, int32_t* err_count, void* stream) {
+                   int32_t* pair_row, int32_t* err_count, void* ws, size_t ws_bytes, void* stream) {
   if (!topk_ids || !group_offsets || !sorted_token || !sorted_pair || !pair_row) return MOE_ERR_NULL;
-  if (T < 1 || k < 1 || E < 1 || E > 1024) return MOE_ERR_SHAPE;
-  if ((int64_t)T * k > kMaxRows) return MOE_ERR_SHAPE;
+  const int st = route_sort_shape(T, k, E);
+  if (st != MOE_OK) return st;
+  const size_t need = moe::route_plan((int64_t)T * k, E).ws_bytes;
+  if (need > 0) {
+    if (!ws) return MOE_ERR_NULL;
+    if (ws_bytes < need || ((uintptr_t)ws & 3)) return MOE_ERR_SHAPE;
+  }
   return hip_status(moe::launch_route_sort(topk_ids, T, k, E, group_offsets, sorted_token,
-                                           sorted_pair, pair_row, err_count,
+                                           sorted_pair, pair_row, err_count, static_cast<int32_t*>(ws),
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -66,7 +84,7 @@ size_t moe_packed_weight_bytes(int fmt, int32_t E, int32_t N, int32_t K) {
 }
 
 int mxfp4_encode(int fmt, const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
-                 int32_t E, int32_t N, int32_t K, void* packed, void* stream) {
+                 int32_t E, int32_t N, int32_t K, void* packed, int32_t* err_count, void* stream) {
   const int st = check_weight_shape(fmt, E, N, K);
   if (st != MOE_OK) return st;
   if (!codes || !scales || !packed) return MOE_ERR_NULL;
@@ -75,7 +93,7 @@ int mxfp4_encode(int fmt, const uint8_t* codes, const uint8_t* scales, const flo
   if (fmt == MOE_W_MXFP4 && tensor_scale) return MOE_ERR_FORMAT;
   if (((uintptr_t)codes & 15) || ((uintptr_t)packed & 255)) return MOE_ERR_SHAPE;
   return hip_status(moe::launch_encode(fmt, codes, scales, tensor_scale, E, N, K,
-                                       static_cast<uint8_t*>(packed),
+                                       static_cast<uint8_t*>(packed), err_count,
                                        static_cast<hipStream_t>(stream)));
 }
 

@@ -27,12 +27,18 @@ __global__ __launch_bounds__(256) void encode_codes_kernel(const u32x4_t* __rest
   }
 }
 
-// One thread per packed scale dword (lane l of record (e, nt, q)).
+// One thread per packed scale dword (lane l of record (e, nt, q)).  Every
+// scale byte is read by exactly one thread, which also counts the bytes
+// outside the exact-decode domain: E8M0 bytes other than 2..252 (block
+// exponents -125..125; 255 is NaN), E4M3 NaN bytes, and non-finite tensor
+// scales.
 __global__ __launch_bounds__(256) void encode_scales_kernel(int fmt, const uint8_t* __restrict__ scales,
                                                             const float* __restrict__ tscale, Layout L,
-                                                            uint8_t* __restrict__ packed) {
+                                                            uint8_t* __restrict__ packed,
+                                                            int32_t* __restrict__ err_count) {
   const int64_t words = L.E * L.NT * L.groups * 64;
   uint32_t* out = reinterpret_cast<uint32_t*>(packed + L.scales_off);
+  int bad = 0;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < words;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t lane = i & 63;
@@ -46,7 +52,9 @@ __global__ __launch_bounds__(256) void encode_scales_kernel(int fmt, const uint8
         const int64_t kc = q * 4 + c;
         if (kc < L.KC) {
           const int64_t kb = kc * 4 + (lane >> 4);
-          word |= (uint32_t)scales[(e * L.N + n) * L.KB + kb] << (8 * c);
+          const uint32_t b = scales[(e * L.N + n) * L.KB + kb];
+          bad += (b < 2u || b > 252u) ? 1 : 0;
+          word |= b << (8 * c);
         }
       }
     } else {
@@ -55,6 +63,7 @@ __global__ __launch_bounds__(256) void encode_scales_kernel(int fmt, const uint8
         if (kc < L.KC) {
           const int64_t kb = kc * 4 + (lane >> 4);
           const uint8_t* s = scales + (e * L.N + n) * (L.KB * 2) + kb * 2;
+          bad += ((s[0] & 0x7F) == 0x7F ? 1 : 0) + ((s[1] & 0x7F) == 0x7F ? 1 : 0);
           word |= ((uint32_t)s[0] | ((uint32_t)s[1] << 8)) << (16 * c);
         }
       }
@@ -64,15 +73,26 @@ __global__ __launch_bounds__(256) void encode_scales_kernel(int fmt, const uint8
   if (fmt == 1) {
     float* ts = reinterpret_cast<float*>(packed + L.tscale_off);
     for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < L.E;
-         e += (int64_t)gridDim.x * blockDim.x)
-      ts[e] = tscale[e];
+         e += (int64_t)gridDim.x * blockDim.x) {
+      const float t = tscale[e];
+      bad += (__float_as_uint(t) & 0x7F800000u) == 0x7F800000u ? 1 : 0;
+      ts[e] = t;
+    }
   }
+  if (err_count && bad) atomicAdd(err_count, bad);
+}
+
+// Clears a small int32 counter with a kernel (kept out of memset nodes so the
+// call stays safe to record into a HIP graph).
+__global__ void zero_i32_kernel(int32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
 }
 
 hipError_t launch_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
                          const float* tensor_scale, int32_t E, int32_t N, int32_t K,
-                         uint8_t* packed, hipStream_t stream) {
+                         uint8_t* packed, int32_t* err_count, hipStream_t stream) {
   const Layout L = make_layout(fmt, E, N, K);
+  if (err_count) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, stream, err_count, 1);
   const int64_t runs = L.E * L.N * L.KB;
   const int grid_c = (int)((runs + 255) / 256 < 65536 ? (runs + 255) / 256 : 65536);
   hipLaunchKernelGGL(encode_codes_kernel, dim3(grid_c), dim3(256), 0, stream,
@@ -80,7 +100,7 @@ hipError_t launch_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
   const int64_t words = L.E * L.NT * L.groups * 64;
   const int grid_s = (int)((words + 255) / 256 < 65536 ? (words + 255) / 256 : 65536);
   hipLaunchKernelGGL(encode_scales_kernel, dim3(grid_s), dim3(256), 0, stream, fmt, scales,
-                     tensor_scale, L, packed);
+                     tensor_scale, L, packed, err_count);
   return hipGetLastError();
 }
 
@@ -240,12 +260,6 @@ hipError_t launch_quantize_mxfp4(const uint16_t* x, int32_t R, int32_t K, uint8_
   return hipGetLastError();
 }
 
-// Clears a small int32 counter with a kernel (kept out of memset nodes so the
-// call stays safe to record into a HIP graph).
-__global__ void zero_i32_kernel(int32_t* p, int n) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
-}
-
 // Lossless scale cast: one workgroup per expert.  Pass 1 finds the largest
 // block exponent; pass 2 writes both 16-half E4M3 bytes of every block.
 __global__ __launch_bounds__(256) void mxfp4_to_nvfp4_kernel(const uint8_t* __restrict__ scales,
@@ -286,7 +300,9 @@ __global__ __launch_bounds__(256) void mxfp4_to_nvfp4_kernel(const uint8_t* __re
   if (bad) atomicAdd(&s_bad, bad);
   __syncthreads();
   if (threadIdx.x == 0) {
-    ts[e] = __uint_as_float((uint32_t)(bmax - 8) << 23);
+    // 2^(k_max - 8) = 2^(bmax - 135): a normal f32 for bmax >= 9, else the
+    // subnormal with mantissa bit bmax + 14 (exact down to bmax = 0)
+    ts[e] = __uint_as_float(bmax >= 9 ? (uint32_t)(bmax - 8) << 23 : 1u << (bmax + 14));
     if (err_count && s_bad) atomicAdd(err_count, s_bad);
   }
 }

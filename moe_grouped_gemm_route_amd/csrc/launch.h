@@ -7,13 +7,23 @@
 
 namespace moe {
 
+// Route-sort plan for M pairs: G segments of S pairs, one workgroup each.
+// Small M: one workgroup, no workspace (fused); else a count kernel and a
+// place kernel with a [G][E] int32 count table in the workspace.
+struct RoutePlan {
+  int fused;
+  int S, G;
+  size_t ws_bytes;
+};
+RoutePlan route_plan(int64_t M, int32_t E);
+
 hipError_t launch_route_sort(const int32_t* ids, int32_t T, int32_t k, int32_t E,
                              int32_t* group_offsets, int32_t* sorted_token, int32_t* sorted_pair,
-                             int32_t* pair_row, int32_t* err_count, hipStream_t stream);
+                             int32_t* pair_row, int32_t* err_count, int32_t* ws, hipStream_t stream);
 
 hipError_t launch_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
                          const float* tensor_scale, int32_t E, int32_t N, int32_t K,
-                         uint8_t* packed, hipStream_t stream);
+                         uint8_t* packed, int32_t* err_count, hipStream_t stream);
 
 hipError_t launch_bf16_encode(const uint16_t* w, int32_t E, int32_t N, int32_t K, uint8_t* packed,
                               hipStream_t stream);

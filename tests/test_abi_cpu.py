@@ -58,23 +58,51 @@ def test_packed_bytes(lib):
     assert lib.moe_packed_weight_bytes(7, 8, 512, 256) == 0
 
 
+def _ws_formula(T, k, E):
+    """The workspace size the header documents: none up to 4,096 pairs, else
+    4 E bytes per segment of max(1024, ceil(M / 64) rounded up to 512)
+    pairs."""
+    M = T * k
+    if M <= 4096:
+        return 0
+    s = max(1024, -(-(-(-M // 64)) // 512) * 512)
+    return 4 * E * -(-M // s)
+
+
+def test_route_sort_workspace_bytes(lib):
+    f = lib.moe_route_sort_workspace_bytes
+    for T, k, E in [(64, 2, 8), (64, 6, 256), (256, 6, 256), (682, 6, 256), (4096, 1, 1024),
+                    (4097, 1, 256), (4096, 6, 256), (1 << 21, 8, 1024), (1 << 22, 4, 256),
+                    (3000, 8, 1024), (100000, 7, 3)]:
+        assert f(T, k, E) == _ws_formula(T, k, E), (T, k, E)
+    assert f(4096, 6, 256) == 24 * 256 * 4            # the 4,096-token prefill: 24 segments
+    assert f(4097, 1, 256) == 5 * 256 * 4
+    assert f(1 << 21, 8, 1024) == 64 * 1024 * 4       # the largest accepted problem: 256 KiB
+    assert f(0, 6, 256) == 0 and f(4, 2, 1025) == 0 and f(1 << 22, 8, 8) == 0
+
+
 def test_route_sort_validation(lib):
     f = lib.moe_route_sort
-    assert f(None, 4, 2, 8, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_NULL
-    assert f(FAKE, 0, 2, 8, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
-    assert f(FAKE, 4, 0, 8, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
-    assert f(FAKE, 4, 2, 1025, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
-    assert f(FAKE, 1 << 22, 8, 8, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert f(None, 4, 2, 8, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == ERR_NULL
+    assert f(FAKE, 0, 2, 8, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == ERR_SHAPE
+    assert f(FAKE, 4, 0, 8, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == ERR_SHAPE
+    assert f(FAKE, 4, 2, 1025, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == ERR_SHAPE
+    assert f(FAKE, 1 << 22, 8, 8, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == ERR_SHAPE
+    need = lib.moe_route_sort_workspace_bytes(4096, 6, 256)
+    assert f(FAKE, 4096, 6, 256, FAKE, FAKE, FAKE, FAKE, None, None, need, None) == ERR_NULL
+    assert f(FAKE, 4096, 6, 256, FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 4, None) == ERR_SHAPE
+    assert f(FAKE, 4096, 6, 256, FAKE, FAKE, FAKE, FAKE, None, ctypes.c_void_p((1 << 20) + 2), need,
+             None) == ERR_SHAPE
 
 
 def test_encode_validation(lib):
     f = lib.mxfp4_encode
-    assert f(0, None, FAKE, None, 8, 512, 256, FAKE_ALIGNED, None) == ERR_NULL
-    assert f(0, FAKE, FAKE, None, 8, 512, 96, FAKE_ALIGNED, None) == ERR_SHAPE
-    assert f(2, FAKE, FAKE, None, 8, 512, 256, FAKE_ALIGNED, None) == ERR_FORMAT
-    assert f(1, FAKE, FAKE, None, 8, 512, 256, FAKE_ALIGNED, None) == ERR_NULL      # NVFP4 needs tensor scales
-    assert f(0, FAKE, FAKE, FAKE, 8, 512, 256, FAKE_ALIGNED, None) == ERR_FORMAT    # MXFP4 takes none
-    assert f(0, FAKE, FAKE, None, 8, 512, 256, ctypes.c_void_p((1 << 30) + 16), None) == ERR_SHAPE
+    assert f(0, None, FAKE, None, 8, 512, 256, FAKE_ALIGNED, None, None) == ERR_NULL
+    assert f(0, FAKE, FAKE, None, 8, 512, 96, FAKE_ALIGNED, None, None) == ERR_SHAPE
+    assert f(2, FAKE, FAKE, None, 8, 512, 256, FAKE_ALIGNED, None, None) == ERR_FORMAT
+    assert f(1, FAKE, FAKE, None, 8, 512, 256, FAKE_ALIGNED, None, None) == ERR_NULL      # NVFP4 needs tensor scales
+    assert f(0, FAKE, FAKE, FAKE, 8, 512, 256, FAKE_ALIGNED, None, None) == ERR_FORMAT    # MXFP4 takes none
+    assert f(0, FAKE, FAKE, None, 8, 512, 256, ctypes.c_void_p((1 << 30) + 16), None, None) == ERR_SHAPE
 
 
 def test_gmm_validation(lib):
@@ -104,7 +132,7 @@ def test_gmm_validation(lib):
 
 def test_bf16_arm_validation(lib):
     assert lib.moe_packed_weight_bytes(2, 8, 512, 256) == 8 * 512 * 256 * 2
-    assert lib.mxfp4_encode(2, FAKE, FAKE, None, 8, 512, 256, FAKE_ALIGNED, None) == ERR_FORMAT
+    assert lib.mxfp4_encode(2, FAKE, FAKE, None, 8, 512, 256, FAKE_ALIGNED, None, None) == ERR_FORMAT
     assert lib.moe_bf16_encode(None, 8, 512, 256, FAKE_ALIGNED, None) == ERR_NULL
     assert lib.moe_bf16_encode(FAKE, 8, 512, 200, FAKE_ALIGNED, None) == ERR_SHAPE
     assert lib.moe_bf16_encode(FAKE, 8, 512, 256, ctypes.c_void_p((1 << 30) + 16), None) == ERR_SHAPE

@@ -16,7 +16,7 @@ import torch
 import moe_grouped_gemm_route_amd as moe
 import oracle
 from moe_grouped_gemm_route_amd.synth import make_config, make_problem, random_bf16_bits
-from gpu_util import (REL_TOL, bf16_bits_to_f64, bf16_ulp, rel_err, run_gpu, to_dev,
+from gpu_util import (DEV, REL_TOL, bf16_bits_to_f64, bf16_ulp, rel_err, run_gpu, to_dev,
                       weights_for)
 
 pytestmark = pytest.mark.gpu
@@ -24,9 +24,9 @@ pytestmark = pytest.mark.gpu
 KERNELS = [moe.GMM_STREAM, moe.GMM_TILED]
 
 
-def _route_check(ids, E):
+def _route_check(ids, E, ws=None):
     ref = oracle.route_sort(ids, E)
-    got = moe.route_sort(to_dev(ids), E)
+    got = moe.route_sort(to_dev(ids), E, ws=ws)
     torch.cuda.synchronize()
     for key in ("group_offsets", "sorted_token", "sorted_pair", "pair_row"):
         assert np.array_equal(got[key].cpu().numpy(), ref[key]), key
@@ -75,6 +75,46 @@ def test_nvfp4_cast_gpu_matches_oracle():
     assert err.item() == 1
 
 
+def test_nvfp4_cast_experts_with_tiny_kmax():
+    # largest E8M0 byte 5 and an all-zero expert: subnormal tensor scales,
+    # bit for bit as the oracle's cast
+    rng = np.random.default_rng(103)
+    sc = rng.integers(0, 6, size=(3, 16, 8)).astype(np.uint8)
+    sc[0, 0, 0] = 5
+    sc[1] = 0
+    sc[2] = rng.integers(120, 138, size=(16, 8)).astype(np.uint8)
+    bs_ref, ts_ref = oracle.mxfp4_to_nvfp4(sc)
+    bs, ts, err = moe.mxfp4_to_nvfp4(to_dev(sc))
+    assert np.array_equal(bs.cpu().numpy(), bs_ref)
+    assert np.array_equal(ts.cpu().numpy().view(np.uint32), ts_ref.view(np.uint32))
+    assert err.item() == 0
+
+
+def test_encode_counts_scales_outside_exact_domain():
+    # E8M0 bytes 0, 1, 253, 254 and 255 planted in an MXFP4 tensor, E4M3 NaN
+    # bytes and a non-finite tensor scale in an NVFP4 one: each is counted;
+    # in-domain tensors count zero
+    rng = np.random.default_rng(104)
+    E, N, K = 2, 64, 256
+    codes = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    scales = rng.integers(2, 253, size=(E, N, K // 32)).astype(np.uint8)
+    err = torch.full((1,), 77, dtype=torch.int32, device=DEV)
+    moe.mxfp4_encode(to_dev(codes), to_dev(scales), None, moe.MXFP4, err_count=err)
+    assert err.item() == 0
+    bad = scales.copy()
+    bad[0, 0, 0], bad[0, 5, 3], bad[1, 63, 7], bad[1, 9, 2], bad[0, 40, 6] = 0, 1, 253, 254, 255
+    moe.mxfp4_encode(to_dev(codes), to_dev(bad), None, moe.MXFP4, err_count=err)
+    assert err.item() == 5
+    bs = rng.integers(0, 0x7F, size=(E, N, K // 16)).astype(np.uint8)
+    ts = np.array([1.0, 0.25], dtype=np.float32)
+    moe.mxfp4_encode(to_dev(codes), to_dev(bs), to_dev(ts), moe.NVFP4, err_count=err)
+    assert err.item() == 0
+    bs[1, 2, 3], bs[0, 7, 15] = 0x7F, 0xFF
+    ts[1] = np.inf
+    moe.mxfp4_encode(to_dev(codes), to_dev(bs), to_dev(ts), moe.NVFP4, err_count=err)
+    assert err.item() == 3
+
+
 # ------------------------------------------------------------ route sort ---
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
@@ -94,6 +134,40 @@ def test_route_sort_edge_cases():
     _route_check(ids, 256)
     _route_check(rng.integers(0, 1024, size=(3000, 8)).astype(np.int32), 1024)
     _route_check(rng.integers(0, 3, size=(5000, 1)).astype(np.int32), 3)
+
+
+def test_route_sort_unit_boundaries():
+    # around the one-workgroup limit (4,096 pairs) and the segments of the
+    # two-kernel path: a ragged last segment of one pair, segments of 4,608
+    # pairs (262,145 pairs: sub-segments of 576 pairs, two id batches per
+    # wave), 1,024 experts (two per scan thread), more than 32 segments (two
+    # batches of count-table rows), one expert, and dropped ids spread over
+    # the segments
+    rng = np.random.default_rng(9)
+    for M, E in [(4096, 256), (4097, 256), (4097, 1), (8191, 7), (24576, 256), (262145, 1024),
+                 (262145, 600)]:
+        ids = rng.integers(0, E, size=(M, 1), dtype=np.int32)
+        _route_check(ids, E)
+        bad = ids.copy()
+        bad[rng.random(bad.shape) < 0.1] = E + 3
+        bad[rng.random(bad.shape) < 0.05] = -1
+        _route_check(bad, E)
+    _route_check(np.full((6000, 4), 9, dtype=np.int32), 16)                # one band
+    _route_check(np.full((6000, 4), 99, dtype=np.int32), 16)               # every pair dropped
+
+
+def test_route_sort_workspace_needs_no_clearing():
+    # the count table is written in full before it is read: a workspace full
+    # of stale values, passed explicitly and reused, gives the same result
+    rng = np.random.default_rng(10)
+    ids = rng.integers(0, 256, size=(4096, 6), dtype=np.int32)
+    need = moe.route_sort_workspace_bytes(4096, 6, 256)
+    assert need == 24 * 256 * 4
+    ws = torch.randint(-2 ** 31, 2 ** 31 - 1, (need // 4,), dtype=torch.int32, device=DEV)
+    _route_check(ids, 256, ws=ws)
+    _route_check(rng.integers(0, 256, size=(1000, 6), dtype=np.int32), 256, ws=ws)
+    with pytest.raises(moe.MoeGmmError):
+        moe.route_sort(to_dev(ids), 256, ws=ws[:-1])
 
 
 def test_route_sort_max_pairs():

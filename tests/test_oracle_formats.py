@@ -132,6 +132,22 @@ def test_nvfp4_cast_rejects_out_of_range_blocks_and_nan():
         F.mxfp4_to_nvfp4(np.array([[[255]]], dtype=np.uint8))
 
 
+def test_nvfp4_cast_experts_with_tiny_kmax():
+    # an expert whose largest E8M0 byte is 5 (k_max = -122) and an all-zero
+    # expert (k_max = -127): the tensor scales 2^-130 and 2^-135 are float32
+    # subnormals with the single mantissa bit 19 and 14, the block scales stay
+    # 2^8 at k_max, and the cast stays lossless in float64
+    sc = np.array([[[5, 3, 0, 5]], [[0, 0, 0, 0]]], dtype=np.uint8)
+    bs, ts = F.mxfp4_to_nvfp4(sc)
+    assert ts.view(np.uint32).tolist() == [1 << 19, 1 << 14]
+    assert bs[1].reshape(-1).tolist() == [0x78] * 8                 # 2^8 = E4M3 exponent field 15
+    assert bs[0].reshape(-1).tolist() == [0x78, 0x78, 0x68, 0x68, 0x50, 0x50, 0x78, 0x78]
+    codes = np.arange(64, dtype=np.uint8).reshape(2, 1, 32) * 3
+    a = F.decode_mxfp4(codes.repeat(2, axis=2)[:, :, :64], sc)
+    b = F.decode_nvfp4(codes.repeat(2, axis=2)[:, :, :64], bs, ts)
+    assert np.array_equal(a, b)
+
+
 def test_decode_mxfp4_scale_blocks_run_along_k():
     codes = np.full((1, 2, 32), 0x22, dtype=np.uint8)       # every weight 1.0
     scales = np.array([[[127, 128], [126, 130]]], dtype=np.uint8)
