@@ -109,6 +109,29 @@ int moe_route_sort(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                    void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_route_sort_noalloc - moe_route_sort for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.
+ *
+ * Same arguments, results and errors as moe_route_sort without ws/ws_bytes.
+ * The count table lives in a library-owned array of 256 KiB per GPU (the
+ * largest moe_route_sort_workspace_bytes of any accepted size), resolved on
+ * the first call on each device and held until the process ends; the call
+ * allocates nothing.  It uses the array of the current device, which must be
+ * the device of `stream`.  Every call on one GPU shares that GPU's array:
+ * calls that may overlap on one GPU (on different streams, or from several
+ * host threads without ordering) race on it and must be serialised by the
+ * caller.  The table is written in full before it is read, so nothing needs
+ * clearing between calls.  A size needing more than the array returns
+ * MOE_ERR_SHAPE (none of the accepted sizes does); a failure to resolve the
+ * array returns MOE_ERR_HIP.
+ */
+int moe_route_sort_noalloc(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                           int32_t* group_offsets, int32_t* sorted_token,
+                           int32_t* sorted_pair, int32_t* pair_row, int32_t* err_count,
+                           void* stream);
+
+/*
  * moe_packed_weight_bytes - size in bytes of the packed buffer that
  * mxfp4_encode writes for E experts of an [N, K] weight (0 on bad sizes).
  * Codes stay 4 bits per weight; scales stay one byte per block (padded to

@@ -33,6 +33,7 @@ _SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_route_sort_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "moe_route_sort": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_route_sort_noalloc": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_packed_weight_bytes": (_sz, [ctypes.c_int, _i32, _i32, _i32]),
     "mxfp4_encode": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "moe_bf16_encode": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp]),

@@ -78,6 +78,24 @@ int moe_route_sort(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                                            static_cast<hipStream_t>(stream)));
 }
 
+int moe_route_sort_noalloc(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                           int32_t* group_offsets, int32_t* sorted_token, int32_t* sorted_pair,
+                           int32_t* pair_row, int32_t* err_count, void* stream) {
+  if (!topk_ids || !group_offsets || !sorted_token || !sorted_pair || !pair_row) return MOE_ERR_NULL;
+  const int st = route_sort_shape(T, k, E);
+  if (st != MOE_OK) return st;
+  const size_t need = moe::route_plan((int64_t)T * k, E).ws_bytes;
+  int32_t* ws = nullptr;
+  if (need > 0) {
+    size_t have = 0;
+    if (moe::route_sort_scratch(&ws, &have) != hipSuccess) return MOE_ERR_HIP;
+    if (need > have) return MOE_ERR_SHAPE;
+  }
+  return hip_status(moe::launch_route_sort(topk_ids, T, k, E, group_offsets, sorted_token,
+                                           sorted_pair, pair_row, err_count, ws,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 size_t moe_packed_weight_bytes(int fmt, int32_t E, int32_t N, int32_t K) {
   if (check_weight_shape(fmt, E, N, K) != MOE_OK) return 0;
   return (size_t)moe::make_layout(fmt, E, N, K).total_bytes;

@@ -17,6 +17,10 @@ struct RoutePlan {
 };
 RoutePlan route_plan(int64_t M, int32_t E);
 
+// Device address and size of the current device's route-sort count table
+// (the no-allocation entry point's scratch array).
+hipError_t route_sort_scratch(int32_t** ptr, size_t* bytes);
+
 hipError_t launch_route_sort(const int32_t* ids, int32_t T, int32_t k, int32_t E,
                              int32_t* group_offsets, int32_t* sorted_token, int32_t* sorted_pair,
                              int32_t* pair_row, int32_t* err_count, int32_t* ws, hipStream_t stream);

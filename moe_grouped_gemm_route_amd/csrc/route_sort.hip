@@ -24,6 +24,8 @@
 //          lowest such lane advances the cursor.
 // Up to RS_FUSED_MAX pairs one workgroup does all of it with every id held in
 // registers and no workspace.  No atomic decides a position.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -338,6 +340,35 @@ static void launch_route_t(const RoutePlan& pl, const int32_t* ids, int32_t M, i
   hipLaunchKernelGGL(route_count_kernel, dim3(pl.G), dim3(RS_THREADS), lds, stream, ids, M, E, pl.S, ws);
   hipLaunchKernelGGL(route_place_kernel<PER>, dim3(pl.G), dim3(RS_THREADS), lds, stream, ids, M, k, E, bits, pl.S,
                      pl.G, ws, group_offsets, sorted_token, sorted_pair, pair_row, err_count);
+}
+
+// Count table of moe_route_sort_noalloc: one per GPU, for the life of the
+// process.  The largest table any accepted size needs is RS_MAX_SEGMENTS x
+// 1024 experts of int32 (256 KiB).  In host code `scratch` names a host-side
+// stand-in, never the device memory: kernels get the address that
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t RS_SCRATCH_BYTES = (size_t)RS_MAX_SEGMENTS * 1024 * sizeof(int32_t);
+static __device__ __align__(256) int32_t scratch[RS_SCRATCH_BYTES / sizeof(int32_t)];
+
+hipError_t route_sort_scratch(int32_t** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int32_t* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    // resolved once per device, with that device current
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    addr[dev] = static_cast<int32_t*>(p);
+  }
+  *ptr = addr[dev];
+  *bytes = RS_SCRATCH_BYTES;
+  return hipSuccess;
 }
 
 hipError_t launch_route_sort(const int32_t* ids, int32_t T, int32_t k, int32_t E,

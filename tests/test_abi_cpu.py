@@ -211,3 +211,12 @@ def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(moe.MoeGmmError):
         moe.route_sort(torch.zeros((4, 2), dtype=torch.int32), 8)
+
+
+def test_route_sort_noalloc_validation(lib):
+    f = lib.moe_route_sort_noalloc
+    assert f(None, 4, 2, 8, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_NULL
+    assert f(FAKE, 4, 2, 8, FAKE, None, FAKE, FAKE, None, None) == ERR_NULL
+    assert f(FAKE, 0, 2, 8, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert f(FAKE, 4, 2, 1025, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert f(FAKE, 1 << 22, 8, 8, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
