@@ -1,6 +1,7 @@
 """Benchmark of the routed-expert W4A16 grouped matmul on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--tokens T] [--kernel auto|stream|tiled] [--only]
 
 A step is one pass of the hot path over one batch of synthetic input with the
 expert weights already packed and resident in HBM (the one-time load-time
@@ -8,27 +9,39 @@ repack is excluded, as the grouped-matmul timings of "Running DeepSeek V4
 Flash on TPU v6", section "Grouped matmul performance vs bf16", exclude it):
   route-sort of the top-k ids -> grouped matmul (-> top-k combine for the
   down-projection workload, whose router weights are given).
+
 The default workload is the gate/up (w13) decode: 64 tokens, hidden 4096,
 256 experts, top-6 uniform routing, fused gate+up weight K = N = 4096 in
-MXFP4, bf16 output.  The layer_decode workload runs one whole routed-expert
-layer on the same tokens: route-sort -> w13 with the SiLU-gated gate/up
-activation fused (bf16 [384, 2048]) -> w2 (K = 2048, N = 4096, f32) ->
-top-k combine; layer_prefill runs the same layer on config 4's 4,096
-tokens (both matmuls on the LDS-tiled kernel), and w4a4_layer_prefill runs it
-W4A4 (x and the activation h quantized to MXFP4 inside the step).  The bf16_w13_decode, bf16_w2_decode and bf16_w13_prefill
-workloads time the bf16-weight comparison arm on the decoded weights of
-configs 2, 3 and 4 (the same values, four times the bytes) next to the MXFP4
-kernel on the same inputs, and report the MXFP4 speedup.  The w4a4_w13_prefill workload runs
-the 4,096-token w13 prefill W4A4: the activations are quantized to MXFP4
-inside the step and the matmul runs on the scaled FP4 matrix instructions.
+MXFP4, bf16 output.  Its line is the headline, timed over exactly --steps
+steps.  Unless --only is given, the default run then times every other
+benchmark workload (fewer steps each, and a shorter CPU-baseline sample) and
+reports them in the same line under "workloads": tiny (64 tokens, 8 experts),
+w2_decode (256 tokens, Zipf routing, K = 2048, with the combine), w13_prefill
+(4,096 tokens), nvfp4_w13 (256 tokens, NVFP4 weights from the lossless cast),
+and the whole routed-expert layer at decode and at prefill.
 
-One JSON line is printed.  value is the whole step's throughput in the
-algorithmic bytes of the matmul (codes + scales of the experts that received
-tokens, plus the activations read) per second; roofline.achieved is the same
-bytes over the grouped-matmul kernel's own average duration, timed with HIP
-events on the stream it runs on (gmm_us; the median and minimum are reported
-beside it).  The CPU baseline times the float64 oracle on a bounded sample of
-the same workload on the host cores; gpu_over_cpu is value over its value.
+Other workloads, run alone with --workload:
+  layer_decode / layer_prefill: route-sort -> w13 with the SiLU-gated gate/up
+    activation fused (bf16 [M, 2048]) -> w2 (K = 2048, N = 4096, f32) ->
+    top-k combine, on config 2's 64 or config 4's 4,096 tokens;
+  w4a4_layer_prefill: the same layer W4A4 (x and h quantized to MXFP4 inside
+    the step), w4a4_w13_prefill: the 4,096-token w13 W4A4;
+  bf16_w13_decode, bf16_w2_decode, bf16_w13_prefill: the bf16-weight
+    comparison arm on the decoded weights of configs 2, 3 and 4 (the same
+    values, four times the bytes) next to the MXFP4 kernel on the same inputs.
+--tokens T replaces a workload's token count (the weights stay the config's;
+x and the routing are redrawn the same way), for the kernel-choice sweep.
+
+value is the whole step's throughput: the algorithmic bytes of the matmul
+(codes + scales of the experts that received tokens, plus the activations
+read) per second for HBM-bound shapes, 2 M K N FLOP per second for the
+MFMA-bound prefill.  roofline.achieved is the same quantity over the
+grouped-matmul kernel's own average duration, timed with HIP events on the
+stream it runs on (gmm_us; median and minimum beside it).  hbm_calibration
+and mfma_calibration report the read rate and the matrix-unit rate this part
+sustains on plain loops, with the kernel's fraction of them.  The CPU
+baseline times the float64 oracle on a bounded sample of the same workload on
+the host cores; gpu_over_cpu is value over its value.
 """
 
 import argparse
@@ -46,12 +59,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 MFMA, published
+METRIC = "moe_gmm TFLOP/s and HBM GB/s (% roofline), w13/w2, 256 experts top-6"
 
-WORKLOADS = {
+GMM_WORKLOADS = {
     "tiny": 1, "w13_decode": 2, "w2_decode": 3, "w13_prefill": 4, "nvfp4_w13": 5,
-    "layer_decode": 0, "layer_prefill": 0, "w4a4_layer_prefill": 0, "bf16_w13_decode": 2, "bf16_w2_decode": 3, "bf16_w13_prefill": 4,
-    "w4a4_w13_prefill": 4,
+    "bf16_w13_decode": 2, "bf16_w2_decode": 3, "bf16_w13_prefill": 4,
 }
+LAYER_WORKLOADS = ("layer_decode", "layer_prefill", "w4a4_layer_prefill")
+WORKLOADS = sorted(list(GMM_WORKLOADS) + list(LAYER_WORKLOADS) + ["w4a4_w13_prefill"])
+# timed after the headline in the default run
+EXTRA_WORKLOADS = ("tiny", "w2_decode", "w13_prefill", "nvfp4_w13", "layer_decode", "layer_prefill")
 KERNELS = {"auto": 0, "stream": 1, "tiled": 2}
 GMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_route_amd", "csrc", "gmm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
@@ -74,16 +91,45 @@ def algorithmic_bytes(p, fmt):
     return w_bytes + x_rows * p["K"] * 2, active
 
 
+def roofline(nbytes, flops, kernel_s, peak_tflops=BF16_PEAK_TFLOPS):
+    """The roof whose time at peak is the longer one (the matrix unit for the
+    MXFP4 prefill, HBM for decode shapes and bf16 weights), and the kernel's
+    achieved rate against it."""
+    peak_flops = peak_tflops * 1e12
+    if flops / peak_flops > nbytes / (HBM_PEAK_GBS * 1e9):
+        achieved = flops / kernel_s / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_tflops,
+                "unit": "TFLOP/s", "frac": round(achieved / peak_tflops, 4)}
+    achieved = nbytes / kernel_s / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(p, fmt, unit, target_s=15.0):
     """The float64 oracle on the host: route-sort of the whole batch, then the
     grouped matmul of as many expert bands (in expert order) as fit in about
-    target_s seconds.  Reported as the same algorithmic bytes per second."""
+    target_s seconds.  Reported as the same algorithmic bytes (or FLOPs) per
+    second."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = _threads()
     if fmt == "nvfp4":
         bs, ts = oracle.mxfp4_to_nvfp4(p["scales"])
         w = {"fmt": "nvfp4", "codes": p["codes"], "block_scales": bs, "tensor_scale": ts}
@@ -127,27 +173,13 @@ def cpu_baseline(p, fmt, unit, target_s=15.0):
     }
 
 
-def cpu_model():
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return "unknown CPU"
-
-
 def layer_cpu_baseline(p, unit="GB/s", target_s=15.0):
     """The float64 oracle for one layer on the host: route-sort, then for as
     many active experts (in expert order) as fit in about target_s seconds,
     the w13 band matmul, the gate/up activation and the w2 band matmul."""
     import oracle
     from moe_grouped_gemm_route_amd.synth import f32_to_bf16_bits
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = _threads()
     t0 = time.perf_counter()
     r = oracle.route_sort(p["topk_ids"], p["E"])
     off = r["group_offsets"]
@@ -180,49 +212,212 @@ def layer_cpu_baseline(p, unit="GB/s", target_s=15.0):
     }
 
 
-def route_workspace(T, k, E, dev):
-    """The route sort's device workspace, allocated once outside the timed
-    steps (None when the sort needs none)."""
-    import torch
-    import moe_grouped_gemm_route_amd as moe
-    need = moe.route_sort_workspace_bytes(T, k, E)
-    return torch.empty((need + 3) // 4, dtype=torch.int32, device=dev) if need else None
+def recorded_traffic(workload):
+    """HBM bytes per launch of the workload's matmul kernel from the committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, calibrated on a copy kernel),
+    or None when there is none or the kernel source has changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        entry = json.load(open(TRAFFIC_FILE)).get(workload, {})
+    except (OSError, ValueError):
+        return None
+    if entry.get("gmm_source_sha256_16") != gmm_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
 
 
-def run_layer(args):
-    """One routed-expert layer (the layer_decode and layer_prefill workloads)."""
-    import torch
-    import moe_grouped_gemm_route_amd as moe
+# ---------------------------------------------------------------- GPU side --
+
+class Gpu:
+    """torch, the binding and device 0, imported on first use."""
+
+    def __init__(self):
+        import torch
+        import moe_grouped_gemm_route_amd as moe
+        self.torch, self.moe = torch, moe
+        self.dev = torch.device("cuda", 0)
+        torch.cuda.set_device(self.dev)
+
+    def put(self, a):
+        a = np.ascontiguousarray(a)
+        return self.torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(self.dev)
+
+    def route_workspace(self, T, k, E):
+        """The route sort's device workspace, allocated once outside the
+        timed steps (None when the sort needs none)."""
+        need = self.moe.route_sort_workspace_bytes(T, k, E)
+        return self.torch.empty((need + 3) // 4, dtype=self.torch.int32, device=self.dev) if need else None
+
+    def event(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def timed_steps(self, step, steps, warmup):
+        """warmup untimed steps, then exactly `steps` steps between two
+        device synchronisations; step(timed) returns its kernel events or
+        None.  Returns (wall seconds, list of event tuples)."""
+        for _ in range(warmup):
+            step(False)
+        self.torch.cuda.synchronize()
+        ev = []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            ev.append(step(True))
+        self.torch.cuda.synchronize()
+        return time.perf_counter() - t0, ev
+
+
+def base_line(workload, steps, warmup, step_s, value, unit, dtype, config):
+    cfg = {"workload": workload}
+    cfg.update(config)
+    return {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic", "config": cfg,
+    }
+
+
+def run_gmm(gpu, workload, steps, warmup, cpu_s, kernel="auto", out_dtype=None, tokens=None):
+    """One grouped-matmul workload: route_sort + moe_gmm (+ moe_combine for
+    the down projection) per step."""
+    torch, moe = gpu.torch, gpu.moe
+    from moe_grouped_gemm_route_amd.synth import make_config, make_tokens_problem
+
+    cfg = GMM_WORKLOADS[workload]
+    p = make_config(cfg) if tokens is None else make_tokens_problem(cfg, tokens)
+    bf16_arm = workload.startswith("bf16_")
+    fmt = "nvfp4" if cfg == 5 else "mxfp4"
+    out_dtype = out_dtype or p["out"]
+    odt = moe.BF16 if out_dtype == "bf16" else moe.F32
+    E, K, N, T, k = p["E"], p["K"], p["N"], p["T"], p["k"]
+    M = T * k
+
+    ids, x = gpu.put(p["topk_ids"]), gpu.put(p["x"])
+    codes = gpu.put(p["codes"])
+    if fmt == "mxfp4":
+        packed = moe.mxfp4_encode(codes, gpu.put(p["scales"]), None, moe.MXFP4)
+        wf = moe.MXFP4
+    else:
+        bs, ts, err = moe.mxfp4_to_nvfp4(gpu.put(p["scales"]))
+        packed = moe.mxfp4_encode(codes, bs, ts, moe.NVFP4)
+        wf = moe.NVFP4
+        assert err.item() == 0
+    del codes
+    packed_mx = None
+    if bf16_arm:
+        # the comparison arm streams the decoded weights as bf16
+        dense = moe.debug_decode(packed, wf, E, N, K)
+        packed_mx, packed = packed, moe.bf16_encode(dense)
+        del dense
+        fmt, wf = "bf16", moe.W_BF16
+    tw = gpu.put(p["topk_weights"])
+    combine = cfg == 3
+    y = torch.empty((M, N), dtype=torch.bfloat16 if odt == moe.BF16 else torch.float32, device=gpu.dev)
+    kern = KERNELS[kernel]
+    ws = gpu.route_workspace(T, k, E)
+    torch.cuda.synchronize()
+
+    def gmm(pk, f, r):
+        moe.moe_gmm(pk, f, E, N, K, x, r["group_offsets"], M,
+                    row_index=r["sorted_token"] if p["gather"] else None,
+                    out_dtype=odt, kernel=kern, out=y)
+
+    def step(timed):
+        r = moe.route_sort(ids, E, ws=ws)
+        e = (gpu.event(), gpu.event()) if timed else None
+        if timed:
+            e[0].record()
+        gmm(packed, wf, r)
+        if timed:
+            e[1].record()
+        if combine:
+            moe.moe_combine(y, tw, r["pair_row"])
+        return e
+
+    wall, ev = gpu.timed_steps(step, steps, warmup)
+
+    mx_ms = None
+    if bf16_arm:
+        # the MXFP4 kernel on the same inputs, for the speedup
+        r = moe.route_sort(ids, E, ws=ws)
+        for _ in range(warmup):
+            gmm(packed_mx, moe.MXFP4, r)
+        e = [gpu.event() for _ in range(steps + 1)]
+        e[0].record()
+        for i in range(steps):
+            gmm(packed_mx, moe.MXFP4, r)
+            e[i + 1].record()
+        torch.cuda.synchronize()
+        mx_ms = [e[i].elapsed_time(e[i + 1]) for i in range(steps)]
+
+    gmm_ms = [a.elapsed_time(b) for a, b in ev]
+    gmm_s = float(np.mean(gmm_ms)) / 1e3
+    nbytes, active = algorithmic_bytes(p, fmt)
+    flops = 2.0 * M * K * N
+    step_s = wall / steps
+    roof = roofline(nbytes, flops, gmm_s)
+    roof["traffic"] = recorded_traffic(workload) if tokens is None else None
+    if roof["bound"] == "mfma":
+        value, unit = flops / step_s / 1e12, "TFLOP/s"
+    else:
+        value, unit = nbytes / step_s / 1e9, "GB/s"
+    config = {"tokens": T, "top_k": k, "experts": E, "K": K, "N": N, "routed_rows": M,
+              "weights": fmt + (" (decoded MXFP4 weights)" if bf16_arm else ""),
+              "activations": "bf16", "output": out_dtype, "kernel": kernel,
+              "step": "route_sort + moe_gmm" + (" + moe_combine" if combine else "")}
+    out = base_line(workload, steps, warmup, step_s, value, unit, "bf16", config)
+    out.update({
+        "gmm_us": round(gmm_s * 1e6, 2),
+        "gmm_us_median": round(float(np.median(gmm_ms)) * 1e3, 2),
+        "gmm_us_min": round(float(np.min(gmm_ms)) * 1e3, 2),
+        "gmm_tflops": round(flops / gmm_s / 1e12, 2),
+        "gmm_gbs": round(nbytes / gmm_s / 1e9, 1),
+        "active_experts": active,
+        "algorithmic_bytes": int(nbytes),
+        # + the output written and the index arrays read (band offsets, row index)
+        "algorithmic_bytes_all": int(nbytes + M * N * (2 if odt == moe.BF16 else 4)
+                                     + 4 * (E + 1) + (4 * M if p["gather"] else 0)),
+        "roofline": roof,
+    })
+    if roof["bound"] == "mfma":
+        out["mfma_calibration"] = mfma_calibration(gpu, roof["achieved"])
+    if mx_ms is not None:
+        mx_s = float(np.mean(mx_ms)) / 1e3
+        out["mxfp4_us"] = round(mx_s * 1e6, 2)
+        out["mxfp4_speedup_over_bf16"] = round(gmm_s / mx_s, 3)
+    if cpu_s > 0:
+        out["cpu_baseline"] = cpu_baseline(p, "mxfp4" if bf16_arm else fmt, unit, target_s=cpu_s)
+        out["gpu_over_cpu"] = round(value / out["cpu_baseline"]["value"], 1)
+    return out
+
+
+def run_layer(gpu, workload, steps, warmup, cpu_s):
+    """One routed-expert layer (layer_decode, layer_prefill and its W4A4
+    form)."""
+    torch, moe = gpu.torch, gpu.moe
     from moe_grouped_gemm_route_amd.synth import make_layer_decode, make_layer_prefill
 
-    prefill = args.workload in ("layer_prefill", "w4a4_layer_prefill")
-    w4a4 = args.workload == "w4a4_layer_prefill"
+    prefill = workload in ("layer_prefill", "w4a4_layer_prefill")
+    w4a4 = workload == "w4a4_layer_prefill"
     p = make_layer_prefill() if prefill else make_layer_decode()
     E, K, N, T, k = p["E"], p["K"], p["N"], p["T"], p["k"]
     M, H = T * k, N // 2
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-
-    def d(a):
-        a = np.ascontiguousarray(a)
-        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
-
-    ids, x, tw = d(p["topk_ids"]), d(p["x"]), d(p["topk_weights"])
-    codes = d(p["codes"])
-    w13 = moe.mxfp4_encode(codes, d(p["scales"]), None, moe.MXFP4)
+    ids, x, tw = gpu.put(p["topk_ids"]), gpu.put(p["x"]), gpu.put(p["topk_weights"])
+    codes = gpu.put(p["codes"])
+    w13 = moe.mxfp4_encode(codes, gpu.put(p["scales"]), None, moe.MXFP4)
     del codes
-    codes = d(p["w2_codes"])
-    w2 = moe.mxfp4_encode(codes, d(p["w2_scales"]), None, moe.MXFP4)
+    codes = gpu.put(p["w2_codes"])
+    w2 = moe.mxfp4_encode(codes, gpu.put(p["w2_scales"]), None, moe.MXFP4)
     del codes
-    h = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
-    y2 = torch.empty((M, K), dtype=torch.float32, device=dev)
-    ws = route_workspace(T, k, E, dev)
+    h = torch.empty((M, H), dtype=torch.bfloat16, device=gpu.dev)
+    y2 = torch.empty((M, K), dtype=torch.float32, device=gpu.dev)
+    ws = gpu.route_workspace(T, k, E)
     torch.cuda.synchronize()
-    ev = []
 
     def step(timed):
         # events around each matmul kernel (the W4A4 quantizations fall between)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
+        e = [gpu.event() for _ in range(4)] if timed else None
         r = moe.route_sort(ids, E, ws=ws)
         if w4a4:
             qc, qs = moe.mxfp4_quantize(x)
@@ -247,107 +442,131 @@ def run_layer(args):
             moe.moe_gmm(w2, moe.MXFP4, E, K, H, h, r["group_offsets"], M, out_dtype=moe.F32, out=y2)
         if timed:
             e[3].record()
-            ev.append(e)
-        return moe.moe_combine(y2, tw, r["pair_row"])
+        moe.moe_combine(y2, tw, r["pair_row"])
+        return e
 
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
+    wall, ev = gpu.timed_steps(step, steps, warmup)
     t13 = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) / 1e3
     t2 = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) / 1e3
     counts = np.bincount(p["topk_ids"].reshape(-1), minlength=E)
     active = int(np.count_nonzero(counts))
-    b13 = active * N * K * (0.5 + 1.0 / 32) + T * K * 2
-    b2 = active * K * H * (0.5 + 1.0 / 32) + M * H * 2
-    step_s = wall / args.steps
-    flops = 2.0 * M * K * (N + H)
     if w4a4:
         # quantized activations: K/2 + K/32 bytes per row instead of 2K
         b13 = active * N * K * (0.5 + 1.0 / 32) + T * (K // 2 + K // 32)
         b2 = active * K * H * (0.5 + 1.0 / 32) + M * (H // 2 + H // 32)
-    # matrix-unit bound when its roof time is the longer one (bf16 prefill)
-    peak_flops = (FP4_PEAK_TFLOPS if w4a4 else BF16_PEAK_TFLOPS) * 1e12
-    mfma_bound = flops / peak_flops > (b13 + b2) / (HBM_PEAK_GBS * 1e9)
-    if mfma_bound:
-        achieved = flops / (t13 + t2) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        b13 = active * N * K * (0.5 + 1.0 / 32) + T * K * 2
+        b2 = active * K * H * (0.5 + 1.0 / 32) + M * H * 2
+    step_s = wall / steps
+    flops = 2.0 * M * K * (N + H)
+    roof = roofline(b13 + b2, flops, t13 + t2, FP4_PEAK_TFLOPS if w4a4 else BF16_PEAK_TFLOPS)
+    roof["traffic"] = None
+    if w4a4:
+        roof["fp4_mfma_frac"] = round(flops / (t13 + t2) / (FP4_PEAK_TFLOPS * 1e12), 4)
+    if roof["bound"] == "mfma" or prefill:
         value, unit = flops / step_s / 1e12, "TFLOP/s"
     else:
-        achieved = (b13 + b2) / (t13 + t2) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
         value, unit = (b13 + b2) / step_s / 1e9, "GB/s"
-        if prefill:
-            value, unit = flops / step_s / 1e12, "TFLOP/s"
-    if w4a4:
-        roof["fp4_mfma_frac"] = round(flops / (t13 + t2) / peak_flops, 4)
-    calib = mfma_calibration(roof["achieved"]) if mfma_bound else None
-    out = {
-        "metric": "moe_gmm TFLOP/s and HBM GB/s (% roofline), w13/w2, 256 experts top-6",
-        "value": round(value, 2),
-        "unit": unit,
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_s * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp4" if w4a4 else "bf16",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": T, "top_k": k, "experts": E,
-                   "w13": [K, N], "w2": [H, K], "routed_rows": M, "weights": "mxfp4",
-                   "activations": "mxfp4 (quantized in the step)" if w4a4 else "bf16",
-                   "gate_up": "silu(gate) * up fused into the w13 epilogue",
-                   "step": ("route_sort + mxfp4_quantize(x) + moe_gmm_w4a4(w13, act) + mxfp4_quantize(h) "
-                            "+ moe_gmm_w4a4(w2) + moe_combine") if w4a4 else
-                           "route_sort + moe_gmm(w13, act) + moe_gmm(w2) + moe_combine"},
+    config = {"tokens": T, "top_k": k, "experts": E, "w13": [K, N], "w2": [H, K], "routed_rows": M,
+              "weights": "mxfp4", "activations": "mxfp4 (quantized in the step)" if w4a4 else "bf16",
+              "gate_up": "silu(gate) * up fused into the w13 epilogue",
+              "step": ("route_sort + mxfp4_quantize(x) + moe_gmm_w4a4(w13, act) + mxfp4_quantize(h) "
+                       "+ moe_gmm_w4a4(w2) + moe_combine") if w4a4 else
+                      "route_sort + moe_gmm(w13, act) + moe_gmm(w2) + moe_combine"}
+    out = base_line(workload, steps, warmup, step_s, value, unit, "fp4" if w4a4 else "bf16", config)
+    out.update({
         "w13_us": round(t13 * 1e6, 2),
         "w2_us": round(t2 * 1e6, 2),
         "active_experts": active,
         "algorithmic_bytes": int(b13 + b2),
         "layer_tflops": round(flops / (t13 + t2) / 1e12, 2),
         "roofline": roof,
-    }
-    if calib is not None:
-        out["mfma_calibration"] = calib
-    if not args.no_cpu_baseline and not w4a4:
-        out["cpu_baseline"] = layer_cpu_baseline(p, unit)
+    })
+    if roof["bound"] == "mfma" and not w4a4:
+        out["mfma_calibration"] = mfma_calibration(gpu, roof["achieved"])
+    if cpu_s > 0 and not w4a4:
+        out["cpu_baseline"] = layer_cpu_baseline(p, unit, target_s=cpu_s)
         out["gpu_over_cpu"] = round(out["value"] / out["cpu_baseline"]["value"], 1)
-    print(json.dumps(out), flush=True)
+    return out
+
+
+def run_w4a4(gpu, steps, warmup):
+    """The W4A4 prefill workload: route-sort, MXFP4 activation quantization and
+    the grouped matmul on the scaled FP4 MFMA, over config 4's problem."""
+    torch, moe = gpu.torch, gpu.moe
+    from moe_grouped_gemm_route_amd.synth import make_config
+
+    p = make_config(4)
+    E, K, N, T, k = p["E"], p["K"], p["N"], p["T"], p["k"]
+    M = T * k
+    ids, x = gpu.put(p["topk_ids"]), gpu.put(p["x"])
+    codes = gpu.put(p["codes"])
+    packed = moe.mxfp4_encode(codes, gpu.put(p["scales"]), None, moe.MXFP4)
+    del codes
+    y = torch.empty((M, N), dtype=torch.float32, device=gpu.dev)
+    ws = gpu.route_workspace(T, k, E)
+    torch.cuda.synchronize()
+
+    def step(timed):
+        r = moe.route_sort(ids, E, ws=ws)
+        qc, qs = moe.mxfp4_quantize(x)
+        e = (gpu.event(), gpu.event()) if timed else None
+        if timed:
+            e[0].record()
+        moe.moe_gmm_w4a4(packed, E, N, K, qc, qs, r["group_offsets"], M, row_index=r["sorted_token"], out=y)
+        if timed:
+            e[1].record()
+        return e
+
+    wall, ev = gpu.timed_steps(step, steps, warmup)
+    gmm_ms = [a.elapsed_time(b) for a, b in ev]
+    gmm_s = float(np.mean(gmm_ms)) / 1e3
+    flops = 2.0 * M * K * N
+    counts = np.bincount(p["topk_ids"].reshape(-1), minlength=E)
+    active = int(np.count_nonzero(counts))
+    nbytes = active * N * K * (0.5 + 1.0 / 32) + T * (K // 2 + K // 32)
+    step_s = wall / steps
+    roof = roofline(nbytes, flops, gmm_s, FP4_PEAK_TFLOPS)
+    roof["traffic"] = recorded_traffic("w4a4_w13_prefill")
+    roof["fp4_mfma_frac"] = round(flops / gmm_s / 1e12 / FP4_PEAK_TFLOPS, 4)
+    config = {"tokens": T, "top_k": k, "experts": E, "K": K, "N": N, "routed_rows": M, "weights": "mxfp4",
+              "activations": "mxfp4 (quantized in the step)", "output": "f32",
+              "step": "route_sort + mxfp4_quantize + moe_gmm_w4a4"}
+    out = base_line("w4a4_w13_prefill", steps, warmup, step_s, flops / step_s / 1e12, "TFLOP/s", "fp4", config)
+    out.update({
+        "gmm_us": round(gmm_s * 1e6, 2),
+        "gmm_us_median": round(float(np.median(gmm_ms)) * 1e3, 2),
+        "gmm_us_min": round(float(np.min(gmm_ms)) * 1e3, 2),
+        "gmm_tflops": round(flops / gmm_s / 1e12, 2),
+        "active_experts": active,
+        "algorithmic_bytes": int(nbytes),
+        "roofline": roof,
+    })
+    return out
 
 
 CALIB_BLOCKS, CALIB_ITERS = 512, 12800     # two workgroups per CU, about 25 ms per launch
+HBM_CALIB_BYTES, HBM_CALIB_BLOCKS = 2 << 30, 1536   # regions of 341 KiB per wave: not a power of two
 
 
-def mfma_calibration(achieved_tflops):
+def mfma_calibration(gpu, achieved_tflops):
     """The bf16 matrix-unit rate this part sustains with no memory traffic
     (moe_calib_mfma_bf16: the tiled kernel's 128 x 64 wave tile of 16x16x32
     MFMAs on register-resident N(0,1) activations and decoded MXFP4 weights),
     the median of 3 launches after one warm-up, with the matmul's achieved
     rate as a fraction of it.  Measured after the timed steps; the roofline
     fraction stays the one against the published peak."""
-    import torch
-    import moe_grouped_gemm_route_amd as moe
+    torch, moe = gpu.torch, gpu.moe
     from moe_grouped_gemm_route_amd.synth import make_problem
 
     q = make_problem(T=2048, k=1, E=1, K=4096, N=1024, seed=41)
-    dev = torch.device("cuda", 0)
-    a = torch.from_numpy(q["x"].view(np.int16)).to(dev)
-    packed = moe.mxfp4_encode(torch.from_numpy(q["codes"]).to(dev), torch.from_numpy(q["scales"]).to(dev),
-                              None, moe.MXFP4)
+    a = gpu.put(q["x"])
+    packed = moe.mxfp4_encode(gpu.put(q["codes"]), gpu.put(q["scales"]), None, moe.MXFP4)
     b = moe.debug_decode(packed, moe.MXFP4, 1, 1024, 4096)
     moe.calib_mfma_bf16(a, b, CALIB_BLOCKS, CALIB_ITERS)
     ms = []
     for _ in range(3):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = gpu.event(), gpu.event()
         e0.record()
         moe.calib_mfma_bf16(a, b, CALIB_BLOCKS, CALIB_ITERS)
         e1.record()
@@ -361,101 +580,53 @@ def mfma_calibration(achieved_tflops):
                     "%d workgroups of 4 waves, %.1f ms per launch" % (CALIB_BLOCKS, float(np.median(ms)))}
 
 
-def recorded_traffic(workload):
-    """HBM bytes per launch of the workload's matmul kernel from the committed
-    counter summary (FETCH_SIZE + WRITE_SIZE, calibrated on a copy kernel),
-    or None when there is none or the kernel source has changed since."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    try:
-        entry = json.load(open(TRAFFIC_FILE)).get(workload, {})
-    except (OSError, ValueError):
-        return None
-    if entry.get("gmm_source_sha256_16") != gmm_source_hash():
-        return None
-    return entry.get("bytes_per_launch")
+def hbm_calibration(gpu):
+    """The HBM read rate this part sustains (moe_calib_hbm_read: 16-byte
+    non-temporal loads, each wave reading contiguous 1 KiB runs, over a 2 GiB
+    buffer, eight times the last-level cache), median of 5 launches after
+    one warm-up."""
+    torch, moe = gpu.torch, gpu.moe
+    buf = torch.ones(HBM_CALIB_BYTES // 4, dtype=torch.int32, device=gpu.dev)
+    moe.calib_hbm_read(buf, HBM_CALIB_BLOCKS)
+    ms = []
+    for _ in range(5):
+        e0, e1 = gpu.event(), gpu.event()
+        e0.record()
+        moe.calib_hbm_read(buf, HBM_CALIB_BLOCKS)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del buf
+    gbs = HBM_CALIB_BYTES / (float(np.median(ms)) / 1e3) / 1e9
+    return {"read_gbs": round(gbs, 1),
+            "loop": "%d MiB read with 16-byte loads, %d workgroups of 256 threads, %.3f ms per launch"
+                    % (HBM_CALIB_BYTES >> 20, HBM_CALIB_BLOCKS, float(np.median(ms)))}
 
 
-def run_w4a4(args):
-    """The W4A4 prefill workload: route-sort, MXFP4 activation quantization and
-    the grouped matmul on the scaled FP4 MFMA, over config 4's problem."""
-    import torch
-    import moe_grouped_gemm_route_amd as moe
-    from moe_grouped_gemm_route_amd.synth import make_config
+def with_hbm_fraction(line, calib):
+    """Adds the kernel's fraction of the calibrated read rate to an
+    HBM-bound line."""
+    if line["roofline"]["bound"] == "hbm":
+        line["hbm_calibration"] = dict(calib)
+        line["hbm_calibration"]["kernel_frac_of_read"] = round(line["roofline"]["achieved"] / calib["read_gbs"], 4)
+    return line
 
-    p = make_config(4)
-    E, K, N, T, k = p["E"], p["K"], p["N"], p["T"], p["k"]
-    M = T * k
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
 
-    def d(a):
-        a = np.ascontiguousarray(a)
-        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+def summary(line):
+    """The compact record of a workload timed after the headline."""
+    keep = ("steps", "warmup", "ms_per_step", "value", "unit", "dtype", "config", "gmm_us", "gmm_us_median",
+            "gmm_us_min", "w13_us", "w2_us", "active_experts", "algorithmic_bytes", "roofline",
+            "mfma_calibration", "hbm_calibration", "cpu_baseline", "gpu_over_cpu")
+    return {key: line[key] for key in keep if key in line}
 
-    ids, x = d(p["topk_ids"]), d(p["x"])
-    codes = d(p["codes"])
-    packed = moe.mxfp4_encode(codes, d(p["scales"]), None, moe.MXFP4)
-    del codes
-    y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    ws = route_workspace(T, k, E, dev)
-    torch.cuda.synchronize()
-    ev = []
 
-    def step(timed):
-        r = moe.route_sort(ids, E, ws=ws)
-        qc, qs = moe.mxfp4_quantize(x)
-        if timed:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-        moe.moe_gmm_w4a4(packed, E, N, K, qc, qs, r["group_offsets"], M, row_index=r["sorted_token"], out=y)
-        if timed:
-            e1.record()
-            ev.append((e0, e1))
-
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gmm_ms = [a.elapsed_time(b) for a, b in ev]
-    gmm_s = float(np.mean(gmm_ms)) / 1e3
-    flops = 2.0 * M * K * N
-    counts = np.bincount(p["topk_ids"].reshape(-1), minlength=E)
-    active = int(np.count_nonzero(counts))
-    nbytes = active * N * K * (0.5 + 1.0 / 32) + T * (K // 2 + K // 32)
-    achieved = nbytes / gmm_s / 1e9
-    step_s = wall / args.steps
-    out = {
-        "metric": "moe_gmm TFLOP/s and HBM GB/s (% roofline), w13/w2, 256 experts top-6",
-        "value": round(flops / step_s / 1e12, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_s * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp4",
-        "data": "synthetic",
-        "config": {"workload": "w4a4_w13_prefill", "tokens": T, "top_k": k, "experts": E, "K": K,
-                   "N": N, "routed_rows": M, "weights": "mxfp4", "activations": "mxfp4 (quantized in the step)",
-                   "output": "f32", "step": "route_sort + mxfp4_quantize + moe_gmm_w4a4"},
-        "gmm_us": round(gmm_s * 1e6, 2),
-        "gmm_us_median": round(float(np.median(gmm_ms)) * 1e3, 2),
-        "gmm_us_min": round(float(np.min(gmm_ms)) * 1e3, 2),
-        "gmm_tflops": round(flops / gmm_s / 1e12, 2),
-        "active_experts": active,
-        "algorithmic_bytes": int(nbytes),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(args.workload),
-                     "fp4_mfma_frac": round(flops / gmm_s / 1e12 / FP4_PEAK_TFLOPS, 4)},
-    }
-    print(json.dumps(out), flush=True)
+def run_workload(gpu, name, steps, warmup, cpu_s, args):
+    if name in LAYER_WORKLOADS:
+        return run_layer(gpu, name, steps, warmup, cpu_s)
+    if name == "w4a4_w13_prefill":
+        return run_w4a4(gpu, steps, warmup)
+    return run_gmm(gpu, name, steps, warmup, cpu_s, kernel=args.kernel, out_dtype=args.out_dtype,
+                   tokens=args.tokens)
 
 
 def main():
@@ -463,9 +634,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="w13_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="w13_decode", choices=WORKLOADS)
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="token count in place of the workload's (grouped-matmul workloads only)")
     ap.add_argument("--kernel", default="auto", choices=sorted(KERNELS))
     ap.add_argument("--out-dtype", default=None, choices=["f32", "bf16"])
+    ap.add_argument("--only", action="store_true",
+                    help="time the named workload alone (no other workloads after the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer --steps times (a plain copy "
@@ -476,175 +651,38 @@ def main():
               "(the routed-expert matmul would shard by experts, 32 per GPU on 8 GPUs)",
               file=sys.stderr)
         sys.exit(2)
+    if args.tokens is not None and args.workload not in GMM_WORKLOADS:
+        print("--tokens applies to the grouped-matmul workloads only", file=sys.stderr)
+        sys.exit(2)
 
-    if args.workload in ("layer_decode", "layer_prefill", "w4a4_layer_prefill") and not args.copy_calibration:
-        run_layer(args)
-        return
-    if args.workload == "w4a4_w13_prefill" and not args.copy_calibration:
-        run_w4a4(args)
-        return
-
-    import torch
-    import moe_grouped_gemm_route_amd as moe
-    from moe_grouped_gemm_route_amd.synth import make_config
-
+    gpu = Gpu()
     if args.copy_calibration:
         n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
+        src = gpu.torch.ones(n, dtype=gpu.torch.uint8, device=gpu.dev)
+        dst = gpu.torch.empty_like(src)
         for _ in range(args.steps):
             dst.copy_(src)
-        torch.cuda.synchronize()
+        gpu.torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n, "launches": args.steps}), flush=True)
         return
 
-    cfg = WORKLOADS[args.workload]
-    p = make_config(cfg)
-    bf16_arm = args.workload.startswith("bf16_")
-    fmt = "nvfp4" if cfg == 5 else "mxfp4"
-    out_dtype = args.out_dtype or p["out"]
-    odt = moe.BF16 if out_dtype == "bf16" else moe.F32
-    E, K, N, T, k = p["E"], p["K"], p["N"], p["T"], p["k"]
-    M = T * k
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-
-    def d(a):
-        a = np.ascontiguousarray(a)
-        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
-
-    ids = d(p["topk_ids"])
-    x = d(p["x"])
-    codes = d(p["codes"])
-    if fmt == "mxfp4":
-        packed = moe.mxfp4_encode(codes, d(p["scales"]), None, moe.MXFP4)
-        wf = moe.MXFP4
-    else:
-        bs, ts, err = moe.mxfp4_to_nvfp4(d(p["scales"]))
-        packed = moe.mxfp4_encode(codes, bs, ts, moe.NVFP4)
-        wf = moe.NVFP4
-        assert err.item() == 0
-    del codes
-    packed_mx = None
-    if bf16_arm:
-        # the comparison arm streams the decoded weights as bf16
-        dense = moe.debug_decode(packed, wf, E, N, K)
-        packed_mx, packed = packed, moe.bf16_encode(dense)
-        del dense
-        fmt, wf = "bf16", moe.W_BF16
-    tw = d(p["topk_weights"])
-    combine = cfg == 3
-    y = torch.empty((M, N), dtype=torch.bfloat16 if odt == moe.BF16 else torch.float32, device=dev)
-    kernel = KERNELS[args.kernel]
-    ws = route_workspace(T, k, E, dev)
-    torch.cuda.synchronize()
-
-    ev = []
-
-    def step(timed):
-        r = moe.route_sort(ids, E, ws=ws)
-        if timed:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-        moe.moe_gmm(packed, wf, E, N, K, x, r["group_offsets"], M,
-                    row_index=r["sorted_token"] if p["gather"] else None,
-                    out_dtype=odt, kernel=kernel, out=y)
-        if timed:
-            e1.record()
-            ev.append((e0, e1))
-        if combine:
-            moe.moe_combine(y, tw, r["pair_row"])
-
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    mx_ms = None
-    if bf16_arm:
-        # the MXFP4 kernel on the same inputs, for the speedup
-        r = moe.route_sort(ids, E, ws=ws)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-        for i in range(args.warmup):
-            moe.moe_gmm(packed_mx, moe.MXFP4, E, N, K, x, r["group_offsets"], M,
-                        row_index=r["sorted_token"] if p["gather"] else None,
-                        out_dtype=odt, kernel=kernel, out=y)
-        e[0].record()
-        for i in range(args.steps):
-            moe.moe_gmm(packed_mx, moe.MXFP4, E, N, K, x, r["group_offsets"], M,
-                        row_index=r["sorted_token"] if p["gather"] else None,
-                        out_dtype=odt, kernel=kernel, out=y)
-            e[i + 1].record()
-        torch.cuda.synchronize()
-        mx_ms = [e[i].elapsed_time(e[i + 1]) for i in range(args.steps)]
-
-    gmm_ms = [a.elapsed_time(b) for a, b in ev]
-    gmm_avg_s = float(np.mean(gmm_ms)) / 1e3
-    gmm_med_s = float(np.median(gmm_ms)) / 1e3
-    gmm_min_s = float(np.min(gmm_ms)) / 1e3
-    nbytes, active = algorithmic_bytes(p, fmt)
-    flops = 2.0 * M * K * N
-    step_s = wall / args.steps
-    # the roof is whichever bound takes longer at peak: the matrix unit for
-    # MXFP4 prefill, HBM for decode and for bf16 weights at prefill
-    prefill = flops / (BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9)
-    if prefill:
-        achieved = flops / gmm_avg_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
-        value, unit = flops / step_s / 1e12, "TFLOP/s"
-    else:
-        achieved = nbytes / gmm_avg_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
-        value, unit = nbytes / step_s / 1e9, "GB/s"
-    roof["traffic"] = recorded_traffic(args.workload)
-
-    out = {
-        "metric": "moe_gmm TFLOP/s and HBM GB/s (% roofline), w13/w2, 256 experts top-6",
-        "value": round(value, 2),
-        "unit": unit,
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_s * 1e3, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": T, "top_k": k, "experts": E, "K": K,
-                   "N": N, "routed_rows": M,
-                   "weights": fmt + (" (decoded MXFP4 weights)" if bf16_arm else ""),
-                   "activations": "bf16",
-                   "output": out_dtype, "kernel": args.kernel,
-                   "step": "route_sort + moe_gmm" + (" + moe_combine" if combine else "")},
-        "gmm_us": round(gmm_avg_s * 1e6, 2),
-        "gmm_us_median": round(gmm_med_s * 1e6, 2),
-        "gmm_us_min": round(gmm_min_s * 1e6, 2),
-        "gmm_tflops": round(flops / gmm_avg_s / 1e12, 2),
-        "gmm_gbs": round(nbytes / gmm_avg_s / 1e9, 1),
-        "active_experts": active,
-        "algorithmic_bytes": int(nbytes),
-        # + the output written and the index arrays read (band offsets, row index)
-        "algorithmic_bytes_all": int(nbytes + M * N * (2 if odt == moe.BF16 else 4)
-                                     + 4 * (E + 1) + (4 * M if p["gather"] else 0)),
-        "roofline": roof,
-    }
-    if prefill:
-        out["mfma_calibration"] = mfma_calibration(roof["achieved"])
-    if mx_ms is not None:
-        mx_s = float(np.mean(mx_ms)) / 1e3
-        out["mxfp4_us"] = round(mx_s * 1e6, 2)
-        out["mxfp4_speedup_over_bf16"] = round(gmm_avg_s / mx_s, 3)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(p, "mxfp4" if bf16_arm else fmt, unit)
-        out["gpu_over_cpu"] = round(value / out["cpu_baseline"]["value"], 1)
-    print(json.dumps(out), flush=True)
+    cpu_s = 0.0 if args.no_cpu_baseline else 15.0
+    line = run_workload(gpu, args.workload, args.steps, args.warmup, cpu_s, args)
+    extras = args.workload == "w13_decode" and not args.only and args.tokens is None
+    calib = hbm_calibration(gpu) if (line["roofline"]["bound"] == "hbm" or extras) else None
+    if calib is not None:
+        with_hbm_fraction(line, calib)
+    if extras:
+        sub_args = argparse.Namespace(**vars(args))
+        sub_args.kernel, sub_args.out_dtype, sub_args.tokens = "auto", None, None
+        sub_cpu = 0.0 if args.no_cpu_baseline else 3.0
+        work = {}
+        for name in EXTRA_WORKLOADS:
+            sub = run_workload(gpu, name, min(args.steps, 20), min(args.warmup, 5), sub_cpu, sub_args)
+            work[name] = summary(with_hbm_fraction(sub, calib))
+            print("bench: %s done" % name, file=sys.stderr, flush=True)
+        line["workloads"] = work
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

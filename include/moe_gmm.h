@@ -376,6 +376,24 @@ int moe_debug_decode(const void* packed, int fmt, int32_t E, int32_t N,
 int moe_calib_mfma_bf16(const uint16_t* a, const uint16_t* b, int32_t blocks,
                         int32_t iters, float* out, void* stream);
 
+/*
+ * moe_calib_hbm_read - measurement support: the HBM read rate this part
+ * sustains with the weight-streaming kernel's access pattern (each wave walks
+ * its own contiguous region of src in 1 KiB runs, one 16-byte non-temporal
+ * buffer load per lane, eight runs in flight), for reading the decode
+ * kernels' HBM-bound fraction against.
+ *
+ * src    [bytes] device buffer, 16-byte aligned; bytes a multiple of 16.
+ *        Make it larger than the 256 MiB last-level cache (the bench uses
+ *        2 GiB) so the reads come from HBM.
+ * out    [blocks * 256] uint32, out: each thread's XOR of the 32-bit words it
+ *        read; the XOR over all of out equals the XOR of every 32-bit word
+ *        of src.
+ * Bytes per call: bytes.  Limits: 1 <= blocks <= 65535, and at most 2^22
+ * runs of 1 KiB per wave (bytes < blocks * 2^34).
+ */
+int moe_calib_hbm_read(const void* src, size_t bytes, int32_t blocks, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,6 +51,7 @@ _SIGNATURES = {
     "moe_mxfp4_to_nvfp4": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "moe_debug_decode": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp]),
     "moe_calib_mfma_bf16": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
+    "moe_calib_hbm_read": (ctypes.c_int, [_vp, _sz, _i32, _vp, _vp]),
 }
 
 
@@ -326,4 +327,16 @@ def calib_mfma_bf16(a, b, blocks, iters):
         raise MoeGmmError("calib_mfma_bf16: a needs %d and b %d bf16 values" % (lanes * 64, lanes * 32))
     out = torch.empty(lanes, dtype=torch.float32, device=a.device)
     _check(library().moe_calib_mfma_bf16(_ptr(a), _ptr(b), blocks, iters, _ptr(out), _stream()))
+    return out
+
+
+def calib_hbm_read(src, blocks):
+    """moe_calib_hbm_read: blocks workgroups of 256 threads stream the device
+    buffer src (16-byte aligned, a multiple of 16 bytes) with 16-byte loads.
+    Returns the [blocks * 256] uint32 XOR partials (as int32 bits)."""
+    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous():
+        raise MoeGmmError("src must be a contiguous CUDA (HIP) tensor")
+    nbytes = src.numel() * src.element_size()
+    out = torch.empty(blocks * 256, dtype=torch.int32, device=src.device)
+    _check(library().moe_calib_hbm_read(_ptr(src), nbytes, blocks, _ptr(out), _stream()))
     return out

@@ -244,4 +244,13 @@ int moe_calib_mfma_bf16(const uint16_t* a, const uint16_t* b, int32_t blocks, in
   return hip_status(moe::launch_calib_mfma(a, b, blocks, iters, out, static_cast<hipStream_t>(stream)));
 }
 
+int moe_calib_hbm_read(const void* src, size_t bytes, int32_t blocks, uint32_t* out, void* stream) {
+  if (!src || !out) return MOE_ERR_NULL;
+  if (bytes < 16 || bytes % 16 != 0 || blocks < 1 || blocks > 65535) return MOE_ERR_SHAPE;
+  // a wave's region of whole 1 KiB runs is addressed with 32-bit offsets
+  if (bytes / 1024 / ((uint64_t)blocks * 4) >= (1u << 22)) return MOE_ERR_SHAPE;
+  if (((uintptr_t)src & 15) || ((uintptr_t)out & 3)) return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_calib_hbm_read(src, bytes, blocks, out, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -418,10 +418,12 @@ __global__ __launch_bounds__(256, NS > 4 ? 2 : 3) void gmm_stream_kernel(const u
 // issue order, so its share of chunk kc+1 is then in LDS, while the codes
 // may still be in flight.  The barrier that follows makes every wave's share
 // visible and guarantees that every wave has finished reading buffer kc & 1
-// before it is refilled with chunk kc+2.  Every chunk but the last issues the
-// same loads, so the count is the same at every wait; the last chunk issues
-// none (its wait then passes at once), and a final vmcnt(0) drains the
-// weight loads before the epilogue.
+// before it is refilled with chunk kc+2.  Every chunk issues the same loads,
+// so the count is the same at every wait: the last chunk still stages into
+// buffer (kc+1) & 1, which the previous barrier freed, but from an offset
+// past the activation buffer, so those loads write zeros without fetching
+// anything; its code loads repeat the last chunk's into the unused register
+// slot.  A final vmcnt(0) drains them before the epilogue.
 //
 // A-fragment reads are ds_read_b128 issued P - 1 fragments ahead of their
 // MFMAs (inline asm, so the compiler cannot sink them next to their use);
@@ -472,6 +474,13 @@ __device__ __forceinline__ u32x4_t lds_read16(uint32_t addr) {
   return r;
 }
 
+// Scalar offset of the staging loads of chunk kn: its 256-byte slice of every
+// activation row, or, past the last chunk, an offset beyond any activation
+// buffer (below 2^31 bytes) so the loads write zeros to LDS without a fetch.
+__device__ __forceinline__ uint32_t stage_soff(int kn, int KC) {
+  return kn < KC ? (uint32_t)kn * 256u : BUF_OOB;
+}
+
 // Fragment f of a chunk (step s = f / NSUB, row subtile ms = f % NSUB) of
 // the LDS buffer BUF: decode the step's weights at its first fragment, wait
 // for the fragment's read, issue its NS MFMAs, then issue the read of
@@ -515,7 +524,7 @@ __device__ __forceinline__ void tiled_prologue(std::index_sequence<Is...>, u32x4
 // a time: bw[s] holds step s of the current chunk, and once the last row
 // subtile of step s has issued its MFMAs, bw[s] is refilled with step s of
 // the next chunk.  One chunk of weights stays in flight with 64 registers.
-template <int NSUB, int P, int BUF, int ACT, bool LOAD, int F>
+template <int NSUB, int P, int BUF, int ACT, int F>
 __device__ __forceinline__ void tiled_fragment_bf16(u32x4_t (&ar)[P], const uint32_t (&va)[4],
                                                     u32x4_t (&bw)[4][TL_NS], __amdgpu_buffer_rsrc_t cr,
                                                     uint32_t c_voff, int KC, int h16, int kn,
@@ -529,7 +538,7 @@ __device__ __forceinline__ void tiled_fragment_bf16(u32x4_t (&ar)[P], const uint
   constexpr int NF = F + P - 1;
   if constexpr (NF < FT)
     ar[NF % P] = lds_read16<(NF % NSUB) * 16 * TL_ROW_BYTES + BUF * TL_BUF_BYTES>(va[NF / NSUB]);
-  if constexpr (LOAD && ms == NSUB - 1) {
+  if constexpr (ms == NSUB - 1) {
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) {
       const int sub = col_sub<ACT>(ns, h16);
@@ -538,18 +547,20 @@ __device__ __forceinline__ void tiled_fragment_bf16(u32x4_t (&ar)[P], const uint
   }
 }
 
-template <int NSUB, int P, int BUF, int ACT, bool LOAD, size_t... Fs>
+template <int NSUB, int P, int BUF, int ACT, size_t... Fs>
 __device__ __forceinline__ void tiled_chunk_bf16(std::index_sequence<Fs...>, u32x4_t (&ar)[P],
                                                  const uint32_t (&va)[4], u32x4_t (&bw)[4][TL_NS],
                                                  __amdgpu_buffer_rsrc_t cr, uint32_t c_voff, int KC, int h16,
                                                  int kn, f32x4_t (&acc)[TL_MS][TL_NS]) {
-  (tiled_fragment_bf16<NSUB, P, BUF, ACT, LOAD, (int)Fs>(ar, va, bw, cr, c_voff, KC, h16, kn, acc), ...);
+  (tiled_fragment_bf16<NSUB, P, BUF, ACT, (int)Fs>(ar, va, bw, cr, c_voff, KC, h16, kn, acc), ...);
 }
 
 // The K walk with bf16 weights.  Per chunk a wave issues its share of the
 // next activation chunk (LOADS direct-to-LDS loads), then, step by step, the
 // next chunk's weights (4 * NS loads); the wait before the barrier leaves
-// only those weight loads outstanding.  The last chunk issues no loads.
+// only those weight loads outstanding.  On the last chunk the staging loads
+// read past the buffer (zeros, no fetch) and the weight loads repeat the last
+// chunk's into the unused registers, so the counts stay the same.
 template <int NSUB, int ACT>
 __device__ __forceinline__ void tiled_k_walk_bf16(uint8_t* s_a, __amdgpu_buffer_rsrc_t xr,
                                                   const uint32_t (&avo)[TL_LOADS], __amdgpu_buffer_rsrc_t cr,
@@ -561,31 +572,25 @@ __device__ __forceinline__ void tiled_k_walk_bf16(uint8_t* s_a, __amdgpu_buffer_
   const int lane = threadIdx.x & 63;
   const uint32_t c_voff = lane * 16;
   u32x4_t bw[4][TL_NS];
-  auto stage = [&](int kc) {
-    uint8_t* buf = s_a + (kc & 1) * TL_BUF_BYTES + wave * TL_LOADS * 1024;
+  auto stage = [&](int buf, uint32_t soff) {
+    uint8_t* dst = s_a + buf * TL_BUF_BYTES + wave * TL_LOADS * 1024;
 #pragma unroll
     for (int j = 0; j < TL_LOADS; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(buf + j * 1024), 16, avo[j], kc * 256, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(dst + j * 1024), 16, avo[j], soff, 0, 0);
   };
-  auto chunk = [&](auto bc, auto lastc, int kc) {
+  auto chunk = [&](auto bc, int kc) {
     constexpr int d = decltype(bc)::value;   // kc & 1: LDS buffer
-    constexpr bool last = decltype(lastc)::value;
-    const int kn = kc + 1;
-    if constexpr (!last) {
-      stage(kn);
-      __builtin_amdgcn_sched_barrier(0);     // the activation loads go first
-    }
+    const int kn = min(kc + 1, KC - 1);
+    stage(d ^ 1, stage_soff(kc + 1, KC));
+    __builtin_amdgcn_sched_barrier(0);       // the activation loads go first
     u32x4_t ar[P];
     tiled_prologue<NSUB, P, d>(std::make_index_sequence<PRO>{}, ar, va);
-    tiled_chunk_bf16<NSUB, P, d, ACT, !last>(std::make_index_sequence<FT>{}, ar, va, bw, cr, c_voff, KC, h16, kn,
-                                             acc);
-    if constexpr (!last) vm_wait_barrier<4 * TL_NS>();
+    tiled_chunk_bf16<NSUB, P, d, ACT>(std::make_index_sequence<FT>{}, ar, va, bw, cr, c_voff, KC, h16, kn, acc);
+    vm_wait_barrier<4 * TL_NS>();
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  using Mid = std::false_type;
-  using Last = std::true_type;
-  stage(0);
+  stage(0, 0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
@@ -595,16 +600,11 @@ __device__ __forceinline__ void tiled_k_walk_bf16(uint8_t* s_a, __amdgpu_buffer_
                                                         BUF_NT);
   vm_wait_barrier<0>();
   int k0 = 0;
-  for (; k0 + 2 < KC; k0 += 2) {
-    chunk(B0{}, Mid{}, k0);
-    chunk(B1{}, Mid{}, k0 + 1);
+  for (; k0 + 2 <= KC; k0 += 2) {
+    chunk(B0{}, k0);
+    chunk(B1{}, k0 + 1);
   }
-  if (k0 + 2 == KC) {
-    chunk(B0{}, Mid{}, k0);
-    chunk(B1{}, Last{}, k0 + 1);
-  } else {
-    chunk(B0{}, Last{}, k0);
-  }
+  if (k0 < KC) chunk(B0{}, k0);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>());
 }
 
@@ -625,11 +625,11 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
   // buffer: rows 4(LOADS w + j) .. +3, lane l landing at byte 16 l, i.e. row
   // 4(LOADS w + j) + l/16, physical segment l & 15, which holds logical
   // segment (l & 15) ^ (row & 15) (avo carries the source offsets).
-  auto stage = [&](int kc) {
-    uint8_t* buf = s_a + (kc & 1) * TL_BUF_BYTES + wave * TL_LOADS * 1024;
+  auto stage = [&](int buf, uint32_t soff) {
+    uint8_t* dst = s_a + buf * TL_BUF_BYTES + wave * TL_LOADS * 1024;
 #pragma unroll
     for (int j = 0; j < TL_LOADS; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(buf + j * 1024), 16, avo[j], kc * 256, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(dst + j * 1024), 16, avo[j], soff, 0, 0);
   };
   auto load_codes = [&](int slot, int kc) {
     const int rec = scale_record<FMT>(kc);
@@ -640,14 +640,11 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
       ws[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (sub * groups + rec) * 256, 0);
     }
   };
-  auto chunk = [&](auto bc, auto lastc, int kc) {
+  auto chunk = [&](auto bc, int kc) {
     constexpr int d = decltype(bc)::value;   // kc & 1: LDS buffer and code slot
-    constexpr bool last = decltype(lastc)::value;
-    if constexpr (!last) {
-      stage(kc + 1);
-      __builtin_amdgcn_sched_barrier(0);     // the activation loads go first
-      load_codes(d ^ 1, kc + 1);
-    }
+    stage(d ^ 1, stage_soff(kc + 1, KC));
+    __builtin_amdgcn_sched_barrier(0);       // the activation loads go first
+    load_codes(d ^ 1, min(kc + 1, KC - 1));
     float lo[TL_NS], hi[TL_NS];
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) chunk_scales<FMT>(ws[d][ns], kc, lo[ns], hi[ns]);
@@ -656,27 +653,20 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
     u32x4_t b[TL_NS];
     tiled_prologue<NSUB, P, d>(std::make_index_sequence<PRO>{}, ar, va);
     tiled_chunk<NSUB, P, d, FMT>(std::make_index_sequence<FT>{}, ar, va, b, cs[d], lo, hi, general, acc);
-    if constexpr (!last) vm_wait_barrier<2 * TL_NS>();
+    vm_wait_barrier<2 * TL_NS>();
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  using Mid = std::false_type;
-  using Last = std::true_type;
-  stage(0);
+  stage(0, 0);
   __builtin_amdgcn_sched_barrier(0);
   load_codes(0, 0);
   vm_wait_barrier<0>();
   int k0 = 0;
-  for (; k0 + 2 < KC; k0 += 2) {
-    chunk(B0{}, Mid{}, k0);
-    chunk(B1{}, Mid{}, k0 + 1);
+  for (; k0 + 2 <= KC; k0 += 2) {
+    chunk(B0{}, k0);
+    chunk(B1{}, k0 + 1);
   }
-  if (k0 + 2 == KC) {
-    chunk(B0{}, Mid{}, k0);
-    chunk(B1{}, Last{}, k0 + 1);
-  } else {
-    chunk(B0{}, Last{}, k0);
-  }
+  if (k0 < KC) chunk(B0{}, k0);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>());
 }
 

@@ -62,6 +62,11 @@ hipError_t launch_quantize_mxfp4(const uint16_t* x, int32_t R, int32_t K, uint8_
 hipError_t launch_calib_mfma(const uint16_t* a, const uint16_t* b, int32_t blocks, int32_t iters, float* out,
                              hipStream_t stream);
 
+// HBM read calibration: blocks workgroups of 256 threads XOR-reduce the
+// 16-byte words of src (bytes a multiple of 16) into out[blocks * 256].
+hipError_t launch_calib_hbm_read(const void* src, size_t bytes, int32_t blocks, uint32_t* out,
+                                 hipStream_t stream);
+
 hipError_t launch_combine(const void* y, int y_bf16, const float* w, const int32_t* pair_row,
                           int32_t T, int32_t k, int32_t N, void* out, int out_bf16,
                           hipStream_t stream);

@@ -139,6 +139,26 @@ def make_config(i):
     return p
 
 
+def make_tokens_problem(cfg, T):
+    """Config cfg's weights with T tokens: x and routing drawn like the
+    config's (same routing law and top-k; seed 1000 * cfg + T), the codes and
+    scales taken from make_config(cfg).  For a band-ordered input (the down
+    matmul) x has T * k rows."""
+    c = CONFIGS[cfg]
+    src = make_config(c.get("weights_from", cfg))
+    q = make_problem(T=T, k=c["k"], E=c["E"], K=c["K"], N=8, seed=1000 * cfg + T,
+                     routing=c["routing"], exp_range=c["exp_range"],
+                     empty_experts=c.get("empty_experts", ()),
+                     x_rows=T * c["k"] if c.get("band_input") else None)
+    p = dict(q)
+    p["N"] = c["N"]
+    p["codes"], p["scales"] = src["codes"], src["scales"]
+    p["name"] = "%s_%dtok" % (c["name"], T)
+    p["out"] = c["out"]
+    p["config"] = cfg
+    return p
+
+
 @lru_cache(maxsize=1)
 def make_layer_decode():
     """One MoE layer at decode: config 2's tokens, routing, router weights and

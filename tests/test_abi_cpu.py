@@ -220,3 +220,14 @@ def test_route_sort_noalloc_validation(lib):
     assert f(FAKE, 0, 2, 8, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
     assert f(FAKE, 4, 2, 1025, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
     assert f(FAKE, 1 << 22, 8, 8, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+
+
+def test_calib_hbm_read_validation(lib):
+    f = lib.moe_calib_hbm_read
+    assert f(None, 1 << 20, 64, FAKE_ALIGNED, None) == ERR_NULL
+    assert f(FAKE_ALIGNED, 1 << 20, 64, None, None) == ERR_NULL
+    assert f(FAKE_ALIGNED, 8, 64, FAKE_ALIGNED, None) == ERR_SHAPE
+    assert f(FAKE_ALIGNED, (1 << 20) + 4, 64, FAKE_ALIGNED, None) == ERR_SHAPE
+    assert f(FAKE_ALIGNED, 1 << 20, 0, FAKE_ALIGNED, None) == ERR_SHAPE
+    assert f(FAKE_ALIGNED, 1 << 20, 65536, FAKE_ALIGNED, None) == ERR_SHAPE
+    assert f(ctypes.c_void_p((1 << 30) + 8), 1 << 20, 64, FAKE_ALIGNED, None) == ERR_SHAPE

@@ -54,3 +54,28 @@ def test_cpu_baseline_record():
     assert out["value"] > 0 and out["cores"] >= 1
     assert "active experts" in out["sample"]
     assert np.isfinite(out["value"])
+
+
+def test_roofline_picks_the_longer_roof_and_reports_against_its_own_peak():
+    # HBM roof time 1e9 B / 8 TB/s = 125 us; bf16 MFMA roof of 1e11 FLOP at
+    # 2.5 PFLOP/s = 40 us: HBM-bound
+    r = bench.roofline(1e9, 1e11, 250e-6)
+    assert r["bound"] == "hbm" and r["peak"] == bench.HBM_PEAK_GBS
+    assert abs(r["achieved"] - 4000.0) < 0.1 and abs(r["frac"] - 0.5) < 1e-4
+    # 1e12 FLOP: 400 us on bf16 MFMA, the longer roof
+    r = bench.roofline(1e9, 1e12, 1e-3)
+    assert r["bound"] == "mfma" and r["peak"] == bench.BF16_PEAK_TFLOPS
+    assert abs(r["frac"] - 1000.0 / bench.BF16_PEAK_TFLOPS) < 1e-4
+    # a W4A4 shape bound by the FP4 matrix unit (5e12 FLOP: 495 us at 10.1
+    # PFLOP/s) is reported against the FP4 peak, not the bf16 one
+    r = bench.roofline(1e9, 5e12, 1e-3, bench.FP4_PEAK_TFLOPS)
+    assert r["bound"] == "mfma" and r["peak"] == bench.FP4_PEAK_TFLOPS
+    assert abs(r["frac"] - 5000.0 / bench.FP4_PEAK_TFLOPS) < 1e-4
+    # 1e12 FLOP at FP4 speed is 99 us, shorter than the 125 us of HBM
+    assert bench.roofline(1e9, 1e12, 1e-3, bench.FP4_PEAK_TFLOPS)["bound"] == "hbm"
+
+
+def test_tokens_flag_is_refused_for_layer_workloads():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "layer_prefill",
+                        "--tokens", "512"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "--tokens" in r.stderr

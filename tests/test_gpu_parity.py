@@ -773,3 +773,16 @@ def test_calib_mfma_closed_form():
         torch.cuda.synchronize()
         assert torch.all(out == 16384.0 * iters * bv)
 
+
+
+def test_calib_hbm_read_closed_form():
+    # the XOR of every thread's partial is the XOR of the buffer's 32-bit
+    # words: regions of unequal length, bytes past the last whole 1 KiB run,
+    # fewer runs than waves, and no whole run at all
+    rng = np.random.default_rng(105)
+    for nbytes, blocks in (((1 << 22) + 48, 7), ((1 << 22) + 2048 + 32, 5), (4096, 3), (48, 2)):
+        buf = rng.integers(0, 1 << 32, size=nbytes // 4, dtype=np.uint32)
+        out = moe.calib_hbm_read(torch.from_numpy(buf.view(np.int32)).to(DEV), blocks)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(buf)
