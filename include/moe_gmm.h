@@ -1,15 +1,16 @@
 /*
  * moe_gmm.h - routed-expert W4A16 grouped matmul for AMD MI355X (gfx950).
  *
- * C ABI of libmoegmm.so.  The path computes one MoE layer's routed-expert
- * matmuls the way "Running DeepSeek V4 Flash on TPU v6" (section "1. Four
- * bits that v6e can't hold") describes them: token-expert pairs are sorted
- * into one contiguous band of rows per expert, and for every (expert, M-tile)
- * x N-tile the K dimension is walked with the 4-bit weight tile decoded to
- * bf16 right after it arrives on chip, block-scaled, and accumulated in f32 on
- * the bf16 matrix unit.  Weights are MXFP4 (e2m1 codes, one E8M0 power-of-two
- * scale per 32 weights along K) or NVFP4 (e2m1 codes, one E4M3 scale per 16
- * weights along K, one f32 scale per expert); activations stay bf16.
+ * C ABI of libmoegmm.so: the routed-expert matmuls of one MoE layer
+ * (source: "Running DeepSeek V4 Flash on TPU v6", section "1. Four bits that
+ * v6e can't hold").  moe_route_sort groups the (token, slot) pairs by expert;
+ * moe_gmm multiplies each expert's group of rows by that expert's 4-bit
+ * weights, which it decodes exactly to bf16 on chip as they stream in and
+ * feeds to the bf16 matrix cores with f32 accumulation; moe_combine weighs
+ * and sums each token's k results.  Weights are MXFP4 (e2m1 codes, one E8M0
+ * power-of-two scale per 32 weights along K) or NVFP4 (e2m1 codes, one E4M3
+ * scale per 16 weights along K, one f32 scale per expert); activations stay
+ * bf16.
  *
  * Conventions for every call below:
  *  - Every data pointer is a DEVICE pointer (hipMalloc'd or a torch CUDA

@@ -1,13 +1,15 @@
 // moe_gmm: routed-expert grouped matmul, W4A16 on bf16 MFMA (gfx950).
 //
-// "Running DeepSeek V4 Flash on TPU v6", section "1. Four bits that v6e can't
-// hold": the grid walks (expert, M-tile) x N-tile pairs over the expert
-// bands, the inner loop walks K, each 4-bit weight tile is decoded to bf16 as
-// soon as it is on chip, multiplied by its block scale, and accumulated in an
-// f32 tile that never leaves the chip; ragged and empty bands are handled.
-// Section "Grouped matmul performance vs bf16": the NVFP4 variant reads
-// per-16 E4M3 block scales (and a per-expert tensor scale, applied here in
-// the epilogue).
+// Source: "Running DeepSeek V4 Flash on TPU v6", section "1. Four bits that
+// v6e can't hold" (the loop nest and the decode placement) and section
+// "Grouped matmul performance vs bf16" (the NVFP4 variant).  Here every
+// workgroup owns one tile of rows of one expert's band and a range of output
+// columns; it walks K in 128-deep chunks, turns each chunk's 4-bit codes
+// into exact bf16 weights in registers right after they arrive (E8M0 or E4M3
+// block scale folded into the convert), feeds them to the matrix cores with
+// f32 accumulators held on chip for the whole walk, and writes only the
+// band's real rows at the end.  Experts with no rows produce no work.  NVFP4's
+// per-expert tensor scale is one multiply in that final write.
 //
 // MFMA mapping.  v_mfma_f32_16x16x32_bf16 multiplies a 16x32 A fragment by a
 // 32x16 B fragment; lane l supplies row (l & 15) of A and column (l & 15) of

@@ -1,11 +1,12 @@
 """Expert-sorted token layout (test infrastructure; see the package docstring).
 
-"Running DeepSeek V4 Flash on TPU v6", section "1. Four bits that v6e can't
-hold": tokens are sorted by expert so the activations form one contiguous band
-of rows per expert, and the grouped matmul walks (expert, M-tile) pairs from
-the band sizes.  The pages do not say how ties inside a band are ordered; this
-oracle takes the stable order by flat pair index p = t * k + j, so that the
-indices are unique and comparable bit for bit.
+Source: "Running DeepSeek V4 Flash on TPU v6", section "1. Four bits that v6e
+can't hold".  This module turns the router's top-k choices into the layout
+the grouped matmul consumes: every (token, slot) pair becomes one row, rows
+are grouped by the expert they go to, and group_offsets gives where each
+expert's rows start and end.  The page leaves the order of rows within one
+expert open; here they keep increasing flat pair index p = t * k + j (a stable
+sort), which makes every index array unique and comparable bit for bit.
 
 A pair whose expert id lies outside [0, E) belongs to no band: it is dropped,
 counted, and its pair_row is -1.
