@@ -63,3 +63,43 @@ def bf16_ulp(ref):
     a = np.abs(np.asarray(ref, dtype=np.float64))
     e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
     return np.ldexp(1.0, (e - 7).astype(np.int64))
+
+
+def _expert_slice(w, e):
+    """The one-expert weight dict of expert e (the oracle's own format)."""
+    sub = {"fmt": w["fmt"], "codes": w["codes"][e:e + 1]}
+    if w["fmt"] == "mxfp4":
+        sub["scales"] = w["scales"][e:e + 1]
+    else:
+        sub["block_scales"] = w["block_scales"][e:e + 1]
+        sub["tensor_scale"] = np.asarray(w["tensor_scale"])[e:e + 1]
+    return sub
+
+
+def oracle_gmm_bands(x_bits, row_index, group_offsets, w, experts=None, quantized=None):
+    """The oracle's grouped matmul over the bands of the given experts (all by
+    default), one oracle.gmm call per expert on that expert's slice, spread
+    over host threads (numpy releases the GIL in the decode and the matmul).
+    quantized = (codes, scales) of MXFP4 activations runs oracle.gmm_w4a4
+    instead.  Returns {expert: [band rows, N] float64}."""
+    import concurrent.futures
+    import os
+    off = np.asarray(group_offsets, dtype=np.int64)
+    if experts is None:
+        experts = [e for e in range(off.size - 1) if off[e + 1] > off[e]]
+
+    def one(e):
+        lo, hi = int(off[e]), int(off[e + 1])
+        sub_off = np.array([0, hi - lo], dtype=np.int64)
+        ri = None if row_index is None else np.asarray(row_index)[lo:hi]
+        if quantized is not None:
+            qc, qs = quantized
+            if row_index is None:
+                qc, qs = qc[lo:hi], qs[lo:hi]
+            return e, oracle.gmm_w4a4(qc, qs, ri, sub_off, _expert_slice(w, e))
+        xs = x_bits if row_index is not None else x_bits[lo:hi]
+        return e, oracle.gmm(xs, ri, sub_off, _expert_slice(w, e))
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        return dict(ex.map(one, experts))

@@ -16,8 +16,8 @@ import torch
 import moe_grouped_gemm_route_amd as moe
 import oracle
 from moe_grouped_gemm_route_amd.synth import make_config, make_problem, random_bf16_bits
-from gpu_util import (DEV, REL_TOL, bf16_bits_to_f64, bf16_ulp, rel_err, run_gpu, to_dev,
-                      weights_for)
+from gpu_util import (DEV, REL_TOL, bf16_bits_to_f64, bf16_ulp, oracle_gmm_bands, rel_err, run_gpu,
+                      to_dev, weights_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -613,23 +613,68 @@ def test_gmm_silu_mul_config_sampled(cfg):
 
 
 @pytest.mark.slow
-def test_gmm_w4a4_config4_sampled():
+@pytest.mark.parametrize("cfg", [2, 3, 5])
+def test_gmm_config_full_output(cfg):
+    # every output element of the full-size decode workloads against the
+    # whole oracle: f32 output to the 1e-5 bound, and for config 2 (timed with
+    # bf16 output) the bf16 output as well.  A bf16 output is the RNE of the
+    # f32 sum, so it equals the f32 output's RNE bit for bit and lies within
+    # one bf16 ulp of the oracle plus the f32 sum's own 1e-5 max|ref| bound
+    # (the second term governs outputs whose sum cancels to near zero)
+    p = make_config(cfg)
+    fmt = "nvfp4" if cfg == 5 else "mxfp4"
+    w, packed = weights_for(p, fmt)
+    r, y32 = run_gpu(p, packed, fmt)
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    assert np.array_equal(r["group_offsets"].cpu().numpy(), ref_r["group_offsets"])
+    ri = ref_r["sorted_token"] if p["gather"] else None
+    bands = oracle_gmm_bands(p["x"], ri, ref_r["group_offsets"], w)
+    off = ref_r["group_offsets"]
+    ref = np.concatenate([bands[e] for e in sorted(bands)])
+    assert ref.shape == (int(off[-1]), p["N"]) and off[-1] == p["T"] * p["k"]
+    assert rel_err(y32.cpu().numpy(), ref) <= REL_TOL
+    if p["out"] == "bf16":
+        _, yb = run_gpu(p, packed, fmt, out_dtype=moe.BF16, routed=r)
+        assert torch.equal(yb, y32.to(torch.bfloat16))
+        got = yb.float().cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - ref) <= bf16_ulp(ref) + REL_TOL * np.max(np.abs(ref)))
+
+
+@pytest.mark.slow
+def test_gmm_config4_whole_experts():
+    # every output of 32 whole experts' bands (every eighth expert) of the
+    # 4,096-token prefill, f32 output
+    p = make_config(4)
+    w, packed = weights_for(p, "mxfp4")
+    r, y = run_gpu(p, packed, "mxfp4")
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    off = ref_r["group_offsets"]
+    experts = list(range(0, p["E"], 8))
+    bands = oracle_gmm_bands(p["x"], ref_r["sorted_token"], off, w, experts)
+    yh = y.cpu().numpy()
+    got = np.concatenate([yh[off[e]:off[e + 1]] for e in experts])
+    ref = np.concatenate([bands[e] for e in experts])
+    assert ref.shape[0] >= 32 * 64
+    assert rel_err(got, ref) <= REL_TOL
+
+
+@pytest.mark.slow
+def test_gmm_w4a4_config4_whole_experts():
+    # W4A4 on the 4,096-token prefill: every output of 8 whole experts' bands
+    # (over 3,000,000 outputs) against the oracle's W4A4 grouped matmul on its
+    # own quantization of the token rows those bands read
     p = make_config(4)
     w, packed = weights_for(p, "mxfp4")
     y = _run_w4a4(p, packed)
     ref_r = oracle.route_sort(p["topk_ids"], p["E"])
-    M = p["T"] * p["k"]
-    rows, cols = _sample(M, p["N"], 2000, 460)
-    # only the token rows the samples read are quantized by the oracle
-    toks = np.unique(ref_r["sorted_token"][rows])
-    qc, qs = oracle.quantize_mxfp4_rows(p["x"][toks])
-    xq = np.zeros((p["T"], p["K"]))
-    xq[toks] = oracle.dequantize_mxfp4_rows(qc, qs)
-    ref = np.array([float(np.dot(xq[ref_r["sorted_token"][r]],
-                                 oracle.dense_weights(w, int(np.searchsorted(ref_r["group_offsets"], r,
-                                                                              side="right") - 1))[c]))
-                    for r, c in zip(rows[:200], cols[:200])])
-    got = y.cpu().numpy()[rows[:200], cols[:200]].astype(np.float64)
+    off = ref_r["group_offsets"]
+    experts = list(range(3, p["E"], 32))
+    qc, qs = oracle.quantize_mxfp4_rows(p["x"])
+    bands = oracle_gmm_bands(None, ref_r["sorted_token"], off, w, experts, quantized=(qc, qs))
+    yh = y.cpu().numpy()
+    got = np.concatenate([yh[off[e]:off[e + 1]] for e in experts])
+    ref = np.concatenate([bands[e] for e in experts])
+    assert ref.size >= 3000
     assert rel_err(got, ref) <= REL_TOL
 
 
