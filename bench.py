@@ -25,7 +25,9 @@ Other workloads, run alone with --workload:
     activation fused (bf16 [M, 2048]) -> w2 (K = 2048, N = 4096, f32) ->
     top-k combine, on config 2's 64 or config 4's 4,096 tokens;
   w4a4_layer_prefill: the same layer W4A4 (x and h quantized to MXFP4 inside
-    the step), w4a4_w13_prefill: the 4,096-token w13 W4A4;
+    the step); w4a4_w13_prefill: the 4,096-token w13 W4A4, with MXFP4
+    weights, or with NVFP4 ones from the lossless cast (w4a4_nvfp4_w13_prefill);
+    w4a4_nvfp4_w13: config 5's 256 tokens, W4A4 with its NVFP4 weights;
   bf16_w13_decode, bf16_w2_decode, bf16_w13_prefill: the bf16-weight
     comparison arm on the decoded weights of configs 2, 3 and 4 (the same
     values, four times the bytes) next to the MXFP4 kernel on the same inputs.
@@ -66,7 +68,10 @@ GMM_WORKLOADS = {
     "bf16_w13_decode": 2, "bf16_w2_decode": 3, "bf16_w13_prefill": 4,
 }
 LAYER_WORKLOADS = ("layer_decode", "layer_prefill", "w4a4_layer_prefill")
-WORKLOADS = sorted(list(GMM_WORKLOADS) + list(LAYER_WORKLOADS) + ["w4a4_w13_prefill"])
+# W4A4 grouped matmul: config, weight format
+W4A4_WORKLOADS = {"w4a4_w13_prefill": (4, "mxfp4"), "w4a4_nvfp4_w13_prefill": (4, "nvfp4"),
+                  "w4a4_nvfp4_w13": (5, "nvfp4")}
+WORKLOADS = sorted(list(GMM_WORKLOADS) + list(LAYER_WORKLOADS) + list(W4A4_WORKLOADS))
 # timed after the headline in the default run
 EXTRA_WORKLOADS = ("tiny", "w2_decode", "w13_prefill", "nvfp4_w13", "layer_decode", "layer_prefill")
 KERNELS = {"auto": 0, "stream": 1, "tiled": 2}
@@ -490,21 +495,32 @@ def run_layer(gpu, workload, steps, warmup, cpu_s):
     return out
 
 
-def run_w4a4(gpu, steps, warmup):
-    """The W4A4 prefill workload: route-sort, MXFP4 activation quantization and
-    the grouped matmul on the scaled FP4 MFMA, over config 4's problem."""
+def run_w4a4(gpu, workload, steps, warmup):
+    """The W4A4 workloads: route-sort, MXFP4 activation quantization and the
+    grouped matmul on the scaled FP4 MFMA, over config 4's problem (MXFP4
+    weights, or NVFP4 ones from the library's lossless cast) or config 5's
+    (NVFP4 by the cast)."""
     torch, moe = gpu.torch, gpu.moe
     from moe_grouped_gemm_route_amd.synth import make_config
 
-    p = make_config(4)
+    cfg, wfmt = W4A4_WORKLOADS[workload]
+    p = make_config(cfg)
     E, K, N, T, k = p["E"], p["K"], p["N"], p["T"], p["k"]
     M = T * k
     ids, x = gpu.put(p["topk_ids"]), gpu.put(p["x"])
     codes = gpu.put(p["codes"])
-    packed = moe.mxfp4_encode(codes, gpu.put(p["scales"]), None, moe.MXFP4)
+    if wfmt == "mxfp4":
+        packed = moe.mxfp4_encode(codes, gpu.put(p["scales"]), None, moe.MXFP4)
+        wf = moe.MXFP4
+    else:
+        bs, ts, err = moe.mxfp4_to_nvfp4(gpu.put(p["scales"]))
+        assert err.item() == 0
+        packed = moe.mxfp4_encode(codes, bs, ts, moe.NVFP4)
+        wf = moe.NVFP4
     del codes
     y = torch.empty((M, N), dtype=torch.float32, device=gpu.dev)
     ws = gpu.route_workspace(T, k, E)
+    bad = torch.zeros(1, dtype=torch.int32, device=gpu.dev)
     torch.cuda.synchronize()
 
     def step(timed):
@@ -513,7 +529,8 @@ def run_w4a4(gpu, steps, warmup):
         e = (gpu.event(), gpu.event()) if timed else None
         if timed:
             e[0].record()
-        moe.moe_gmm_w4a4(packed, E, N, K, qc, qs, r["group_offsets"], M, row_index=r["sorted_token"], out=y)
+        moe.moe_gmm_w4a4(packed, E, N, K, qc, qs, r["group_offsets"], M, row_index=r["sorted_token"], out=y,
+                         fmt=wf, err_count=bad if wf == moe.NVFP4 else None)
         if timed:
             e[1].record()
         return e
@@ -522,17 +539,22 @@ def run_w4a4(gpu, steps, warmup):
     gmm_ms = [a.elapsed_time(b) for a, b in ev]
     gmm_s = float(np.mean(gmm_ms)) / 1e3
     flops = 2.0 * M * K * N
+    assert bad.item() == 0
     counts = np.bincount(p["topk_ids"].reshape(-1), minlength=E)
     active = int(np.count_nonzero(counts))
-    nbytes = active * N * K * (0.5 + 1.0 / 32) + T * (K // 2 + K // 32)
+    per_weight = 0.5 + (1.0 / 32 if wfmt == "mxfp4" else 1.0 / 16)
+    nbytes = active * N * K * per_weight + (active * 4 if wfmt == "nvfp4" else 0) + T * (K // 2 + K // 32)
     step_s = wall / steps
     roof = roofline(nbytes, flops, gmm_s, FP4_PEAK_TFLOPS)
-    roof["traffic"] = recorded_traffic("w4a4_w13_prefill")
+    roof["traffic"] = recorded_traffic(workload)
     roof["fp4_mfma_frac"] = round(flops / gmm_s / 1e12 / FP4_PEAK_TFLOPS, 4)
-    config = {"tokens": T, "top_k": k, "experts": E, "K": K, "N": N, "routed_rows": M, "weights": "mxfp4",
+    config = {"tokens": T, "top_k": k, "experts": E, "K": K, "N": N, "routed_rows": M,
+              "weights": wfmt + (" (from the lossless cast)" if wfmt == "nvfp4" else ""),
               "activations": "mxfp4 (quantized in the step)", "output": "f32",
               "step": "route_sort + mxfp4_quantize + moe_gmm_w4a4"}
-    out = base_line("w4a4_w13_prefill", steps, warmup, step_s, flops / step_s / 1e12, "TFLOP/s", "fp4", config)
+    rate, unit = (flops / step_s / 1e12, "TFLOP/s") if roof["bound"] == "mfma" or cfg == 4 else \
+        (nbytes / step_s / 1e9, "GB/s")
+    out = base_line(workload, steps, warmup, step_s, rate, unit, "fp4", config)
     out.update({
         "gmm_us": round(gmm_s * 1e6, 2),
         "gmm_us_median": round(float(np.median(gmm_ms)) * 1e3, 2),
@@ -623,8 +645,8 @@ def summary(line):
 def run_workload(gpu, name, steps, warmup, cpu_s, args):
     if name in LAYER_WORKLOADS:
         return run_layer(gpu, name, steps, warmup, cpu_s)
-    if name == "w4a4_w13_prefill":
-        return run_w4a4(gpu, steps, warmup)
+    if name in W4A4_WORKLOADS:
+        return run_w4a4(gpu, name, steps, warmup)
     return run_gmm(gpu, name, steps, warmup, cpu_s, kernel=args.kernel, out_dtype=args.out_dtype,
                    tokens=args.tokens)
 

@@ -286,27 +286,42 @@ int moe_mxfp4_quantize(const uint16_t* x, int32_t R, int32_t K, uint8_t* codes, 
                        void* stream);
 
 /*
- * moe_gmm_w4a4 - the grouped matmul with MXFP4 weights and MXFP4-quantized
+ * moe_gmm_w4a4 - the grouped matmul with 4-bit weights and MXFP4-quantized
  * activations, on the scaled FP4 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4).
  *
  * Source: the grouped matmul of moe_gmm ("Running DeepSeek V4 Flash on TPU
  * v6", section "1. Four bits that v6e can't hold") with the W4A4 execution of
- * "DeepSeek-V4-Flash-0731-NVFP4" (see moe_mxfp4_quantize).
+ * "DeepSeek-V4-Flash-0731-NVFP4" (sections "What was quantized" and
+ * "Performance"), whose NVFP4 weights come from MXFP4 by the scale mapping of
+ * its section "The lossless weight cast".
  *
  * For every row r of band e:  y[r, n] = sum_k A[src(r), k] * W_e[n, k] with
  * A = e2m1(code) * 2^(scale - 127) of the quantized activations; the products
  * are exact, the sums f32 (the matrix unit adds each 128-deep chunk, then
  * the running sum).  act as moe_gmm_act.
  *
- * packed         mxfp4_encode output for (MOE_W_MXFP4, E, N, K).
+ * packed         mxfp4_encode output for (fmt, E, N, K).
+ * fmt            MOE_W_MXFP4, or MOE_W_NVFP4 whose two E4M3 scales of every
+ *                32-weight block are one equal power of two (2^-9 .. 2^8; true
+ *                of every pack made by moe_mxfp4_to_nvfp4): that scale is
+ *                given to the instruction as the block's E8M0 byte and the
+ *                per-expert tensor scale multiplies the f32 sums, so the
+ *                output equals, bit for bit, that of the MXFP4 weights the
+ *                cast came from.  MOE_W_BF16 returns MOE_ERR_UNSUPPORTED.
  * xq_codes       [x_rows, K/2] from moe_mxfp4_quantize, 16-byte aligned.
  * xq_scales      [x_rows, K/32].
+ * err_count      out [1] int32, may be NULL: with NVFP4 weights, the number
+ *                of (expert, column, 32-block) weight blocks this call used
+ *                whose scales do not qualify (whether they do is known only
+ *                on the device); outputs that read such a block are
+ *                unspecified.  Always 0 for MXFP4.
  * Other arguments, limits and errors as moe_gmm_act, with
  * x_rows * K/2 < 2^31.  LDS-tiled kernel (meant for prefill bands).
  */
-int moe_gmm_w4a4(const void* packed, int32_t E, int32_t N, int32_t K, const uint8_t* xq_codes,
+int moe_gmm_w4a4(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint8_t* xq_codes,
                  const uint8_t* xq_scales, int32_t x_rows, const int32_t* row_index,
-                 const int32_t* group_offsets, int32_t M, void* y, int y_dtype, int act, void* stream);
+                 const int32_t* group_offsets, int32_t M, void* y, int y_dtype, int act,
+                 int32_t* err_count, void* stream);
 
 /*
  * moe_combine - top-k weighted unpermute back to token order.

@@ -38,8 +38,8 @@ _SIGNATURES = {
     "mxfp4_encode": (ctypes.c_int, [ctypes.c_int, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "moe_bf16_encode": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp]),
     "moe_mxfp4_quantize": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
-    "moe_gmm_w4a4": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp,
-                                    ctypes.c_int, ctypes.c_int, _vp]),
+    "moe_gmm_w4a4": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp, _i32, _vp,
+                                    ctypes.c_int, ctypes.c_int, _vp, _vp]),
     "moe_gmm": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32,
                                _vp, ctypes.c_int, _vp]),
     "moe_gmm_ex": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _i32, _vp, _vp, _i32,
@@ -238,9 +238,12 @@ def mxfp4_quantize(x):
 
 
 def moe_gmm_w4a4(packed, E, N, K, xq_codes, xq_scales, group_offsets, M, row_index=None,
-                 out_dtype=F32, act=ACT_NONE, out=None):
+                 out_dtype=F32, act=ACT_NONE, out=None, fmt=MXFP4, err_count=None):
     """moe_gmm_w4a4.  xq_codes [rows, K/2], xq_scales [rows, K/32] from
-    mxfp4_quantize; packed MXFP4 weights.  Returns y [M, N] or [M, N/2]."""
+    mxfp4_quantize; packed MXFP4 or NVFP4 (power-of-two block scales)
+    weights.  Returns y [M, N] or [M, N/2].  err_count: an optional [1] int32
+    device tensor that receives the NVFP4 weight blocks whose scales do not
+    qualify."""
     _dev(packed, torch.uint8, "packed", 1)
     _dev(xq_codes, torch.uint8, "xq_codes", 2)
     _dev(xq_scales, torch.uint8, "xq_scales", 2)
@@ -257,7 +260,7 @@ def moe_gmm_w4a4(packed, E, N, K, xq_codes, xq_scales, group_offsets, M, row_ind
         _dev(row_index, torch.int32, "row_index", 1)
         if row_index.numel() < M:
             raise MoeGmmError("row_index must have M entries")
-    if packed.numel() < packed_weight_bytes(MXFP4, E, N, K):
+    if packed.numel() < packed_weight_bytes(fmt, E, N, K):
         raise MoeGmmError("packed buffer too small")
     dt = torch.float32 if out_dtype == F32 else torch.bfloat16
     cols = N // 2 if act == ACT_SILU_MUL else N
@@ -267,9 +270,11 @@ def moe_gmm_w4a4(packed, E, N, K, xq_codes, xq_scales, group_offsets, M, row_ind
         _dev(out, dt, "out", 2)
         if tuple(out.shape) != (M, cols):
             raise MoeGmmError("out must be [M, %d]" % cols)
-    _check(library().moe_gmm_w4a4(_ptr(packed), E, N, K, _ptr(xq_codes), _ptr(xq_scales), rows,
+    if err_count is not None:
+        _dev(err_count, torch.int32, "err_count", 1)
+    _check(library().moe_gmm_w4a4(_ptr(packed), fmt, E, N, K, _ptr(xq_codes), _ptr(xq_scales), rows,
                                   _ptr(row_index), _ptr(group_offsets), M, _ptr(out), out_dtype, act,
-                                  _stream()))
+                                  _ptr(err_count), _stream()))
     return out
 
 

@@ -174,10 +174,12 @@ int moe_mxfp4_quantize(const uint16_t* x, int32_t R, int32_t K, uint8_t* codes, 
   return hip_status(moe::launch_quantize_mxfp4(x, R, K, codes, scales, static_cast<hipStream_t>(stream)));
 }
 
-int moe_gmm_w4a4(const void* packed, int32_t E, int32_t N, int32_t K, const uint8_t* xq_codes,
+int moe_gmm_w4a4(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint8_t* xq_codes,
                  const uint8_t* xq_scales, int32_t x_rows, const int32_t* row_index,
-                 const int32_t* group_offsets, int32_t M, void* y, int y_dtype, int act, void* stream) {
-  const int st = check_weight_shape(MOE_W_MXFP4, E, N, K);
+                 const int32_t* group_offsets, int32_t M, void* y, int y_dtype, int act, int32_t* err_count,
+                 void* stream) {
+  if (fmt == MOE_W_BF16) return MOE_ERR_UNSUPPORTED;
+  const int st = check_weight_shape(fmt, E, N, K);
   if (st != MOE_OK) return st;
   if (!dtype_ok(y_dtype)) return MOE_ERR_FORMAT;
   if (act != MOE_ACT_NONE && act != MOE_ACT_SILU_MUL) return MOE_ERR_FORMAT;
@@ -191,9 +193,9 @@ int moe_gmm_w4a4(const void* packed, int32_t E, int32_t N, int32_t K, const uint
     if (N % 128 != 0) return MOE_ERR_SHAPE;
     if ((int64_t)(N / 32 + 2) * (K / 128) * 1024 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
   }
-  return hip_status(moe::launch_gmm_w4a4(static_cast<const uint8_t*>(packed), E, N, K, xq_codes, xq_scales,
+  return hip_status(moe::launch_gmm_w4a4(static_cast<const uint8_t*>(packed), fmt, E, N, K, xq_codes, xq_scales,
                                          x_rows, row_index, group_offsets, M, y, y_dtype == MOE_BF16, act,
-                                         static_cast<hipStream_t>(stream)));
+                                         err_count, static_cast<hipStream_t>(stream)));
 }
 
 int moe_gmm(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint16_t* x,

@@ -88,11 +88,15 @@ __global__ void zero_i32_kernel(int32_t* p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
 }
 
+void launch_zero_i32(int32_t* p, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, stream, p, n);
+}
+
 hipError_t launch_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
                          const float* tensor_scale, int32_t E, int32_t N, int32_t K,
                          uint8_t* packed, int32_t* err_count, hipStream_t stream) {
   const Layout L = make_layout(fmt, E, N, K);
-  if (err_count) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, stream, err_count, 1);
+  if (err_count) launch_zero_i32(err_count, 1, stream);
   const int64_t runs = L.E * L.N * L.KB;
   const int grid_c = (int)((runs + 255) / 256 < 65536 ? (runs + 255) / 256 : 65536);
   hipLaunchKernelGGL(encode_codes_kernel, dim3(grid_c), dim3(256), 0, stream,
@@ -311,7 +315,7 @@ hipError_t launch_mxfp4_to_nvfp4(const uint8_t* scales, int32_t E, int32_t N, in
                                  uint8_t* block_scales, float* tensor_scale, int32_t* err_count,
                                  hipStream_t stream) {
   const int64_t per_expert = (int64_t)N * (K / 32);
-  if (err_count) hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, stream, err_count, 1);
+  if (err_count) launch_zero_i32(err_count, 1, stream);
   hipLaunchKernelGGL(mxfp4_to_nvfp4_kernel, dim3(E), dim3(256), 0, stream, scales, per_expert,
                      block_scales, tensor_scale, err_count);
   return hipGetLastError();

@@ -35,13 +35,20 @@ struct Tile {
   int e;      // expert, or -1 past the last tile
   int m0;     // first band row of the tile
   int rows;   // valid rows in the tile (1..BM)
+  int first;  // 1 for the first tile of its expert's band
 };
 
 // Per-wave view of the tile list "for each expert e, ceil(count_e / BM)
 // tiles": lane l covers experts [l*per, l*per + per) and holds the number of
-// tiles before them (excl) and up to their end (incl).  total is uniform.
+// tiles before them (excl) and up to their end (incl); total is uniform.  The
+// lane's band offsets go[0 .. per] are loaded in one batch and kept in
+// registers, so finding a tile costs one round trip to memory, not one per
+// expert (each round trip takes microseconds while the weights stream).
+constexpr int TS_PER_MAX = 16;   // experts per lane: E <= 1024 over 64 lanes
+
 struct TileScan {
   int per, excl, incl, total;
+  int go[TS_PER_MAX + 1];
 };
 
 __device__ __forceinline__ TileScan scan_tiles(const int32_t* __restrict__ goff, int E, int BM) {
@@ -49,11 +56,12 @@ __device__ __forceinline__ TileScan scan_tiles(const int32_t* __restrict__ goff,
   TileScan ts;
   ts.per = (E + 63) >> 6;
   const int e0 = lane * ts.per;
+#pragma unroll
+  for (int i = 0; i <= TS_PER_MAX; ++i) ts.go[i] = (i <= ts.per && e0 + i <= E) ? goff[e0 + i] : 0;
   int mine = 0;
-  for (int i = 0; i < ts.per; ++i) {
-    const int e = e0 + i;
-    if (e < E) mine += (goff[e + 1] - goff[e] + BM - 1) / BM;
-  }
+#pragma unroll
+  for (int i = 0; i < TS_PER_MAX; ++i)
+    if (i < ts.per && e0 + i < E) mine += (ts.go[i + 1] - ts.go[i] + BM - 1) / BM;
   int incl = mine;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -66,34 +74,37 @@ __device__ __forceinline__ TileScan scan_tiles(const int32_t* __restrict__ goff,
   return ts;
 }
 
-// Tile t (< ts.total) of the list, found by every lane of the wave.
-__device__ __forceinline__ Tile locate_tile(const int32_t* __restrict__ goff, int E, int BM,
-                                            const TileScan& ts, int t) {
+// Tile t (< ts.total) of the list, found by every lane of the wave from the
+// offsets the scan holds in registers.
+__device__ __forceinline__ Tile locate_tile(int E, int BM, const TileScan& ts, int t) {
   const int lane = threadIdx.x & 63;
   const uint64_t hit = __ballot(ts.excl <= t && t < ts.incl);
   const int src = __ffsll((unsigned long long)hit) - 1;
-  int fe = -1, fm0 = 0, frows = 0;
+  int fe = -1, fm0 = 0, frows = 0, ffirst = 0;
   if (lane == src) {
+    const int e0 = lane * ts.per;
     int acc = ts.excl;
-    for (int i = 0; i < ts.per; ++i) {
-      const int e = lane * ts.per + i;
-      if (e >= E) break;
-      const int c = goff[e + 1] - goff[e];
-      const int nt = (c + BM - 1) / BM;
-      if (t < acc + nt) {
-        const int j = t - acc;
-        fe = e;
-        fm0 = goff[e] + j * BM;
-        frows = c - j * BM < BM ? c - j * BM : BM;
-        break;
+#pragma unroll
+    for (int i = 0; i < TS_PER_MAX; ++i) {
+      if (i < ts.per && e0 + i < E && fe < 0) {
+        const int c = ts.go[i + 1] - ts.go[i];
+        const int nt = (c + BM - 1) / BM;
+        if (t < acc + nt) {
+          const int j = t - acc;
+          fe = e0 + i;
+          fm0 = ts.go[i] + j * BM;
+          frows = c - j * BM < BM ? c - j * BM : BM;
+          ffirst = j == 0;
+        }
+        acc += nt;
       }
-      acc += nt;
     }
   }
   Tile out;
   out.e = __builtin_amdgcn_readfirstlane(__shfl(fe, src, 64));
   out.m0 = __builtin_amdgcn_readfirstlane(__shfl(fm0, src, 64));
   out.rows = __builtin_amdgcn_readfirstlane(__shfl(frows, src, 64));
+  out.first = __builtin_amdgcn_readfirstlane(__shfl(ffirst, src, 64));
   return out;
 }
 
@@ -258,12 +269,9 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
   u32x4_t cring[D][NS][CW];
   uint32_t sring[D][NS];
   u32x4_t aring[D][MSUB][4];
+  // the codes go first: they depend only on the expert, so the first ones
+  // are in flight while the gathered row indices are still arriving
   auto load_step = [&](int slot, int kc) {
-#pragma unroll
-    for (int ms = 0; ms < MSUB; ++ms)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        aring[slot][ms][q] = __builtin_amdgcn_raw_buffer_load_b128(xr, a_voff[ms], kc * 256 + q * 16, 0);
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
       const int sub = col_sub<ACT>(ns, h16);
@@ -278,6 +286,11 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
         sring[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (sub * groups + rec) * 256, 0);
       }
     }
+#pragma unroll
+    for (int ms = 0; ms < MSUB; ++ms)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        aring[slot][ms][q] = __builtin_amdgcn_raw_buffer_load_b128(xr, a_voff[ms], kc * 256 + q * 16, 0);
   };
 
   f32x4_t acc[MSUB][NS];
@@ -369,7 +382,7 @@ __global__ __launch_bounds__(256, NS > 4 ? 2 : 3) void gmm_stream_kernel(const u
   const int nb = kth - (kth / NB) * NB;
   if (t >= ts.total) return;
   static_assert(ACT == 0 || NS == 4, "the gate/up activation pairs two gate and two up subtiles");
-  const Tile tile = locate_tile(goff, E, BM, ts, t);
+  const Tile tile = locate_tile(E, BM, ts, t);
   // first column (ACT 0) or first gate column (ACT 1) of this wave
   const int n0 = (nb * 4 + wave) * (ACT == 1 ? 32 : NS * 16);
   if (n0 >= (ACT == 1 ? L.N / 2 : L.N)) return;
@@ -687,7 +700,7 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
   if (item < 0) return;
   const int t = item / NB;
   const int nb = item - t * NB;
-  const Tile tile = locate_tile(goff, E, TL_BM, ts, t);
+  const Tile tile = locate_tile(E, TL_BM, ts, t);
   const int K = (int)L.K;
   const int KC = (int)L.KC;
   const int groups = (int)L.groups;
@@ -778,8 +791,15 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// W4A4 kernel (prefill): MXFP4 weights times MXFP4-quantized activations on
+// W4A4 kernel (prefill): 4-bit weights times MXFP4-quantized activations on
 // gfx950's scaled FP4 MFMA, v_mfma_scale_f32_16x16x128_f8f6f4 (e2m1 A and B).
+// MXFP4 weights pass their E8M0 bytes to the instruction as they are.  NVFP4
+// weights qualify when the two E4M3 scales of every 32-block are one equal
+// power of two (so for every pack made by the lossless MXFP4 cast): that
+// scale becomes the block's E8M0 byte and the per-expert tensor scale is one
+// multiply in the epilogue, so the f32 sums are exactly those of the MXFP4
+// weights the cast came from.  A block that does not qualify is counted in
+// err_count (its outputs are unspecified).
 // Its operands match the packed weights exactly: lane l supplies the 32 codes
 // (16 bytes, low nibble first) of column (l & 15), K block (l >> 4) of a
 // 128-deep chunk and that block's E8M0 scale (byte 0 of the scale operand);
@@ -790,16 +810,17 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
 // Same workgroup shape as the tiled kernel: 4 waves, 128 rows x 256
 // columns, the activation chunk staged in LDS by direct-to-LDS loads.  With a
 // quarter of the matrix work per chunk the kernel is bound by its weight
-// stream, so three chunks are staged (LDS buffers for the activations, a
-// register ring for the weight codes and scale words) and two of them are in
-// flight while the third is computed.  A staged chunk holds the 128 rows'
+// stream, so three chunks are staged (LDS buffers for the activations and
+// each wave's weight scale words, a register ring for the weight codes) and
+// two of them are in flight while the third is computed.  A staged chunk holds the 128 rows'
 // codes (64 bytes per row, rows contiguous: 8 KiB) and their scale dwords
 // (wave w loads rows 32w .. 32w+31 into its own 256-byte slot; lanes 32..63
 // read past the buffer and write zeros into the slot's unused half).
 // ---------------------------------------------------------------------------
 constexpr int Q_CODE_BYTES = TL_BM * 64;                     // 8 KiB
 constexpr int Q_SCALE_BYTES = TL_WAVES * 256;
-constexpr int Q_STAGE_BYTES = Q_CODE_BYTES + Q_SCALE_BYTES;
+constexpr int Q_WSCALE_BYTES = TL_WAVES * TL_NS * 256;       // each wave's weight scale words
+constexpr int Q_STAGE_BYTES = Q_CODE_BYTES + Q_SCALE_BYTES + Q_WSCALE_BYTES;
 constexpr int Q_LOADS = Q_CODE_BYTES / 1024 / TL_WAVES;      // 1 KiB code loads per wave per chunk
 constexpr int Q_STAGES = 3;                                   // chunks staged: two in flight, one computed
 constexpr int Q_ISSUE = Q_LOADS + 1 + 2 * TL_NS;             // vector-memory instructions per chunk
@@ -813,20 +834,45 @@ __device__ __forceinline__ f32x4_t mfma_fp4(u32x4_t a, uint32_t sa, u32x4_t b, u
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
-template <int NSUB, int ACT>
+// The E8M0 operand of one lane's 32-block in chunk kc from its packed scale
+// word.  NVFP4: the block qualifies when its two E4M3 bytes are equal and
+// hold a positive power of two (normal or subnormal); `bad` counts the
+// lane's blocks that do not.
+template <int FMT>
+__device__ __forceinline__ uint32_t w4a4_block_scale(uint32_t word, int kc, int& bad) {
+  if (FMT == 0) return (word >> (8 * (kc & 3))) & 0xFFu;
+  // The hardware E4M3 convert gives the low byte's exact f32 value: a
+  // positive power of two has a zero sign and mantissa, and its f32 exponent
+  // field is the E8M0 byte.  Integer minima stand in for comparisons (lane
+  // masks would sit in scalar registers across the unrolled walk).
+  const uint32_t pair = word >> (16 * (kc & 1));
+  const uint32_t bits = __float_as_uint(__builtin_amdgcn_cvt_f32_fp8(pair, 0));
+  const uint32_t off = min((pair ^ (pair >> 8)) & 0xFFu, 1u) | min(bits & 0x807FFFFFu, 1u) | (1u - min(bits, 1u));
+  bad += (int)off;
+  return off ? 127u : bits >> 23;
+}
+
+// NST staged chunks, NST - 1 in flight: three for MXFP4 weights; two for
+// NVFP4, whose per-block scale conversion needs the registers of the third.
+template <int NSUB, int FMT, int ACT, int NST>
 __device__ __forceinline__ void w4a4_k_walk(uint8_t* s_q, __amdgpu_buffer_rsrc_t qcr, __amdgpu_buffer_rsrc_t qsr,
                                             const uint32_t (&cvo)[Q_LOADS], uint32_t svo,
                                             __amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t sr, int KC,
-                                            int groups, int h16, int wave, f32x4_t (&acc)[TL_MS][TL_NS]) {
+                                            int groups, int h16, int wave, f32x4_t (&acc)[TL_MS][TL_NS],
+                                            int& bad) {
+  static_assert(NST == 2 || NST == 3, "two or three stages");
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
   const uint32_t c_voff = lane * 16, s_voff = lane * 4;
-  u32x4_t cs[Q_STAGES][TL_NS];
-  uint32_t ws[Q_STAGES][TL_NS];
+  u32x4_t cs[NST][TL_NS];
+  // this wave's weight scale words in a stage: 256 bytes per subtile, the
+  // word of lane l at byte 4 l
+  const int wsc = Q_CODE_BYTES + Q_SCALE_BYTES + wave * TL_NS * 256;
   // all loads of chunk kc into stage `slot`: the activation codes and scales
   // (direct to LDS, shared by the four waves), then this wave's weight codes
-  // and scale words (registers); Q_ISSUE vector-memory instructions
+  // (registers) and weight scale words (direct to LDS, its own slot);
+  // Q_ISSUE vector-memory instructions
   auto issue = [&](auto sc, int kc) {
     constexpr int slot = decltype(sc)::value;
     uint8_t* buf = s_q + slot * Q_STAGE_BYTES;
@@ -836,24 +882,28 @@ __device__ __forceinline__ void w4a4_k_walk(uint8_t* s_q, __amdgpu_buffer_rsrc_t
                                                kc * 64, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(qsr, (lds_ptr_t)(buf + Q_CODE_BYTES + wave * 256), 4, svo, kc * 4, 0, 0);
     __builtin_amdgcn_sched_barrier(0);       // the activation loads go first
-    const int rec = scale_record<0>(kc);
+    const int rec = scale_record<FMT>(kc);
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) {
       const int sub = col_sub<ACT>(ns, h16);
       cs[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, chunk_off<10>(sub * KC + kc), BUF_NT);
-      ws[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (sub * groups + rec) * 256, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(buf + wsc + ns * 256), 4, s_voff,
+                                               (sub * groups + rec) * 256, 0, 0);
     }
   };
-  // Chunk kc (stage kc % 3) issues chunk kc + 2 into the stage chunk kc - 1
-  // used, computes, then waits until only those loads are outstanding: chunk
-  // kc + 1 has then landed for every wave when the barrier opens.
+  // Chunk kc (stage kc % NST) issues chunk kc + NST - 1 into the stage that
+  // chunk kc - 1 used, computes, then waits until only the loads of the
+  // chunks after kc + 1 are outstanding: chunk kc + 1 has then landed for
+  // every wave when the barrier opens.  Chunks past the last re-load it into
+  // a stage nobody reads any more.
   auto chunk = [&](auto sc, int kc) {
     constexpr int d = decltype(sc)::value;
-    issue(std::integral_constant<int, (d + 2) % Q_STAGES>{}, min(kc + 2, KC - 1));
+    issue(std::integral_constant<int, (d + NST - 1) % NST>{}, min(kc + NST - 1, KC - 1));
     const uint8_t* buf = s_q + d * Q_STAGE_BYTES;
     uint32_t sb[TL_NS];
 #pragma unroll
-    for (int ns = 0; ns < TL_NS; ++ns) sb[ns] = (ws[d][ns] >> (8 * (kc & 3))) & 0xFFu;
+    for (int ns = 0; ns < TL_NS; ++ns)
+      sb[ns] = w4a4_block_scale<FMT>(*reinterpret_cast<const uint32_t*>(buf + wsc + ns * 256 + lane * 4), kc, bad);
 #pragma unroll
     for (int ms = 0; ms < NSUB; ++ms) {
       const int row = ms * 16 + r;
@@ -863,33 +913,41 @@ __device__ __forceinline__ void w4a4_k_walk(uint8_t* s_q, __amdgpu_buffer_rsrc_t
 #pragma unroll
       for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = mfma_fp4(a, sa, cs[d][ns], sb[ns], acc[ms][ns]);
     }
-    vm_wait_barrier<Q_ISSUE>();
+    vm_wait_barrier<Q_ISSUE * (NST - 2)>();
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
-  static_assert(Q_STAGES == 3, "the walk below is unrolled for three stages");
   issue(S0{}, 0);
-  issue(S1{}, min(1, KC - 1));
-  vm_wait_barrier<Q_ISSUE>();
+  if constexpr (NST == 3) issue(S1{}, min(1, KC - 1));
+  vm_wait_barrier<Q_ISSUE * (NST - 2)>();
   int k0 = 0;
-  for (; k0 + 3 <= KC; k0 += 3) {
-    chunk(S0{}, k0);
-    chunk(S1{}, k0 + 1);
-    chunk(S2{}, k0 + 2);
+  if constexpr (NST == 3) {
+    for (; k0 + 3 <= KC; k0 += 3) {
+      chunk(S0{}, k0);
+      chunk(S1{}, k0 + 1);
+      chunk(S2{}, k0 + 2);
+    }
+    if (k0 < KC) chunk(S0{}, k0);
+    if (k0 + 1 < KC) chunk(S1{}, k0 + 1);
+  } else {
+    for (; k0 + 2 <= KC; k0 += 2) {
+      chunk(S0{}, k0);
+      chunk(S1{}, k0 + 1);
+    }
+    if (k0 < KC) chunk(S0{}, k0);
   }
-  if (k0 < KC) chunk(S0{}, k0);
-  if (k0 + 1 < KC) chunk(S1{}, k0 + 1);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>());
 }
 
-template <bool OBF16, int ACT>
+template <int FMT, bool OBF16, int ACT>
 __global__ __launch_bounds__(256, 2) void gmm_w4a4_kernel(const uint8_t* __restrict__ packed, Layout L,
                                                           const uint8_t* __restrict__ qcodes,
                                                           const uint8_t* __restrict__ qscales, int32_t x_rows,
                                                           const int32_t* __restrict__ row_index,
                                                           const int32_t* __restrict__ goff, int E,
-                                                          void* __restrict__ y, int NB) {
+                                                          void* __restrict__ y, int NB,
+                                                          int32_t* __restrict__ err_count) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_q[Q_STAGES * Q_STAGE_BYTES];
 
   const int lane = threadIdx.x & 63;
@@ -899,7 +957,7 @@ __global__ __launch_bounds__(256, 2) void gmm_w4a4_kernel(const uint8_t* __restr
   if (item < 0) return;
   const int t = item / NB;
   const int nb = item - t * NB;
-  const Tile tile = locate_tile(goff, E, TL_BM, ts, t);
+  const Tile tile = locate_tile(E, TL_BM, ts, t);
   const int K = (int)L.K;
   const int KC = (int)L.KC;
   const int groups = (int)L.groups;
@@ -951,18 +1009,26 @@ __global__ __launch_bounds__(256, 2) void gmm_w4a4_kernel(const uint8_t* __restr
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  int bad = 0;
+  constexpr int NST = FMT == 0 ? 3 : 2;
   switch (nsub) {
-    case 1: w4a4_k_walk<1, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
-    case 2: w4a4_k_walk<2, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
-    case 3: w4a4_k_walk<3, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
-    case 4: w4a4_k_walk<4, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
-    case 5: w4a4_k_walk<5, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
-    case 6: w4a4_k_walk<6, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
-    case 7: w4a4_k_walk<7, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
-    default: w4a4_k_walk<8, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc); break;
+    case 1: w4a4_k_walk<1, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    case 2: w4a4_k_walk<2, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    case 3: w4a4_k_walk<3, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    case 4: w4a4_k_walk<4, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    case 5: w4a4_k_walk<5, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    case 6: w4a4_k_walk<6, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    case 7: w4a4_k_walk<7, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    default: w4a4_k_walk<8, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
   }
 
   if (!wave_active) return;
+  if (FMT == 1 && err_count && tile.first) {
+    // each weight block is counted once: by its expert's first tile
+    for (int d = 32; d > 0; d >>= 1) bad += __shfl_xor(bad, d, 64);
+    if (lane == 0 && bad) atomicAdd(err_count, bad);
+  }
+  const float post = FMT == 1 ? reinterpret_cast<const float*>(packed + L.tscale_off)[tile.e] : 1.0f;
 #pragma unroll
   for (int ms = 0; ms < TL_MS; ++ms) {
     if (ms < nsub) {
@@ -970,42 +1036,55 @@ __global__ __launch_bounds__(256, 2) void gmm_w4a4_kernel(const uint8_t* __restr
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           store_tile_silu_mul<OBF16>(y, L.N / 2, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + j * 16 + r,
-                                     acc[ms][j], acc[ms][j + 2], 1.0f);
+                                     acc[ms][j], acc[ms][j + 2], post);
       } else {
 #pragma unroll
         for (int ns = 0; ns < TL_NS; ++ns)
           store_tile<OBF16>(y, L.N, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + ns * 16 + r,
-                            acc[ms][ns], 1.0f);
+                            acc[ms][ns], post);
       }
     }
   }
 }
 
-template <bool OBF16, int ACT>
+template <int FMT, bool OBF16, int ACT>
 static void launch_w4a4_t(const uint8_t* packed, const Layout& L, const uint8_t* qcodes, const uint8_t* qscales,
                           int32_t x_rows, const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
-                          void* y, hipStream_t stream) {
+                          void* y, int32_t* err_count, hipStream_t stream) {
   const int64_t em = E < M ? E : M;
   const int64_t cols = ACT == 1 ? L.N / 2 : L.N;
   const int bn = ACT == 1 ? TL_BN / 2 : TL_BN;
   const int NB = (int)((cols + bn - 1) / bn);
   const int64_t tiles = (M + TL_BM - 1) / TL_BM + em;
-  hipLaunchKernelGGL((gmm_w4a4_kernel<OBF16, ACT>), dim3((unsigned)(tiles * NB)), dim3(64 * TL_WAVES), 0,
-                     stream, packed, L, qcodes, qscales, x_rows, row_index, goff, E, y, NB);
+  hipLaunchKernelGGL((gmm_w4a4_kernel<FMT, OBF16, ACT>), dim3((unsigned)(tiles * NB)), dim3(64 * TL_WAVES), 0,
+                     stream, packed, L, qcodes, qscales, x_rows, row_index, goff, E, y, NB, err_count);
 }
 
-hipError_t launch_gmm_w4a4(const uint8_t* packed, int32_t E, int32_t N, int32_t K, const uint8_t* qcodes,
+template <int FMT>
+static void launch_w4a4_f(const uint8_t* packed, const Layout& L, const uint8_t* qcodes, const uint8_t* qscales,
+                          int32_t x_rows, const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
+                          void* y, int y_bf16, int act, int32_t* err_count, hipStream_t stream) {
+  if (act == 1) {
+    if (y_bf16) launch_w4a4_t<FMT, true, 1>(packed, L, qcodes, qscales, x_rows, row_index, goff, E, M, y, err_count, stream);
+    else launch_w4a4_t<FMT, false, 1>(packed, L, qcodes, qscales, x_rows, row_index, goff, E, M, y, err_count, stream);
+  } else {
+    if (y_bf16) launch_w4a4_t<FMT, true, 0>(packed, L, qcodes, qscales, x_rows, row_index, goff, E, M, y, err_count, stream);
+    else launch_w4a4_t<FMT, false, 0>(packed, L, qcodes, qscales, x_rows, row_index, goff, E, M, y, err_count, stream);
+  }
+}
+
+hipError_t launch_gmm_w4a4(const uint8_t* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint8_t* qcodes,
                            const uint8_t* qscales, int32_t x_rows, const int32_t* row_index,
                            const int32_t* group_offsets, int32_t M, void* y, int y_bf16, int act,
-                           hipStream_t stream) {
-  const Layout L = make_layout(0, E, N, K);
-  if (act == 1) {
-    if (y_bf16) launch_w4a4_t<true, 1>(packed, L, qcodes, qscales, x_rows, row_index, group_offsets, E, M, y, stream);
-    else launch_w4a4_t<false, 1>(packed, L, qcodes, qscales, x_rows, row_index, group_offsets, E, M, y, stream);
-  } else {
-    if (y_bf16) launch_w4a4_t<true, 0>(packed, L, qcodes, qscales, x_rows, row_index, group_offsets, E, M, y, stream);
-    else launch_w4a4_t<false, 0>(packed, L, qcodes, qscales, x_rows, row_index, group_offsets, E, M, y, stream);
-  }
+                           int32_t* err_count, hipStream_t stream) {
+  const Layout L = make_layout(fmt, E, N, K);
+  if (err_count) launch_zero_i32(err_count, 1, stream);
+  if (fmt == 1)
+    launch_w4a4_f<1>(packed, L, qcodes, qscales, x_rows, row_index, group_offsets, E, M, y, y_bf16, act, err_count,
+                     stream);
+  else
+    launch_w4a4_f<0>(packed, L, qcodes, qscales, x_rows, row_index, group_offsets, E, M, y, y_bf16, act, err_count,
+                     stream);
   return hipGetLastError();
 }
 

@@ -47,12 +47,18 @@ hipError_t launch_gmm(const uint8_t* packed, int fmt, int32_t E, int32_t N, int3
                       const int32_t* group_offsets,
                       int32_t M, void* y, int y_bf16, int act, int kernel, hipStream_t stream);
 
-// W4A4: MXFP4 weights (fmt 0) times MXFP4-quantized activations (codes
-// [x_rows, K/2], E8M0 scales [x_rows, K/32]) on the scaled FP4 MFMA.
-hipError_t launch_gmm_w4a4(const uint8_t* packed, int32_t E, int32_t N, int32_t K, const uint8_t* qcodes,
+// W4A4: MXFP4 (fmt 0) or NVFP4 (fmt 1, power-of-two block scales) weights
+// times MXFP4-quantized activations (codes [x_rows, K/2], E8M0 scales
+// [x_rows, K/32]) on the scaled FP4 MFMA; err_count (may be NULL) receives the
+// NVFP4 blocks whose scales do not qualify.
+hipError_t launch_gmm_w4a4(const uint8_t* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint8_t* qcodes,
                            const uint8_t* qscales, int32_t x_rows, const int32_t* row_index,
                            const int32_t* group_offsets, int32_t M, void* y, int y_bf16, int act,
-                           hipStream_t stream);
+                           int32_t* err_count, hipStream_t stream);
+
+// Sets n int32 to zero with a kernel (no memset node, so the call stays safe
+// to record into a HIP graph).
+void launch_zero_i32(int32_t* p, int n, hipStream_t stream);
 
 hipError_t launch_quantize_mxfp4(const uint16_t* x, int32_t R, int32_t K, uint8_t* codes, uint8_t* scales,
                                  hipStream_t stream);

@@ -439,12 +439,12 @@ def _w4a4_ref(p, w):
                            ref_r["group_offsets"], w)
 
 
-def _run_w4a4(p, packed, out_dtype=moe.F32, act=moe.ACT_NONE):
+def _run_w4a4(p, packed, out_dtype=moe.F32, act=moe.ACT_NONE, fmt=moe.MXFP4, err_count=None):
     r = moe.route_sort(to_dev(p["topk_ids"]), p["E"])
     qc, qs = moe.mxfp4_quantize(to_dev(p["x"]))
     return moe.moe_gmm_w4a4(packed, p["E"], p["N"], p["K"], qc, qs, r["group_offsets"], p["T"] * p["k"],
                             row_index=r["sorted_token"] if p["gather"] else None,
-                            out_dtype=out_dtype, act=act)
+                            out_dtype=out_dtype, act=act, fmt=fmt, err_count=err_count)
 
 
 @pytest.mark.parametrize("case", ["banded", "gathered", "band_input"])
@@ -464,6 +464,70 @@ def test_gmm_w4a4_full_oracle(case):
     if p["N"] % 128 == 0:
         ya = _run_w4a4(p, packed, act=moe.ACT_SILU_MUL)
         assert rel_err(ya.cpu().numpy(), oracle.silu_mul(ref)) <= REL_TOL
+
+
+@pytest.mark.parametrize("case", ["banded", "gathered", "band_input"])
+def test_gmm_w4a4_nvfp4_weights(case):
+    # NVFP4 weights from the lossless cast (both E4M3 halves of a block one
+    # equal power of two) through the W4A4 kernel: the oracle's W4A4 matmul
+    # on the NVFP4 decode within the bound, and bitwise the output of the
+    # MXFP4 weights the cast came from, for every output form; no block is
+    # counted
+    if case == "banded":
+        p = _banded_problem(312)
+    elif case == "gathered":
+        p = make_problem(T=96, k=4, E=8, K=512, N=512, seed=313, routing="zipf", exp_range=(-12, 3))
+    else:
+        p = _small(2)
+    w_nv, packed_nv = weights_for(p, "nvfp4")
+    _, packed_mx = weights_for(p, "mxfp4")
+    err = torch.full((1,), -5, dtype=torch.int32, device=DEV)
+    y = _run_w4a4(p, packed_nv, fmt=moe.NVFP4, err_count=err)
+    assert err.item() == 0
+    assert rel_err(y.cpu().numpy(), _w4a4_ref(p, w_nv)) <= REL_TOL
+    assert torch.equal(y, _run_w4a4(p, packed_mx))
+    for odt, act in ((moe.BF16, moe.ACT_NONE), (moe.F32, moe.ACT_SILU_MUL), (moe.BF16, moe.ACT_SILU_MUL)):
+        if act == moe.ACT_SILU_MUL and p["N"] % 128:
+            continue
+        a = _run_w4a4(p, packed_nv, out_dtype=odt, act=act, fmt=moe.NVFP4)
+        b = _run_w4a4(p, packed_mx, out_dtype=odt, act=act)
+        assert torch.equal(a, b), (odt, act)
+
+
+def test_gmm_w4a4_nvfp4_counts_blocks_that_do_not_qualify():
+    # blocks whose two E4M3 scales differ or are not a power of two are
+    # counted once each (every expert has one tile here), whatever the number
+    # of waves that read them; blocks of experts with no rows are not used
+    p = make_problem(T=24, k=2, E=6, K=256, N=128, seed=314, empty_experts=(5,))
+    bs, ts = oracle.mxfp4_to_nvfp4(p["scales"])
+    bad = bs.copy()
+    planted = [(0, 3, 2, 0x39, 0x38), (1, 100, 5, 0x40, 0x48), (2, 17, 0, 0x00, 0x00), (4, 127, 7, 0x38, 0x30),
+               (5, 0, 0, 0x39, 0x39)]          # the last in the empty expert 5
+    for e, n, j, lo, hi in planted:
+        bad[e, n, 2 * j], bad[e, n, 2 * j + 1] = lo, hi
+    packed = moe.mxfp4_encode(to_dev(p["codes"]), to_dev(bad), to_dev(ts), moe.NVFP4)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    _run_w4a4(p, packed, fmt=moe.NVFP4, err_count=err)
+    assert err.item() == 4
+    _run_w4a4(p, packed, fmt=moe.NVFP4, err_count=err, act=moe.ACT_SILU_MUL, out_dtype=moe.BF16)
+    assert err.item() == 4
+
+
+@pytest.mark.slow
+def test_config5_w4a4_nvfp4_equals_mxfp4_bitwise():
+    # the NVFP4 workload (config 5, scales from the library's own cast)
+    # through the W4A4 kernel equals the MXFP4 weights' output bit for bit
+    p = make_config(5)
+    _, packed_mx = weights_for(p, "mxfp4")
+    bs, ts, err = moe.mxfp4_to_nvfp4(to_dev(p["scales"]))
+    assert err.item() == 0
+    packed_nv = moe.mxfp4_encode(to_dev(p["codes"]), bs, ts, moe.NVFP4)
+    cnt = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    a = _run_w4a4(p, packed_nv, fmt=moe.NVFP4, err_count=cnt)
+    b = _run_w4a4(p, packed_mx)
+    assert cnt.item() == 0
+    assert torch.equal(a, b)
+    del packed_mx, packed_nv
 
 
 def test_w4a4_layer_chain_small():

@@ -106,3 +106,38 @@ def test_gmm_w4a4_brute_force():
                         * math.ldexp(1.0, int(p["scales"][e, n, kk // 32]) - 127)
                     ref += xa * wb
                 assert abs(y[row, n] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def _e4m3_val(b):
+    """E4M3FN byte from its bit fields (finite bytes only): bias 7, subnormal
+    at exponent field 0."""
+    ex, m = (b >> 3) & 0xF, b & 7
+    v = (m / 8.0) * 2.0 ** -6 if ex == 0 else (1 + m / 8.0) * 2.0 ** (ex - 7)
+    return -v if b & 0x80 else v
+
+
+def test_gmm_w4a4_nvfp4_brute_force():
+    # NVFP4 weights (arbitrary finite E4M3 block scales, a tensor scale per
+    # expert) under the W4A4 oracle, every nibble and scale decoded from its
+    # bit fields
+    p = make_problem(T=4, k=2, E=3, K=64, N=5, seed=17)
+    rng = np.random.default_rng(18)
+    bs = rng.integers(0, 0x7F, size=(3, 5, 4)).astype(np.uint8)
+    ts = np.array([0.5, 3.0, 2.0 ** -7], dtype=np.float32)
+    qc, qs = oracle.quantize_mxfp4_rows(p["x"])
+    r = oracle.route_sort(p["topk_ids"], p["E"])
+    w = {"fmt": "nvfp4", "codes": p["codes"], "block_scales": bs, "tensor_scale": ts}
+    y = oracle.gmm_w4a4(qc, qs, r["sorted_token"], r["group_offsets"], w)
+    for t in range(p["T"]):
+        for j in range(p["k"]):
+            e = int(p["topk_ids"][t, j])
+            row = r["pair_row"][t * p["k"] + j]
+            for n in range(p["N"]):
+                ref = 0.0
+                for kk in range(p["K"]):
+                    xa = _e2m1_val((int(qc[t, kk // 2]) >> (4 * (kk % 2))) & 0xF) \
+                        * math.ldexp(1.0, int(qs[t, kk // 32]) - 127)
+                    wb = _e2m1_val((int(p["codes"][e, n, kk // 2]) >> (4 * (kk % 2))) & 0xF) \
+                        * _e4m3_val(int(bs[e, n, kk // 16])) * float(ts[e])
+                    ref += xa * wb
+                assert abs(y[row, n] - ref) <= 1e-12 * (1 + abs(ref))
