@@ -64,16 +64,18 @@ FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 MFMA, published
 METRIC = "moe_gmm TFLOP/s and HBM GB/s (% roofline), w13/w2, 256 experts top-6"
 
 GMM_WORKLOADS = {
-    "tiny": 1, "w13_decode": 2, "w2_decode": 3, "w13_prefill": 4, "nvfp4_w13": 5,
+    "tiny": 1, "w13_decode": 2, "w2_decode": 3, "w13_prefill": 4, "nvfp4_w13": 5, "nvfp4_w13_prefill": 4,
     "bf16_w13_decode": 2, "bf16_w2_decode": 3, "bf16_w13_prefill": 4,
 }
+NVFP4_GMM = ("nvfp4_w13", "nvfp4_w13_prefill")   # NVFP4 weights from the lossless cast
 LAYER_WORKLOADS = ("layer_decode", "layer_prefill", "w4a4_layer_prefill")
 # W4A4 grouped matmul: config, weight format
 W4A4_WORKLOADS = {"w4a4_w13_prefill": (4, "mxfp4"), "w4a4_nvfp4_w13_prefill": (4, "nvfp4"),
                   "w4a4_nvfp4_w13": (5, "nvfp4")}
 WORKLOADS = sorted(list(GMM_WORKLOADS) + list(LAYER_WORKLOADS) + list(W4A4_WORKLOADS))
 # timed after the headline in the default run
-EXTRA_WORKLOADS = ("tiny", "w2_decode", "w13_prefill", "nvfp4_w13", "layer_decode", "layer_prefill")
+EXTRA_WORKLOADS = ("tiny", "w2_decode", "w13_prefill", "nvfp4_w13", "nvfp4_w13_prefill", "layer_decode",
+                   "layer_prefill")
 KERNELS = {"auto": 0, "stream": 1, "tiled": 2}
 GMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_route_amd", "csrc", "gmm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
@@ -292,7 +294,7 @@ def run_gmm(gpu, workload, steps, warmup, cpu_s, kernel="auto", out_dtype=None, 
     cfg = GMM_WORKLOADS[workload]
     p = make_config(cfg) if tokens is None else make_tokens_problem(cfg, tokens)
     bf16_arm = workload.startswith("bf16_")
-    fmt = "nvfp4" if cfg == 5 else "mxfp4"
+    fmt = "nvfp4" if workload in NVFP4_GMM else "mxfp4"
     out_dtype = out_dtype or p["out"]
     odt = moe.BF16 if out_dtype == "bf16" else moe.F32
     E, K, N, T, k = p["E"], p["K"], p["N"], p["T"], p["k"]
@@ -300,16 +302,17 @@ def run_gmm(gpu, workload, steps, warmup, cpu_s, kernel="auto", out_dtype=None, 
 
     ids, x = gpu.put(p["topk_ids"]), gpu.put(p["x"])
     codes = gpu.put(p["codes"])
-    if fmt == "mxfp4":
-        packed = moe.mxfp4_encode(codes, gpu.put(p["scales"]), None, moe.MXFP4)
-        wf = moe.MXFP4
-    else:
-        bs, ts, err = moe.mxfp4_to_nvfp4(gpu.put(p["scales"]))
-        packed = moe.mxfp4_encode(codes, bs, ts, moe.NVFP4)
-        wf = moe.NVFP4
-        assert err.item() == 0
-    del codes
+    packed = moe.mxfp4_encode(codes, gpu.put(p["scales"]), None, moe.MXFP4)
+    wf = moe.MXFP4
     packed_mx = None
+    if fmt == "nvfp4":
+        # the same weights through the lossless cast; the MXFP4 kernel on the
+        # MXFP4 pack is timed beside them
+        bs, ts, err = moe.mxfp4_to_nvfp4(gpu.put(p["scales"]))
+        assert err.item() == 0
+        packed_mx, packed = packed, moe.mxfp4_encode(codes, bs, ts, moe.NVFP4)
+        wf = moe.NVFP4
+    del codes
     if bf16_arm:
         # the comparison arm streams the decoded weights as bf16
         dense = moe.debug_decode(packed, wf, E, N, K)
@@ -343,8 +346,8 @@ def run_gmm(gpu, workload, steps, warmup, cpu_s, kernel="auto", out_dtype=None, 
     wall, ev = gpu.timed_steps(step, steps, warmup)
 
     mx_ms = None
-    if bf16_arm:
-        # the MXFP4 kernel on the same inputs, for the speedup
+    if packed_mx is not None:
+        # the MXFP4 kernel on the same inputs, for the comparison
         r = moe.route_sort(ids, E, ws=ws)
         for _ in range(warmup):
             gmm(packed_mx, moe.MXFP4, r)
@@ -390,7 +393,7 @@ def run_gmm(gpu, workload, steps, warmup, cpu_s, kernel="auto", out_dtype=None, 
     if mx_ms is not None:
         mx_s = float(np.mean(mx_ms)) / 1e3
         out["mxfp4_us"] = round(mx_s * 1e6, 2)
-        out["mxfp4_speedup_over_bf16"] = round(gmm_s / mx_s, 3)
+        out["mxfp4_speedup_over_" + fmt] = round(gmm_s / mx_s, 3)
     if cpu_s > 0:
         out["cpu_baseline"] = cpu_baseline(p, "mxfp4" if bf16_arm else fmt, unit, target_s=cpu_s)
         out["gpu_over_cpu"] = round(value / out["cpu_baseline"]["value"], 1)

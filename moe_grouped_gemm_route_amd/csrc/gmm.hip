@@ -140,10 +140,12 @@ __device__ __forceinline__ void chunk_scales(uint32_t word, int kc, float& lo, f
   }
 }
 
-// NVFP4 chunks whose E4M3 scales are all powers of two (for instance every
-// chunk made by the lossless MXFP4 cast) take the one-instruction decode; a
-// wave with any other scale in the chunk takes the general exact decode.
-// Both give the same bits.
+// Stream kernel: NVFP4 chunks whose E4M3 scales are all powers of two (for
+// instance every chunk made by the lossless MXFP4 cast) take the
+// one-instruction decode; a wave with any other scale in the chunk takes the
+// general exact decode.  Both give the same bits.  (The tiled kernel makes
+// this choice once per walk: its unrolled chunk has no registers for two
+// decode paths.)
 template <int FMT, int NS>
 __device__ __forceinline__ bool general_scales(const float (&lo)[NS], const float (&hi)[NS]) {
   if (FMT == 0) return false;
@@ -501,16 +503,19 @@ __device__ __forceinline__ uint32_t stage_soff(int kn, int KC) {
 // for the fragment's read, issue its NS MFMAs, then issue the read of
 // fragment f + P - 1 into the register of fragment f - 1 (whose MFMAs were
 // issued one fragment earlier).
-template <int NSUB, int P, int BUF, int FMT, int F>
+template <int NSUB, int P, int BUF, bool GEN, int F>
 __device__ __forceinline__ void tiled_fragment(u32x4_t (&ar)[P], const uint32_t (&va)[4],
                                                u32x4_t (&b)[TL_NS], const u32x4_t (&cw)[TL_NS],
                                                const float (&lo)[TL_NS], const float (&hi)[TL_NS],
-                                               bool general, f32x4_t (&acc)[TL_MS][TL_NS]) {
+                                               f32x4_t (&acc)[TL_MS][TL_NS]) {
   constexpr int FT = 4 * NSUB;
   constexpr int s = F / NSUB, ms = F % NSUB;
   if constexpr (ms == 0) {
 #pragma unroll
-    for (int ns = 0; ns < TL_NS; ++ns) b[ns] = decode_step<FMT>(cw[ns][s], s < 2 ? lo[ns] : hi[ns], general);
+    for (int ns = 0; ns < TL_NS; ++ns) {
+      const float sc = s < 2 ? lo[ns] : hi[ns];
+      b[ns] = GEN ? decode8_any_scale(cw[ns][s], sc) : decode8(cw[ns][s], sc);
+    }
   }
   constexpr int newest = (F + P - 2 < FT - 1) ? F + P - 2 : FT - 1;
   lds_read_wait<newest - F>(ar[F % P]);
@@ -521,12 +526,12 @@ __device__ __forceinline__ void tiled_fragment(u32x4_t (&ar)[P], const uint32_t 
     ar[NF % P] = lds_read16<(NF % NSUB) * 16 * TL_ROW_BYTES + BUF * TL_BUF_BYTES>(va[NF / NSUB]);
 }
 
-template <int NSUB, int P, int BUF, int FMT, size_t... Fs>
+template <int NSUB, int P, int BUF, bool GEN, size_t... Fs>
 __device__ __forceinline__ void tiled_chunk(std::index_sequence<Fs...>, u32x4_t (&ar)[P], const uint32_t (&va)[4],
                                             u32x4_t (&b)[TL_NS], const u32x4_t (&cw)[TL_NS],
-                                            const float (&lo)[TL_NS], const float (&hi)[TL_NS], bool general,
+                                            const float (&lo)[TL_NS], const float (&hi)[TL_NS],
                                             f32x4_t (&acc)[TL_MS][TL_NS]) {
-  (tiled_fragment<NSUB, P, BUF, FMT, (int)Fs>(ar, va, b, cw, lo, hi, general, acc), ...);
+  (tiled_fragment<NSUB, P, BUF, GEN, (int)Fs>(ar, va, b, cw, lo, hi, acc), ...);
 }
 
 template <int NSUB, int P, int BUF, size_t... Is>
@@ -623,8 +628,10 @@ __device__ __forceinline__ void tiled_k_walk_bf16(uint8_t* s_a, __amdgpu_buffer_
   __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>());
 }
 
-// The K walk of one wave for a tile with NSUB valid 16-row subtiles.
-template <int NSUB, int FMT, int ACT>
+// The K walk of one wave for a tile with NSUB valid 16-row subtiles.  GEN
+// (NVFP4 only): some block scale of the wave's columns is not a power of
+// two, so every step takes the general exact decode.
+template <int NSUB, int FMT, int ACT, bool GEN = false>
 __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_t xr,
                                              const uint32_t (&avo)[TL_LOADS], __amdgpu_buffer_rsrc_t cr,
                                              __amdgpu_buffer_rsrc_t sr, int KC, int groups, int h16, int wave,
@@ -663,11 +670,10 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
     float lo[TL_NS], hi[TL_NS];
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) chunk_scales<FMT>(ws[d][ns], kc, lo[ns], hi[ns]);
-    const bool general = general_scales<FMT, TL_NS>(lo, hi);
     u32x4_t ar[P];
     u32x4_t b[TL_NS];
     tiled_prologue<NSUB, P, d>(std::make_index_sequence<PRO>{}, ar, va);
-    tiled_chunk<NSUB, P, d, FMT>(std::make_index_sequence<FT>{}, ar, va, b, cs[d], lo, hi, general, acc);
+    tiled_chunk<NSUB, P, d, GEN>(std::make_index_sequence<FT>{}, ar, va, b, cs[d], lo, hi, acc);
     vm_wait_barrier<2 * TL_NS>();
   };
   using B0 = std::integral_constant<int, 0>;
@@ -683,6 +689,45 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
   }
   if (k0 < KC) chunk(B0{}, k0);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>());
+}
+
+// Flags (bit 7 of each byte) the E4M3 bytes of w that are not a positive
+// power of two: a sign, a zero, a normal with a nonzero mantissa (NaN
+// included), or a subnormal whose mantissa has more than one bit.  Byte-wise
+// arithmetic: every partial value stays below 0x80 per byte, so no carry or
+// borrow crosses a byte.
+__device__ __forceinline__ uint32_t e4m3x4_not_pow2(uint32_t w) {
+  constexpr uint32_t H = 0x80808080u, L7 = 0x7F7F7F7Fu;
+  const uint32_t m = w & 0x07070707u, e = w & 0x78787878u;
+  const uint32_t mnz = (m + L7) & H, enz = (e + L7) & H;
+  const uint32_t mbad = ((((m | H) - 0x01010101u) & m) + L7) & H;   // m & (m - 1) != 0
+  return (w & H) | (mnz & enz) | (~enz & H & (~mnz | mbad));
+}
+
+// True when every block scale (E4M3) in the wave's columns is a positive
+// power of two, the case the one-instruction decode handles exactly.
+// The words go in batches of SB records per subtile, all issued before any
+// is tested, so a batch costs one round trip.
+template <int NS, int ACT>
+__device__ __forceinline__ bool span_scales_pow2(__amdgpu_buffer_rsrc_t sr, int groups, int h16) {
+  constexpr int SB = 8;
+  const uint32_t voff = (threadIdx.x & 63) * 4;
+  uint32_t bad = 0;
+  for (int rec0 = 0; rec0 < groups; rec0 += SB) {
+    uint32_t w[NS][SB];
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      const int sub = col_sub<ACT>(ns, h16);
+#pragma unroll
+      for (int i = 0; i < SB; ++i)   // records past the subtile's read its neighbour's (or zeros): not tested
+        w[ns][i] = __builtin_amdgcn_raw_buffer_load_b32(sr, voff, (sub * groups + rec0 + i) * 256, 0);
+    }
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+      for (int i = 0; i < SB; ++i) bad |= rec0 + i < groups ? e4m3x4_not_pow2(w[ns][i]) : 0u;
+  }
+  return __ballot(bad != 0) == 0;
 }
 
 template <int FMT, bool OBF16, int ACT>
@@ -759,6 +804,10 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
       case 7: tiled_k_walk_bf16<7, ACT>(s_a, xr, avo, cr, KC, h16, wave, va, acc); break;
       default: tiled_k_walk_bf16<8, ACT>(s_a, xr, avo, cr, KC, h16, wave, va, acc); break;
     }
+  } else if (FMT == 1 && wave_active && !span_scales_pow2<TL_NS, ACT>(sr, groups, h16)) {
+    // general E4M3 scales: one walk over all eight subtiles (the rows past
+    // the band are zeros in LDS and are never stored)
+    tiled_k_walk<8, FMT, ACT, true>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc);
   } else switch (nsub) {
     case 1: tiled_k_walk<1, FMT, ACT>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc); break;
     case 2: tiled_k_walk<2, FMT, ACT>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc); break;

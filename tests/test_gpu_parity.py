@@ -289,6 +289,33 @@ def test_gmm_nvfp4_general_e4m3_scales(kernel):
     assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("act", [moe.ACT_NONE, moe.ACT_SILU_MUL])
+def test_gmm_nvfp4_scale_kinds_mixed_across_waves(act, kernel):
+    # per expert: only powers of two (the cast's scales); general E4M3 scales
+    # in one 16-column strip only (one wave of a workgroup decodes them, the
+    # others do not); a few zero scales among powers of two
+    E, N = 9, 384
+    p = make_problem(T=96, k=4, E=E, K=512, N=N, seed=252, routing="zipf")
+    rng = np.random.default_rng(253)
+    bs = (rng.integers(1, 16, size=(E, N, 32)) << 3).astype(np.uint8)   # 2^-6 .. 2^8
+    for e in range(E):
+        if e % 3 == 1:
+            c0 = 16 * (e % (N // 16))
+            bs[e, c0:c0 + 16] = rng.integers(0x20, 0x50, size=(16, 32))
+        elif e % 3 == 2:
+            bs[e, rng.integers(0, N, 5), rng.integers(0, 32, 5)] = 0
+    p["block_scales"] = bs
+    p["tensor_scale"] = np.ldexp(1.0, rng.integers(-4, 4, size=E)).astype(np.float32)
+    w, packed = weights_for(p, "nvfp4")
+    _, y = run_gpu(p, packed, "nvfp4", kernel=kernel, act=act)
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    ref = oracle.gmm(p["x"], ref_r["sorted_token"], ref_r["group_offsets"], w)
+    if act == moe.ACT_SILU_MUL:
+        ref = oracle.silu_mul(ref)
+    assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
+
+
 # ---------------------------------------- fused gate/up activation ---
 
 def _act_problems():
