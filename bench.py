@@ -245,6 +245,10 @@ class Gpu:
         self.torch, self.moe = torch, moe
         self.dev = torch.device("cuda", 0)
         torch.cuda.set_device(self.dev)
+        # warm-up floor in seconds of device time, besides the step count;
+        # warmup_done is the number of warm-up steps the last run took
+        self.min_warmup_s = 0.0
+        self.warmup_done = 0
 
     def put(self, a):
         a = np.ascontiguousarray(a)
@@ -260,12 +264,19 @@ class Gpu:
         return self.torch.cuda.Event(enable_timing=True)
 
     def timed_steps(self, step, steps, warmup):
-        """warmup untimed steps, then exactly `steps` steps between two
-        device synchronisations; step(timed) returns its kernel events or
-        None.  Returns (wall seconds, list of event tuples)."""
-        for _ in range(warmup):
+        """warmup untimed steps (and more until min_warmup_s has passed, for
+        the shader clock to settle under sustained matrix work), then exactly
+        `steps` steps between two device synchronisations; step(timed)
+        returns its kernel events or None.  Returns (wall seconds, list of
+        event tuples)."""
+        n, t0 = 0, time.perf_counter()
+        while n < warmup or time.perf_counter() - t0 < self.min_warmup_s:
             step(False)
+            n += 1
+            if n % 8 == 0:
+                self.torch.cuda.synchronize()
         self.torch.cuda.synchronize()
+        self.warmup_done = n
         ev = []
         t0 = time.perf_counter()
         for _ in range(steps):
@@ -374,7 +385,7 @@ def run_gmm(gpu, workload, steps, warmup, cpu_s, kernel="auto", out_dtype=None, 
               "weights": fmt + (" (decoded MXFP4 weights)" if bf16_arm else ""),
               "activations": "bf16", "output": out_dtype, "kernel": kernel,
               "step": "route_sort + moe_gmm" + (" + moe_combine" if combine else "")}
-    out = base_line(workload, steps, warmup, step_s, value, unit, "bf16", config)
+    out = base_line(workload, steps, gpu.warmup_done, step_s, value, unit, "bf16", config)
     out.update({
         "gmm_us": round(gmm_s * 1e6, 2),
         "gmm_us_median": round(float(np.median(gmm_ms)) * 1e3, 2),
@@ -481,7 +492,7 @@ def run_layer(gpu, workload, steps, warmup, cpu_s):
               "step": ("route_sort + mxfp4_quantize(x) + moe_gmm_w4a4(w13, act) + mxfp4_quantize(h) "
                        "+ moe_gmm_w4a4(w2) + moe_combine") if w4a4 else
                       "route_sort + moe_gmm(w13, act) + moe_gmm(w2) + moe_combine"}
-    out = base_line(workload, steps, warmup, step_s, value, unit, "fp4" if w4a4 else "bf16", config)
+    out = base_line(workload, steps, gpu.warmup_done, step_s, value, unit, "fp4" if w4a4 else "bf16", config)
     out.update({
         "w13_us": round(t13 * 1e6, 2),
         "w2_us": round(t2 * 1e6, 2),
@@ -557,7 +568,7 @@ def run_w4a4(gpu, workload, steps, warmup):
               "step": "route_sort + mxfp4_quantize + moe_gmm_w4a4"}
     rate, unit = (flops / step_s / 1e12, "TFLOP/s") if roof["bound"] == "mfma" or cfg == 4 else \
         (nbytes / step_s / 1e9, "GB/s")
-    out = base_line(workload, steps, warmup, step_s, rate, unit, "fp4", config)
+    out = base_line(workload, steps, gpu.warmup_done, step_s, rate, unit, "fp4", config)
     out.update({
         "gmm_us": round(gmm_s * 1e6, 2),
         "gmm_us_median": round(float(np.median(gmm_ms)) * 1e3, 2),
@@ -642,7 +653,9 @@ def summary(line):
     keep = ("steps", "warmup", "ms_per_step", "value", "unit", "dtype", "config", "gmm_us", "gmm_us_median",
             "gmm_us_min", "w13_us", "w2_us", "active_experts", "algorithmic_bytes", "roofline",
             "mfma_calibration", "hbm_calibration", "cpu_baseline", "gpu_over_cpu")
-    return {key: line[key] for key in keep if key in line}
+    out = {key: line[key] for key in keep if key in line}
+    out.update({key: v for key, v in line.items() if key.startswith("mxfp4_")})
+    return out
 
 
 def run_workload(gpu, name, steps, warmup, cpu_s, args):
@@ -659,6 +672,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-seconds", type=float, default=0.0,
+                    help="keep warming up the named workload until this much time has passed")
     ap.add_argument("--workload", default="w13_decode", choices=WORKLOADS)
     ap.add_argument("--tokens", type=int, default=None,
                     help="token count in place of the workload's (grouped-matmul workloads only)")
@@ -692,6 +707,7 @@ def main():
         return
 
     cpu_s = 0.0 if args.no_cpu_baseline else 15.0
+    gpu.min_warmup_s = args.warmup_seconds
     line = run_workload(gpu, args.workload, args.steps, args.warmup, cpu_s, args)
     extras = args.workload == "w13_decode" and not args.only and args.tokens is None
     calib = hbm_calibration(gpu) if (line["roofline"]["bound"] == "hbm" or extras) else None
@@ -702,6 +718,9 @@ def main():
         sub_args.kernel, sub_args.out_dtype, sub_args.tokens = "auto", None, None
         sub_cpu = 0.0 if args.no_cpu_baseline else 3.0
         work = {}
+        # each workload warms up for at least a quarter second: the matrix-bound
+        # ones reach their steady clock after a few dozen calls
+        gpu.min_warmup_s = 0.25
         for name in EXTRA_WORKLOADS:
             sub = run_workload(gpu, name, min(args.steps, 20), min(args.warmup, 5), sub_cpu, sub_args)
             work[name] = summary(with_hbm_fraction(sub, calib))

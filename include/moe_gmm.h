@@ -220,7 +220,7 @@ int moe_bf16_encode(const uint16_t* weights, int32_t E, int32_t N, int32_t K, vo
  * Preconditions not checked: row_index values lie in [0, x_rows); group_offsets
  * is non-decreasing with group_offsets[0] = 0 and group_offsets[E] <= M.
  * Exact-decode domain: MXFP4 scale bytes 2..252 (block exponent -125..125).
- * Limits as mxfp4_encode; M <= 2^24; x_rows * K * 2 < 2^31 bytes.
+ * Limits as mxfp4_encode; E <= 1024; M <= 2^24; x_rows * K * 2 < 2^31 bytes.
  */
 int moe_gmm(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
             const uint16_t* x, int32_t x_rows, const int32_t* row_index,

@@ -31,6 +31,10 @@ int check_weight_shape(int fmt, int32_t E, int32_t N, int32_t K) {
   return MOE_OK;
 }
 
+// The matmul kernels find their tiles from the band offsets with 64 lanes
+// of at most 16 experts each.
+constexpr int32_t kMaxGmmExperts = 1024;
+
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Route-sort sizes: ids fit the 10 id bits the placement ballots, and every
@@ -130,6 +134,7 @@ int moe_gmm_act(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, co
                 int y_dtype, int act, int kernel, void* stream) {
   const int st = check_weight_shape(fmt, E, N, K);
   if (st != MOE_OK) return st;
+  if (E > kMaxGmmExperts) return MOE_ERR_SHAPE;
   if (!dtype_ok(y_dtype)) return MOE_ERR_FORMAT;
   if (kernel < MOE_GMM_AUTO || kernel > MOE_GMM_TILED) return MOE_ERR_FORMAT;
   if (act != MOE_ACT_NONE && act != MOE_ACT_SILU_MUL) return MOE_ERR_FORMAT;
@@ -181,6 +186,7 @@ int moe_gmm_w4a4(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, c
   if (fmt == MOE_W_BF16) return MOE_ERR_UNSUPPORTED;
   const int st = check_weight_shape(fmt, E, N, K);
   if (st != MOE_OK) return st;
+  if (E > kMaxGmmExperts) return MOE_ERR_SHAPE;
   if (!dtype_ok(y_dtype)) return MOE_ERR_FORMAT;
   if (act != MOE_ACT_NONE && act != MOE_ACT_SILU_MUL) return MOE_ERR_FORMAT;
   if (!packed || !xq_codes || !xq_scales || !group_offsets || !y) return MOE_ERR_NULL;

@@ -118,6 +118,7 @@ def test_gmm_validation(lib):
     assert f(*args(K=200)) == ERR_SHAPE
     assert f(*args(N=500)) == ERR_SHAPE
     assert f(*args(E=0)) == ERR_SHAPE
+    assert f(*args(E=1025)) == ERR_SHAPE            # the tile scan covers 1024 experts
     assert f(*args(M=0)) == ERR_SHAPE
     assert f(*args(M=(1 << 24) + 1)) == ERR_SHAPE
     assert f(*args(fmt=3)) == ERR_FORMAT
@@ -156,7 +157,8 @@ def test_w4a4_validation(lib):
     assert q(FAKE_ALIGNED, 0, 64, FAKE_ALIGNED, FAKE, None) == ERR_SHAPE
     assert q(ctypes.c_void_p((1 << 30) + 2), 4, 64, FAKE_ALIGNED, FAKE, None) == ERR_SHAPE
     g = lib.moe_gmm_w4a4
-    args = lambda **kw: [kw.get("packed", FAKE_ALIGNED), kw.get("fmt", 0), 8, kw.get("N", 512), kw.get("K", 256),
+    args = lambda **kw: [kw.get("packed", FAKE_ALIGNED), kw.get("fmt", 0), kw.get("E", 8), kw.get("N", 512),
+                         kw.get("K", 256),
                          kw.get("qc", FAKE_ALIGNED), FAKE, kw.get("rows", 128), None, FAKE, 128,
                          FAKE, kw.get("dt", 0), kw.get("act", 0), None, None]
     assert g(*args(packed=None)) == ERR_NULL
@@ -170,6 +172,7 @@ def test_w4a4_validation(lib):
     assert g(*args(fmt=2)) == 4                     # bf16 weights: unsupported
     assert g(*args(fmt=5)) == ERR_FORMAT
     assert g(*args(fmt=1, K=200)) == ERR_SHAPE
+    assert g(*args(E=1025)) == ERR_SHAPE
 
 
 def test_gmm_act_validation(lib):
