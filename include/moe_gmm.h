@@ -136,7 +136,9 @@ int moe_route_sort_noalloc(const int32_t* topk_ids, int32_t T, int32_t k, int32_
  * moe_packed_weight_bytes - size in bytes of the packed buffer that
  * mxfp4_encode writes for E experts of an [N, K] weight (0 on bad sizes).
  * Codes stay 4 bits per weight; scales stay one byte per block (padded to
- * whole 256-byte groups), plus 4*E bytes of tensor scales for NVFP4.
+ * whole 256-byte groups), plus, for NVFP4, 4*E bytes of tensor scales and a
+ * 4-byte flag per 16 columns of each expert (whether all of their E4M3
+ * scales are powers of two), each part padded to 256 bytes.
  */
 size_t moe_packed_weight_bytes(int fmt, int32_t E, int32_t N, int32_t K);
 

@@ -31,13 +31,15 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // for chunks 4q .. 4q+3 (byte i = chunk 4q+i).  NVFP4: 256-byte records per
 // pair of chunks; lane l's dword holds, for chunk 2q+c, the E4M3 bytes of the
 // low and high 16-halves of its block at bytes 2c and 2c+1.  Missing chunks
-// of the last record are zero.  NVFP4 appends E floats of tensor scales.
+// of the last record are zero.  NVFP4 appends E floats of tensor scales,
+// then one word per (e, nt): nonzero when some E4M3 scale of that subtile is
+// not a positive power of two (the tiled kernel's choice of decode).
 // ---------------------------------------------------------------------------
 struct Layout {
   int64_t E, N, K;
   int64_t NT, KC, KB;     // 16-column tiles, 128-deep chunks, 32-blocks
   int64_t groups;         // scale records per (e, nt)
-  int64_t codes_bytes, scales_off, scales_bytes, tscale_off, total_bytes;
+  int64_t codes_bytes, scales_off, scales_bytes, tscale_off, flags_off, total_bytes;
 };
 
 __host__ __device__ inline Layout make_layout(int fmt, int64_t E, int64_t N, int64_t K) {
@@ -48,7 +50,7 @@ __host__ __device__ inline Layout make_layout(int fmt, int64_t E, int64_t N, int
     // bf16 weights (the comparison arm): 4 KiB chunks, no scales
     L.groups = 0;
     L.codes_bytes = E * N * K * 2;
-    L.scales_off = L.tscale_off = L.total_bytes = L.codes_bytes;
+    L.scales_off = L.tscale_off = L.flags_off = L.total_bytes = L.codes_bytes;
     L.scales_bytes = 0;
     return L;
   }
@@ -58,7 +60,8 @@ __host__ __device__ inline Layout make_layout(int fmt, int64_t E, int64_t N, int
   L.scales_off = L.codes_bytes;
   L.scales_bytes = E * L.NT * L.groups * 256;
   L.tscale_off = L.scales_off + L.scales_bytes;
-  L.total_bytes = L.tscale_off + (fmt == 0 ? 0 : ((E * 4 + 255) / 256) * 256);
+  L.flags_off = L.tscale_off + (fmt == 0 ? 0 : ((E * 4 + 255) / 256) * 256);
+  L.total_bytes = L.flags_off + (fmt == 0 ? 0 : ((E * L.NT * 4 + 255) / 256) * 256);
   return L;
 }
 
@@ -124,6 +127,19 @@ __device__ __forceinline__ u32x4_t decode8_any_scale(uint32_t codes8, float s) {
 __device__ __forceinline__ bool is_pow2_scale(float s) {
   const uint32_t u = __float_as_uint(s);
   return (u & 0x807FFFFFu) == 0 && (u & 0x7F800000u) != 0 && (u & 0x7F800000u) != 0x7F800000u;
+}
+
+// Flags (bit 7 of each byte) the E4M3 bytes of w that are not a positive
+// power of two: a sign, a zero, a normal with a nonzero mantissa (NaN
+// included), or a subnormal whose mantissa has more than one bit.  Byte-wise
+// arithmetic: every partial value stays below 0x80 per byte, so no carry or
+// borrow crosses a byte.
+__host__ __device__ inline uint32_t e4m3x4_not_pow2(uint32_t w) {
+  constexpr uint32_t H = 0x80808080u, L7 = 0x7F7F7F7Fu;
+  const uint32_t m = w & 0x07070707u, e = w & 0x78787878u;
+  const uint32_t mnz = (m + L7) & H, enz = (e + L7) & H;
+  const uint32_t mbad = ((((m | H) - 0x01010101u) & m) + L7) & H;   // m & (m - 1) != 0
+  return (w & H) | (mnz & enz) | (~enz & H & (~mnz | mbad));
 }
 
 // E8M0 byte b (1..254) -> 2^(b - 127) as f32, by placing b in the exponent.

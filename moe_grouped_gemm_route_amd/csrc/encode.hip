@@ -82,6 +82,24 @@ __global__ __launch_bounds__(256) void encode_scales_kernel(int fmt, const uint8
   if (err_count && bad) atomicAdd(err_count, bad);
 }
 
+// NVFP4: the per-subtile flag word of the layout, from the packed scale
+// words just written: one wave per (e, nt), nonzero when some E4M3 scale of
+// the subtile is not a positive power of two.  Bytes past the last chunk
+// (the zero padding of the last record) are not tested.
+__global__ __launch_bounds__(256) void encode_flags_kernel(Layout L, uint8_t* __restrict__ packed) {
+  const int lane = threadIdx.x & 63;
+  for (int64_t sub = blockIdx.x * 4 + (threadIdx.x >> 6); sub < L.E * L.NT; sub += (int64_t)gridDim.x * 4) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(packed + L.scales_off) + sub * L.groups * 64;
+    uint32_t bad = 0;
+    for (int64_t q = 0; q < L.groups; ++q) {
+      const uint32_t valid = 2 * q + 1 < L.KC ? 0xFFFFFFFFu : 0x0000FFFFu;   // chunk 2q + 1 exists?
+      bad |= e4m3x4_not_pow2(w[q * 64 + lane]) & valid;
+    }
+    const bool any = __ballot(bad != 0) != 0;
+    if (lane == 0) reinterpret_cast<uint32_t*>(packed + L.flags_off)[sub] = any ? 1u : 0u;
+  }
+}
+
 // Clears a small int32 counter with a kernel (kept out of memset nodes so the
 // call stays safe to record into a HIP graph).
 __global__ void zero_i32_kernel(int32_t* p, int n) {
@@ -105,6 +123,11 @@ hipError_t launch_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
   const int grid_s = (int)((words + 255) / 256 < 65536 ? (words + 255) / 256 : 65536);
   hipLaunchKernelGGL(encode_scales_kernel, dim3(grid_s), dim3(256), 0, stream, fmt, scales,
                      tensor_scale, L, packed, err_count);
+  if (fmt == 1) {
+    const int64_t subs = L.E * L.NT;
+    const int grid_f = (int)((subs + 3) / 4 < 65536 ? (subs + 3) / 4 : 65536);
+    hipLaunchKernelGGL(encode_flags_kernel, dim3(grid_f), dim3(256), 0, stream, L, packed);
+  }
   return hipGetLastError();
 }
 

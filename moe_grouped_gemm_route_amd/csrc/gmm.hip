@@ -691,43 +691,17 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
   __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>());
 }
 
-// Flags (bit 7 of each byte) the E4M3 bytes of w that are not a positive
-// power of two: a sign, a zero, a normal with a nonzero mantissa (NaN
-// included), or a subnormal whose mantissa has more than one bit.  Byte-wise
-// arithmetic: every partial value stays below 0x80 per byte, so no carry or
-// borrow crosses a byte.
-__device__ __forceinline__ uint32_t e4m3x4_not_pow2(uint32_t w) {
-  constexpr uint32_t H = 0x80808080u, L7 = 0x7F7F7F7Fu;
-  const uint32_t m = w & 0x07070707u, e = w & 0x78787878u;
-  const uint32_t mnz = (m + L7) & H, enz = (e + L7) & H;
-  const uint32_t mbad = ((((m | H) - 0x01010101u) & m) + L7) & H;   // m & (m - 1) != 0
-  return (w & H) | (mnz & enz) | (~enz & H & (~mnz | mbad));
-}
-
 // True when every block scale (E4M3) in the wave's columns is a positive
-// power of two, the case the one-instruction decode handles exactly.
-// The words go in batches of SB records per subtile, all issued before any
-// is tested, so a batch costs one round trip.
-template <int NS, int ACT>
-__device__ __forceinline__ bool span_scales_pow2(__amdgpu_buffer_rsrc_t sr, int groups, int h16) {
-  constexpr int SB = 8;
-  const uint32_t voff = (threadIdx.x & 63) * 4;
-  uint32_t bad = 0;
-  for (int rec0 = 0; rec0 < groups; rec0 += SB) {
-    uint32_t w[NS][SB];
+// power of two, the case the one-instruction decode handles exactly: the
+// encoder's per-subtile flags (uniform loads) say so.
+template <int ACT>
+__device__ __forceinline__ bool span_scales_pow2(const uint8_t* __restrict__ packed, const Layout& L, int64_t et,
+                                                 int h16) {
+  const uint32_t* flags = reinterpret_cast<const uint32_t*>(packed + L.flags_off) + et;
+  uint32_t any = 0;
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns) {
-      const int sub = col_sub<ACT>(ns, h16);
-#pragma unroll
-      for (int i = 0; i < SB; ++i)   // records past the subtile's read its neighbour's (or zeros): not tested
-        w[ns][i] = __builtin_amdgcn_raw_buffer_load_b32(sr, voff, (sub * groups + rec0 + i) * 256, 0);
-    }
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-      for (int i = 0; i < SB; ++i) bad |= rec0 + i < groups ? e4m3x4_not_pow2(w[ns][i]) : 0u;
-  }
-  return __ballot(bad != 0) == 0;
+  for (int ns = 0; ns < TL_NS; ++ns) any |= flags[col_sub<ACT>(ns, h16)];
+  return any == 0;
 }
 
 template <int FMT, bool OBF16, int ACT>
@@ -804,7 +778,7 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
       case 7: tiled_k_walk_bf16<7, ACT>(s_a, xr, avo, cr, KC, h16, wave, va, acc); break;
       default: tiled_k_walk_bf16<8, ACT>(s_a, xr, avo, cr, KC, h16, wave, va, acc); break;
     }
-  } else if (FMT == 1 && wave_active && !span_scales_pow2<TL_NS, ACT>(sr, groups, h16)) {
+  } else if (FMT == 1 && wave_active && !span_scales_pow2<ACT>(packed, L, et, h16)) {
     // general E4M3 scales: one walk over all eight subtiles (the rows past
     // the band are zeros in LDS and are never stored)
     tiled_k_walk<8, FMT, ACT, true>(s_a, xr, avo, cr, sr, KC, groups, h16, wave, va, acc);

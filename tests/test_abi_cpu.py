@@ -52,7 +52,9 @@ def test_packed_bytes(lib):
         assert mx == E * N * K // 2 + E * (N // 16) * groups * 256
         nv = lib.moe_packed_weight_bytes(1, E, N, K)
         groups = -(-(K // 128) // 2)
-        assert nv == E * N * K // 2 + E * (N // 16) * groups * 256 + ((4 * E + 255) // 256) * 256
+        # + the tensor scales and one flag word per 16-column subtile, each padded to 256 bytes
+        assert nv == (E * N * K // 2 + E * (N // 16) * groups * 256 + ((4 * E + 255) // 256) * 256
+                      + ((4 * E * (N // 16) + 255) // 256) * 256)
     assert lib.moe_packed_weight_bytes(0, 8, 512, 100) == 0
     assert lib.moe_packed_weight_bytes(0, 8, 48, 256) == 0
     assert lib.moe_packed_weight_bytes(7, 8, 512, 256) == 0
