@@ -30,7 +30,11 @@ Other workloads, run alone with --workload:
     w4a4_nvfp4_w13: config 5's 256 tokens, W4A4 with its NVFP4 weights;
   bf16_w13_decode, bf16_w2_decode, bf16_w13_prefill: the bf16-weight
     comparison arm on the decoded weights of configs 2, 3 and 4 (the same
-    values, four times the bytes) next to the MXFP4 kernel on the same inputs.
+    values, four times the bytes) next to the MXFP4 kernel on the same inputs;
+  nvfp4_w13_prefill: the 4,096-token w13 with NVFP4 weights from the lossless
+    cast, next to the MXFP4 kernel on the same inputs;
+  route_sort_decode / route_sort_prefill: the route sort alone on config 2's
+    384 or config 4's 24,576 token-expert pairs (Mpairs/s).
 --tokens T replaces a workload's token count (the weights stay the config's;
 x and the routing are redrawn the same way), for the kernel-choice sweep.
 
@@ -72,7 +76,8 @@ LAYER_WORKLOADS = ("layer_decode", "layer_prefill", "w4a4_layer_prefill")
 # W4A4 grouped matmul: config, weight format
 W4A4_WORKLOADS = {"w4a4_w13_prefill": (4, "mxfp4"), "w4a4_nvfp4_w13_prefill": (4, "nvfp4"),
                   "w4a4_nvfp4_w13": (5, "nvfp4")}
-WORKLOADS = sorted(list(GMM_WORKLOADS) + list(LAYER_WORKLOADS) + list(W4A4_WORKLOADS))
+ROUTE_WORKLOADS = {"route_sort_decode": 2, "route_sort_prefill": 4}   # the route sort alone, on a config's routing
+WORKLOADS = sorted(list(GMM_WORKLOADS) + list(LAYER_WORKLOADS) + list(W4A4_WORKLOADS) + list(ROUTE_WORKLOADS))
 # timed after the headline in the default run
 EXTRA_WORKLOADS = ("tiny", "w2_decode", "w13_prefill", "nvfp4_w13", "nvfp4_w13_prefill", "layer_decode",
                    "layer_prefill")
@@ -509,6 +514,36 @@ def run_layer(gpu, workload, steps, warmup, cpu_s):
     return out
 
 
+def run_route(gpu, workload, steps, warmup):
+    """The route sort alone, back to back on one routing (its workspace
+    allocated once): token-expert pairs sorted per second."""
+    moe = gpu.moe
+    from moe_grouped_gemm_route_amd.synth import make_config
+
+    p = make_config(ROUTE_WORKLOADS[workload])
+    E, T, k = p["E"], p["T"], p["k"]
+    ids = gpu.put(p["topk_ids"])
+    ws = gpu.route_workspace(T, k, E)
+
+    def step(timed):
+        e = (gpu.event(), gpu.event()) if timed else None
+        if timed:
+            e[0].record()
+        moe.route_sort(ids, E, ws=ws)
+        if timed:
+            e[1].record()
+        return e
+
+    wall, ev = gpu.timed_steps(step, steps, warmup)
+    sort_s = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    step_s = wall / steps
+    config = {"tokens": T, "top_k": k, "experts": E, "pairs": T * k,
+              "workspace_bytes": moe.route_sort_workspace_bytes(T, k, E), "step": "route_sort"}
+    out = base_line(workload, steps, gpu.warmup_done, step_s, T * k / step_s / 1e6, "Mpairs/s", "int32", config)
+    out["route_sort_us"] = round(sort_s * 1e6, 2)
+    return out
+
+
 def run_w4a4(gpu, workload, steps, warmup):
     """The W4A4 workloads: route-sort, MXFP4 activation quantization and the
     grouped matmul on the scaled FP4 MFMA, over config 4's problem (MXFP4
@@ -642,7 +677,7 @@ def hbm_calibration(gpu):
 def with_hbm_fraction(line, calib):
     """Adds the kernel's fraction of the calibrated read rate to an
     HBM-bound line."""
-    if line["roofline"]["bound"] == "hbm":
+    if line.get("roofline", {}).get("bound") == "hbm":
         line["hbm_calibration"] = dict(calib)
         line["hbm_calibration"]["kernel_frac_of_read"] = round(line["roofline"]["achieved"] / calib["read_gbs"], 4)
     return line
@@ -663,6 +698,8 @@ def run_workload(gpu, name, steps, warmup, cpu_s, args):
         return run_layer(gpu, name, steps, warmup, cpu_s)
     if name in W4A4_WORKLOADS:
         return run_w4a4(gpu, name, steps, warmup)
+    if name in ROUTE_WORKLOADS:
+        return run_route(gpu, name, steps, warmup)
     return run_gmm(gpu, name, steps, warmup, cpu_s, kernel=args.kernel, out_dtype=args.out_dtype,
                    tokens=args.tokens)
 
@@ -710,7 +747,7 @@ def main():
     gpu.min_warmup_s = args.warmup_seconds
     line = run_workload(gpu, args.workload, args.steps, args.warmup, cpu_s, args)
     extras = args.workload == "w13_decode" and not args.only and args.tokens is None
-    calib = hbm_calibration(gpu) if (line["roofline"]["bound"] == "hbm" or extras) else None
+    calib = hbm_calibration(gpu) if (line.get("roofline", {}).get("bound") == "hbm" or extras) else None
     if calib is not None:
         with_hbm_fraction(line, calib)
     if extras:
