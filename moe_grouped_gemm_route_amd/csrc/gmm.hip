@@ -831,22 +831,28 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
 // tile.
 //
 // Same workgroup shape as the tiled kernel: 4 waves, 128 rows x 256
-// columns, the activation chunk staged in LDS by direct-to-LDS loads.  With a
-// quarter of the matrix work per chunk the kernel is bound by its weight
-// stream, so three chunks are staged (LDS buffers for the activations and
-// each wave's weight scale words, a register ring for the weight codes) and
-// two of them are in flight while the third is computed.  A staged chunk holds the 128 rows'
-// codes (64 bytes per row, rows contiguous: 8 KiB) and their scale dwords
-// (wave w loads rows 32w .. 32w+31 into its own 256-byte slot; lanes 32..63
-// read past the buffer and write zeros into the slot's unused half).
+// columns, the activation chunk staged in LDS by direct-to-LDS loads.  Two
+// chunks are staged (LDS buffers for the activations and each wave's weight
+// scale words, a register pair for the weight codes): chunk kc + 1 loads
+// while chunk kc is computed.  A staged chunk holds the 128 rows' codes (64
+// bytes per row, rows contiguous: 8 KiB) and their scale dwords (wave w
+// loads rows 32w .. 32w+31 into its own 256-byte slot; lanes 32..63 read
+// past the buffer and write zeros into the slot's unused half).
+//
+// Each chunk ends by waiting for all of the wave's loads (vmcnt 0), not for
+// a count that leaves later loads in flight.  A counted wait let a third
+// staged chunk's loads stay in flight, and on MI355X some 4-byte
+// direct-to-LDS loads (the weight scale words) had then not landed when
+// their stage was read: one 16-column subtile of a few thin tiles came out
+// wrong, differently from run to run.  With the full wait a third stage
+// buys nothing, and two stages measured the same.
 // ---------------------------------------------------------------------------
 constexpr int Q_CODE_BYTES = TL_BM * 64;                     // 8 KiB
 constexpr int Q_SCALE_BYTES = TL_WAVES * 256;
 constexpr int Q_WSCALE_BYTES = TL_WAVES * TL_NS * 256;       // each wave's weight scale words
 constexpr int Q_STAGE_BYTES = Q_CODE_BYTES + Q_SCALE_BYTES + Q_WSCALE_BYTES;
 constexpr int Q_LOADS = Q_CODE_BYTES / 1024 / TL_WAVES;      // 1 KiB code loads per wave per chunk
-constexpr int Q_STAGES = 3;                                   // chunks staged: two in flight, one computed
-constexpr int Q_ISSUE = Q_LOADS + 1 + 2 * TL_NS;             // vector-memory instructions per chunk
+constexpr int Q_STAGES = 2;                                   // chunks staged: one loading, one computed
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
@@ -875,27 +881,24 @@ __device__ __forceinline__ uint32_t w4a4_block_scale(uint32_t word, int kc, int&
   return off ? 127u : bits >> 23;
 }
 
-// NST staged chunks, NST - 1 in flight: three for MXFP4 weights; two for
-// NVFP4, whose per-block scale conversion needs the registers of the third.
-template <int NSUB, int FMT, int ACT, int NST>
+// The K walk of one wave over a tile with NSUB valid 16-row subtiles.
+template <int NSUB, int FMT, int ACT>
 __device__ __forceinline__ void w4a4_k_walk(uint8_t* s_q, __amdgpu_buffer_rsrc_t qcr, __amdgpu_buffer_rsrc_t qsr,
                                             const uint32_t (&cvo)[Q_LOADS], uint32_t svo,
                                             __amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t sr, int KC,
                                             int groups, int h16, int wave, f32x4_t (&acc)[TL_MS][TL_NS],
                                             int& bad) {
-  static_assert(NST == 2 || NST == 3, "two or three stages");
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
   const uint32_t c_voff = lane * 16, s_voff = lane * 4;
-  u32x4_t cs[NST][TL_NS];
+  u32x4_t cs[Q_STAGES][TL_NS];
   // this wave's weight scale words in a stage: 256 bytes per subtile, the
   // word of lane l at byte 4 l
   const int wsc = Q_CODE_BYTES + Q_SCALE_BYTES + wave * TL_NS * 256;
   // all loads of chunk kc into stage `slot`: the activation codes and scales
   // (direct to LDS, shared by the four waves), then this wave's weight codes
-  // (registers) and weight scale words (direct to LDS, its own slot);
-  // Q_ISSUE vector-memory instructions
+  // (registers) and weight scale words (direct to LDS, its own slot)
   auto issue = [&](auto sc, int kc) {
     constexpr int slot = decltype(sc)::value;
     uint8_t* buf = s_q + slot * Q_STAGE_BYTES;
@@ -914,14 +917,13 @@ __device__ __forceinline__ void w4a4_k_walk(uint8_t* s_q, __amdgpu_buffer_rsrc_t
                                                (sub * groups + rec) * 256, 0, 0);
     }
   };
-  // Chunk kc (stage kc % NST) issues chunk kc + NST - 1 into the stage that
-  // chunk kc - 1 used, computes, then waits until only the loads of the
-  // chunks after kc + 1 are outstanding: chunk kc + 1 has then landed for
-  // every wave when the barrier opens.  Chunks past the last re-load it into
-  // a stage nobody reads any more.
+  // Chunk kc (stage kc & 1) issues chunk kc + 1 into the other stage (freed
+  // by the barrier that ended chunk kc - 1; past the last chunk it re-loads
+  // the last one), computes, then waits for every load of the wave: chunk
+  // kc + 1 has then landed for every wave when the barrier opens.
   auto chunk = [&](auto sc, int kc) {
     constexpr int d = decltype(sc)::value;
-    issue(std::integral_constant<int, (d + NST - 1) % NST>{}, min(kc + NST - 1, KC - 1));
+    issue(std::integral_constant<int, d ^ 1>{}, min(kc + 1, KC - 1));
     const uint8_t* buf = s_q + d * Q_STAGE_BYTES;
     uint32_t sb[TL_NS];
 #pragma unroll
@@ -936,31 +938,18 @@ __device__ __forceinline__ void w4a4_k_walk(uint8_t* s_q, __amdgpu_buffer_rsrc_t
 #pragma unroll
       for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = mfma_fp4(a, sa, cs[d][ns], sb[ns], acc[ms][ns]);
     }
-    vm_wait_barrier<Q_ISSUE * (NST - 2)>();
+    vm_wait_barrier<0>();
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
   issue(S0{}, 0);
-  if constexpr (NST == 3) issue(S1{}, min(1, KC - 1));
-  vm_wait_barrier<Q_ISSUE * (NST - 2)>();
+  vm_wait_barrier<0>();
   int k0 = 0;
-  if constexpr (NST == 3) {
-    for (; k0 + 3 <= KC; k0 += 3) {
-      chunk(S0{}, k0);
-      chunk(S1{}, k0 + 1);
-      chunk(S2{}, k0 + 2);
-    }
-    if (k0 < KC) chunk(S0{}, k0);
-    if (k0 + 1 < KC) chunk(S1{}, k0 + 1);
-  } else {
-    for (; k0 + 2 <= KC; k0 += 2) {
-      chunk(S0{}, k0);
-      chunk(S1{}, k0 + 1);
-    }
-    if (k0 < KC) chunk(S0{}, k0);
+  for (; k0 + 2 <= KC; k0 += 2) {
+    chunk(S0{}, k0);
+    chunk(S1{}, k0 + 1);
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>());
+  if (k0 < KC) chunk(S0{}, k0);
 }
 
 template <int FMT, bool OBF16, int ACT>
@@ -1033,16 +1022,15 @@ __global__ __launch_bounds__(256, 2) void gmm_w4a4_kernel(const uint8_t* __restr
     for (int ns = 0; ns < TL_NS; ++ns) acc[ms][ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   int bad = 0;
-  constexpr int NST = FMT == 0 ? 3 : 2;
   switch (nsub) {
-    case 1: w4a4_k_walk<1, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
-    case 2: w4a4_k_walk<2, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
-    case 3: w4a4_k_walk<3, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
-    case 4: w4a4_k_walk<4, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
-    case 5: w4a4_k_walk<5, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
-    case 6: w4a4_k_walk<6, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
-    case 7: w4a4_k_walk<7, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
-    default: w4a4_k_walk<8, FMT, ACT, NST>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    case 1: w4a4_k_walk<1, FMT, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    case 2: w4a4_k_walk<2, FMT, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    case 3: w4a4_k_walk<3, FMT, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    case 4: w4a4_k_walk<4, FMT, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    case 5: w4a4_k_walk<5, FMT, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    case 6: w4a4_k_walk<6, FMT, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    case 7: w4a4_k_walk<7, FMT, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
+    default: w4a4_k_walk<8, FMT, ACT>(s_q, qcr, qsr, cvo, svo, cr, sr, KC, groups, h16, wave, acc, bad); break;
   }
 
   if (!wave_active) return;

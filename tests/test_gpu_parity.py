@@ -493,6 +493,40 @@ def test_gmm_w4a4_full_oracle(case):
         assert rel_err(ya.cpu().numpy(), oracle.silu_mul(ref)) <= REL_TOL
 
 
+@pytest.mark.parametrize("E", [1000, 1024])
+def test_gmm_most_experts(E):
+    # the largest expert counts the tile scans cover (64 lanes of up to 16
+    # experts; 1000 leaves the last lane partial), every expert's band
+    # checked whole, through both W4A16 kernels and the W4A4 kernel
+    p = make_problem(T=700, k=4, E=E, K=256, N=128, seed=330 + E, routing="zipf", empty_experts=(0, E - 1))
+    w, packed = weights_for(p, "mxfp4")
+    ref_r = oracle.route_sort(p["topk_ids"], E)
+    ref = oracle.gmm(p["x"], ref_r["sorted_token"], ref_r["group_offsets"], w)
+    ys = []
+    for kernel in KERNELS:
+        _, y = run_gpu(p, packed, "mxfp4", kernel=kernel)
+        assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
+        ys.append(y)
+    assert torch.equal(ys[0], ys[1])
+    yq = _run_w4a4(p, packed)
+    assert rel_err(yq.cpu().numpy(), _w4a4_ref(p, w)) <= REL_TOL
+
+
+def test_gmm_w4a4_thin_tiles_every_call():
+    # many tiles of 1..16 rows make chunks short, so each chunk's wait meets
+    # its loads still in flight; every call must give the oracle's output
+    # and the same bits (a wait that trusted the order in which the 4-byte
+    # direct-to-LDS scale loads land once gave one wrong 16-column subtile
+    # in some tiles, differently from call to call)
+    p = make_problem(T=700, k=4, E=1024, K=256, N=128, seed=1354, routing="zipf", empty_experts=(0, 1023))
+    w, packed = weights_for(p, "mxfp4")
+    ref = _w4a4_ref(p, w)
+    ys = [_run_w4a4(p, packed) for _ in range(6)]
+    for y in ys:
+        assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
+        assert torch.equal(y, ys[0])
+
+
 @pytest.mark.parametrize("case", ["banded", "gathered", "band_input"])
 def test_gmm_w4a4_nvfp4_weights(case):
     # NVFP4 weights from the lossless cast (both E4M3 halves of a block one
