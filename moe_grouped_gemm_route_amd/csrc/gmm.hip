@@ -428,19 +428,17 @@ __global__ __launch_bounds__(256, NS > 4 ? 2 : 3) void gmm_stream_kernel(const u
 // registers one chunk ahead.  The K walk is compiled per number of valid
 // 16-row subtiles, so subtiles past the band end cost nothing.
 //
-// Waits are explicit.  Per chunk kc a wave issues, in this order, its share
-// of activation chunk kc+1 (LOADS direct-to-LDS loads) and the codes and
-// scale words of chunk kc+1 (2 * NS loads), computes chunk kc, then waits
-// until at most 2 * NS vector loads are outstanding: loads complete in
-// issue order, so its share of chunk kc+1 is then in LDS, while the codes
-// may still be in flight.  The barrier that follows makes every wave's share
-// visible and guarantees that every wave has finished reading buffer kc & 1
-// before it is refilled with chunk kc+2.  Every chunk issues the same loads,
-// so the count is the same at every wait: the last chunk still stages into
-// buffer (kc+1) & 1, which the previous barrier freed, but from an offset
-// past the activation buffer, so those loads write zeros without fetching
-// anything; its code loads repeat the last chunk's into the unused register
-// slot.  A final vmcnt(0) drains them before the epilogue.
+// Waits are explicit.  Per chunk kc a wave issues its share of activation
+// chunk kc+1 (LOADS direct-to-LDS loads) and the codes and scale words of
+// chunk kc+1 (2 * NS loads), computes chunk kc, then waits for all of its
+// loads (vmcnt 0; a count that left the code loads in flight relied on the
+// order in which direct-to-LDS and register loads land, and measured no
+// faster).  The barrier that follows makes every wave's share visible and
+// guarantees that every wave has finished reading buffer kc & 1 before it
+// is refilled with chunk kc+2.  The last chunk still stages into buffer
+// (kc+1) & 1, which the previous barrier freed, but from an offset past the
+// activation buffer, so those loads write zeros without fetching anything;
+// its code loads repeat the last chunk's into the unused register slot.
 //
 // A-fragment reads are ds_read_b128 issued P - 1 fragments ahead of their
 // MFMAs (inline asm, so the compiler cannot sink them next to their use);
@@ -578,9 +576,12 @@ __device__ __forceinline__ void tiled_chunk_bf16(std::index_sequence<Fs...>, u32
 // The K walk with bf16 weights.  Per chunk a wave issues its share of the
 // next activation chunk (LOADS direct-to-LDS loads), then, step by step, the
 // next chunk's weights (4 * NS loads); the wait before the barrier leaves
-// only those weight loads outstanding.  On the last chunk the staging loads
-// read past the buffer (zeros, no fetch) and the weight loads repeat the last
-// chunk's into the unused registers, so the counts stay the same.
+// only those weight loads outstanding (they are issued late in the chunk,
+// and a full wait would take them off the pipeline), trusting that the
+// 16-byte direct-to-LDS loads issued before them have landed once that many
+// loads remain.  On the last chunk the staging loads read past the buffer
+// (zeros, no fetch) and the weight loads repeat the last chunk's into the
+// unused registers, so the counts stay the same.
 template <int NSUB, int ACT>
 __device__ __forceinline__ void tiled_k_walk_bf16(uint8_t* s_a, __amdgpu_buffer_rsrc_t xr,
                                                   const uint32_t (&avo)[TL_LOADS], __amdgpu_buffer_rsrc_t cr,
@@ -674,7 +675,7 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
     u32x4_t b[TL_NS];
     tiled_prologue<NSUB, P, d>(std::make_index_sequence<PRO>{}, ar, va);
     tiled_chunk<NSUB, P, d, GEN>(std::make_index_sequence<FT>{}, ar, va, b, cs[d], lo, hi, acc);
-    vm_wait_barrier<2 * TL_NS>();
+    vm_wait_barrier<0>();
   };
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
