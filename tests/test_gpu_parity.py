@@ -683,6 +683,48 @@ def test_gmm_deterministic():
         assert torch.equal(a, b)
 
 
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 3, 17, 64, 300, 1024]))
+        k = min(int(rng.integers(1, 9)), E)          # top-k picks distinct experts
+        T = int(rng.integers(1, max(2, 3000 // k)))
+        out.append(dict(T=T, k=k, E=E, K=int(rng.choice([128, 256, 384, 640])),
+                        N=int(rng.choice([64, 128, 192, 320, 512])),
+                        routing=str(rng.choice(["uniform", "zipf"])),
+                        band=bool(rng.integers(0, 2)), seed=700 + i))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(12, 77), ids=lambda c: "E%d_T%d_k%d_K%d_N%d_%s%s" % (
+    c["E"], c["T"], c["k"], c["K"], c["N"], c["routing"], "_band" if c["band"] else ""))
+def test_gmm_random_shapes_all_kernels(shape):
+    # seeded shapes across the expert counts, band sizes, K (odd and even
+    # chunk counts) and N the kernels handle: both W4A16 kernels and the W4A4
+    # kernel against the oracle, each twice (same bits), the two W4A16
+    # kernels bit for bit
+    c = shape
+    p = make_problem(T=c["T"], k=c["k"], E=c["E"], K=c["K"], N=c["N"], seed=c["seed"], routing=c["routing"],
+                     x_rows=c["T"] * c["k"] if c["band"] else None, exp_range=(-6, -2))
+    w, packed = weights_for(p, "mxfp4")
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    ref = oracle.gmm(p["x"], ref_r["sorted_token"] if p["gather"] else None, ref_r["group_offsets"], w)
+    r = moe.route_sort(to_dev(p["topk_ids"]), p["E"])
+    ys = []
+    for kernel in KERNELS:
+        _, a = run_gpu(p, packed, "mxfp4", kernel=kernel, routed=r)
+        _, b = run_gpu(p, packed, "mxfp4", kernel=kernel, routed=r)
+        assert rel_err(a.cpu().numpy(), ref) <= REL_TOL
+        assert torch.equal(a, b)
+        ys.append(a)
+    assert torch.equal(ys[0], ys[1])
+    ref4 = _w4a4_ref(p, w)
+    q = [_run_w4a4(p, packed) for _ in range(2)]
+    assert rel_err(q[0].cpu().numpy(), ref4) <= REL_TOL
+    assert torch.equal(q[0], q[1])
+
+
 # ------------------------------------------------- full-size workloads ---
 
 def _sample(M_valid, N, n, seed):
