@@ -725,6 +725,43 @@ def test_gmm_random_shapes_all_kernels(shape):
     assert torch.equal(q[0], q[1])
 
 
+@pytest.mark.parametrize("shape", _random_shapes(8, 78), ids=lambda c: "E%d_T%d_k%d_K%d_N%d_%s%s" % (
+    c["E"], c["T"], c["k"], c["K"], c["N"], c["routing"], "_band" if c["band"] else ""))
+def test_gmm_random_shapes_nvfp4_and_activation(shape):
+    # the same kind of shapes with NVFP4 weights whose E4M3 block scales are
+    # arbitrary (a quarter of the subtiles) or powers of two, through both
+    # W4A16 kernels; the fused gate/up activation where N allows it
+    c = shape
+    p = make_problem(T=c["T"], k=c["k"], E=c["E"], K=c["K"], N=c["N"], seed=c["seed"], routing=c["routing"],
+                     x_rows=c["T"] * c["k"] if c["band"] else None, exp_range=(-6, -2))
+    rng = np.random.default_rng(c["seed"] + 1)
+    E, N, K = c["E"], c["N"], c["K"]
+    bs = (rng.integers(2, 15, size=(E, N, K // 16)) << 3).astype(np.uint8)        # powers of two
+    general = rng.random((E, N // 16)) < 0.25
+    gen_bytes = rng.integers(0x28, 0x48, size=(E, N, K // 16)).astype(np.uint8)
+    bs = np.where(np.repeat(general, 16, axis=1)[:, :, None], gen_bytes, bs)
+    p["block_scales"] = bs
+    p["tensor_scale"] = np.ldexp(1.0, rng.integers(-3, 3, size=E)).astype(np.float32)
+    w, packed = weights_for(p, "nvfp4")
+    ref_r = oracle.route_sort(p["topk_ids"], E)
+    ref = oracle.gmm(p["x"], ref_r["sorted_token"] if p["gather"] else None, ref_r["group_offsets"], w)
+    r = moe.route_sort(to_dev(p["topk_ids"]), E)
+    ys = []
+    for kernel in KERNELS:
+        _, y = run_gpu(p, packed, "nvfp4", kernel=kernel, routed=r)
+        assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
+        ys.append(y)
+    assert torch.equal(ys[0], ys[1])
+    if N % 128 == 0:
+        refa = oracle.silu_mul(ref)
+        acts = []
+        for kernel in KERNELS:
+            _, ya = run_gpu(p, packed, "nvfp4", kernel=kernel, routed=r, act=moe.ACT_SILU_MUL)
+            assert rel_err(ya.cpu().numpy(), refa) <= REL_TOL
+            acts.append(ya)
+        assert torch.equal(acts[0], acts[1])
+
+
 # ------------------------------------------------- full-size workloads ---
 
 def _sample(M_valid, N, n, seed):
