@@ -45,7 +45,9 @@ MFMA-bound prefill.  roofline.achieved is the same quantity over the
 grouped-matmul kernel's own average duration, timed with HIP events on the
 stream it runs on (gmm_us; median and minimum beside it).  hbm_calibration
 and mfma_calibration report the read rate and the matrix-unit rate this part
-sustains on plain loops, with the kernel's fraction of them.  The CPU
+sustains on plain loops, with the kernel's fraction of them
+(--mixed-calibration prints, alone, what plain PyTorch copy and row-sum
+kernels reach when reads and writes mix, the regime of the combine).  The CPU
 baseline times the float64 oracle on a bounded sample of the same workload on
 the host cores; gpu_over_cpu is value over its value.
 """
@@ -674,6 +676,41 @@ def hbm_calibration(gpu):
                     % (HBM_CALIB_BYTES >> 20, HBM_CALIB_BLOCKS, float(np.median(ms)))}
 
 
+def mixed_calibration(gpu):
+    """HBM rates of plain PyTorch kernels whose reads and writes come in a
+    fixed ratio (f32): a copy (1:1) and sums over the leading dimension of
+    [2, n] and [6, n] tensors (2:1, 6:1).  Reference figures for the kernels
+    that also write what they read (the combine reads six rows per row
+    written); medians of 20 launches after 3 warm-up launches."""
+    torch = gpu.torch
+
+    def rate(fn, nbytes):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [gpu.event() for _ in range(21)]
+        ev[0].record()
+        for i in range(20):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        s = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(20)])) / 1e3
+        return {"us": round(s * 1e6, 1), "gbs": round(nbytes / s / 1e9, 1)}
+
+    out = {}
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.float32, device=gpu.dev)
+    dst = torch.empty_like(src)
+    out["copy_1gib"] = rate(lambda: dst.copy_(src), 2 * n * 4)
+    del src, dst
+    for rows, n in ((2, 64 << 20), (6, 4096 * 4096)):
+        a = torch.ones((rows, n), dtype=torch.float32, device=gpu.dev)
+        o = torch.empty(n, dtype=torch.float32, device=gpu.dev)
+        out["sum_%d_rows_of_%d" % (rows, n)] = rate(lambda: torch.sum(a, dim=0, out=o), (rows + 1) * n * 4)
+        del a, o
+    return out
+
+
 def with_hbm_fraction(line, calib):
     """Adds the kernel's fraction of the calibrated read rate to an
     HBM-bound line."""
@@ -719,6 +756,9 @@ def main():
     ap.add_argument("--only", action="store_true",
                     help="time the named workload alone (no other workloads after the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mixed-calibration", action="store_true",
+                    help="only print the HBM rates of plain PyTorch copy and row-sum kernels "
+                         "(read:write 1:1, 2:1 and 6:1)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer --steps times (a plain copy "
                          "kernel of known size, to scale hardware byte counters)")
@@ -733,6 +773,9 @@ def main():
         sys.exit(2)
 
     gpu = Gpu()
+    if args.mixed_calibration:
+        print(json.dumps({"mixed_calibration": mixed_calibration(gpu)}), flush=True)
+        return
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = gpu.torch.ones(n, dtype=gpu.torch.uint8, device=gpu.dev)
