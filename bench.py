@@ -47,7 +47,10 @@ stream it runs on (gmm_us; median and minimum beside it).  hbm_calibration
 and mfma_calibration report the read rate and the matrix-unit rate this part
 sustains on plain loops, with the kernel's fraction of them
 (--mixed-calibration prints, alone, what plain PyTorch copy and row-sum
-kernels reach when reads and writes mix, the regime of the combine).  The CPU
+kernels reach when reads and writes mix, the regime of the combine;
+--prefill-breakdown prints the matrix-unit rate of the tiled kernel's wave
+tile with each part of its data movement added, and the rate of a plain bf16
+library matmul of the prefill shape).  The CPU
 baseline times the float64 oracle on a bounded sample of the same workload on
 the host cores; gpu_over_cpu is value over its value.
 """
@@ -653,6 +656,98 @@ def mfma_calibration(gpu, achieved_tflops):
                     "%d workgroups of 4 waves, %.1f ms per launch" % (CALIB_BLOCKS, float(np.median(ms)))}
 
 
+def prefill_breakdown(gpu):
+    """The tiled kernel's wave tile built up from the matrix unit alone
+    (moe_calib_mfma_parts), one part of its data movement at a time, then all
+    of it, then all of it at 6 of 8 row subtiles (bands of about 96 rows).
+    Operands as in mfma_calibration; 512 workgroups of 4 waves over 8,000
+    chunks per wave (about 20-40 ms per launch); codes from a 2 GiB buffer,
+    staging from 1 MiB (L2 hits) or 32 MiB (misses).  Best and median of 4
+    launches after one warm-up."""
+    torch, moe = gpu.torch, gpu.moe
+    from moe_grouped_gemm_route_amd.synth import make_problem
+
+    q = make_problem(T=2048, k=1, E=1, K=4096, N=1024, seed=41)
+    a = gpu.put(q["x"])
+    packed = moe.mxfp4_encode(gpu.put(q["codes"]), gpu.put(q["scales"]), None, moe.MXFP4)
+    b = moe.debug_decode(packed, moe.MXFP4, 1, 1024, 4096)
+    del packed
+    g = torch.Generator(device=gpu.dev)
+    g.manual_seed(43)
+    codes = torch.randint(0, 256, (2 << 30,), dtype=torch.uint8, device=gpu.dev, generator=g)
+    x = torch.randn(16 << 20, dtype=torch.float32, device=gpu.dev, generator=g).to(torch.bfloat16)
+    blocks, chunks = CALIB_BLOCKS, 8000
+    P = moe
+    rows = [
+        ("operands in registers", 0, 8, 0),
+        ("a barrier per chunk", P.PARTS_BARRIER, 8, 0),
+        ("decode of register-held codes that change every chunk", P.PARTS_REG_DECODE, 8, 0),
+        ("A fragments read from LDS", P.PARTS_LDS_A, 8, 0),
+        ("activation chunks staged to LDS from 1 MiB (L2 hits), wait and barrier", P.PARTS_STAGE, 8, 1),
+        ("the same staging from 32 MiB (L2 misses)", P.PARTS_STAGE, 8, 32),
+        ("codes streamed from HBM, only XOR-ed", P.PARTS_CODES_XOR, 8, 0),
+        ("codes streamed from HBM and decoded", P.PARTS_CODES, 8, 0),
+        ("all: LDS A reads, code stream and decode, staging from 1 MiB",
+         P.PARTS_LDS_A | P.PARTS_CODES | P.PARTS_STAGE, 8, 1),
+        ("all, staging from 32 MiB", P.PARTS_LDS_A | P.PARTS_CODES | P.PARTS_STAGE, 8, 32),
+        ("all at 6 of 8 row subtiles, staging from 1 MiB", P.PARTS_LDS_A | P.PARTS_CODES | P.PARTS_STAGE, 6, 1),
+        ("all at 6 of 8 row subtiles, staging from 32 MiB", P.PARTS_LDS_A | P.PARTS_CODES | P.PARTS_STAGE, 6, 32),
+    ]
+    out = []
+    for label, parts, rows16, xmib in rows:
+        xs = x[: (max(xmib, 1) << 20) // 2]
+        run = lambda: moe.calib_mfma_parts(parts, rows16, a, b, codes, xs, 2.0 ** -5, blocks, chunks)
+        run()
+        ms = []
+        for _ in range(4):
+            e0, e1 = gpu.event(), gpu.event()
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        flops = blocks * 4.0 * chunks * 4 * rows16 * 4 * 16384
+        rec = {"label": label, "parts": parts, "rows16": rows16,
+               "pflops_best": round(flops / (min(ms) / 1e3) / 1e15, 3),
+               "pflops_median": round(flops / (float(np.median(ms)) / 1e3) / 1e15, 3),
+               "ms_median": round(float(np.median(ms)), 2)}
+        if parts & (P.PARTS_CODES | P.PARTS_CODES_XOR):
+            rec["codes_tbs"] = round(blocks * 4.0 * chunks * 4096 / (float(np.median(ms)) / 1e3) / 1e12, 2)
+        out.append(rec)
+        print("bench: %s %.3f PFLOP/s" % (label, rec["pflops_median"]), file=sys.stderr, flush=True)
+    return {"blocks": blocks, "chunks": chunks, "rows": out}
+
+
+def library_matmul(gpu):
+    """A plain bf16 torch.matmul (hipBLASLt) of the 4,096-token w13 prefill's
+    shape, [24,576 x 4,096] x [4,096 x 4,096], N(0,1) operands: warmed up for
+    half a second (the shader clock settles under sustained matrix work),
+    then 20 launches timed with HIP events; median and best."""
+    torch = gpu.torch
+    g = torch.Generator(device=gpu.dev)
+    g.manual_seed(44)
+    M, K, N = 24576, 4096, 4096
+    A = torch.randn((M, K), dtype=torch.float32, device=gpu.dev, generator=g).to(torch.bfloat16)
+    B = torch.randn((K, N), dtype=torch.float32, device=gpu.dev, generator=g).to(torch.bfloat16).contiguous()
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=gpu.dev)
+    t0 = time.time()
+    while time.time() - t0 < 0.5:
+        for _ in range(8):
+            torch.matmul(A, B, out=C)
+        torch.cuda.synchronize()
+    ev = [gpu.event() for _ in range(21)]
+    ev[0].record()
+    for i in range(20):
+        torch.matmul(A, B, out=C)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(20)]
+    flops = 2.0 * M * K * N
+    return {"shape": [M, K, N], "us_median": round(float(np.median(ms)) * 1e3, 1),
+            "us_min": round(min(ms) * 1e3, 1),
+            "pflops_median": round(flops / (float(np.median(ms)) / 1e3) / 1e15, 3)}
+
+
 def hbm_calibration(gpu):
     """The HBM read rate this part sustains (moe_calib_hbm_read: 16-byte
     non-temporal loads, each wave reading contiguous 1 KiB runs, over a 2 GiB
@@ -756,6 +851,10 @@ def main():
     ap.add_argument("--only", action="store_true",
                     help="time the named workload alone (no other workloads after the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-breakdown", action="store_true",
+                    help="only print the matrix-unit rate of the tiled kernel's wave tile with each "
+                         "part of its data movement added (moe_calib_mfma_parts), and a plain bf16 "
+                         "torch.matmul of the 4,096-token w13 shape")
     ap.add_argument("--mixed-calibration", action="store_true",
                     help="only print the HBM rates of plain PyTorch copy and row-sum kernels "
                          "(read:write 1:1, 2:1 and 6:1)")
@@ -773,6 +872,10 @@ def main():
         sys.exit(2)
 
     gpu = Gpu()
+    if args.prefill_breakdown:
+        print(json.dumps({"prefill_breakdown": prefill_breakdown(gpu), "library_matmul": library_matmul(gpu)}),
+              flush=True)
+        return
     if args.mixed_calibration:
         print(json.dumps({"mixed_calibration": mixed_calibration(gpu)}), flush=True)
         return

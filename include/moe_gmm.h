@@ -395,6 +395,55 @@ int moe_calib_mfma_bf16(const uint16_t* a, const uint16_t* b, int32_t blocks,
                         int32_t iters, float* out, void* stream);
 
 /*
+ * moe_calib_mfma_parts - measurement support: the bf16 matrix-unit rate of
+ * the tiled grouped matmul's wave tile (rows16 row subtiles, 6 or 8, x 4
+ * column subtiles of v_mfma_f32_16x16x32_bf16; 128-deep chunks of 4 steps)
+ * with chosen parts of that kernel's data movement beside it, so that the
+ * rate each part costs can be read off one at a time.  parts is one of:
+ *   0                          operands in registers only;
+ *   MOE_PARTS_LDS_A            A fragments read from LDS (one 1 KiB read per
+ *                              wave, row subtile and step);
+ *   MOE_PARTS_CODES            B decoded (scaled e2m1 convert) from codes
+ *                              streamed from HBM, 4 KiB per wave and chunk,
+ *                              one chunk ahead;
+ *   MOE_PARTS_STAGE            an 8 KiB activation chunk per wave copied
+ *                              into LDS by direct-to-LDS loads, then a wait
+ *                              for all loads and a workgroup barrier;
+ *   MOE_PARTS_BARRIER          a workgroup barrier per chunk only;
+ *   MOE_PARTS_REG_DECODE       B decoded from register-held codes that change
+ *                              every chunk;
+ *   MOE_PARTS_CODES_XOR        the code stream, only XOR-ed into a register;
+ *   MOE_PARTS_LDS_A | MOE_PARTS_CODES | MOE_PARTS_STAGE   all of the kernel's.
+ *
+ * a      [blocks*256*8] 16-byte A fragments (8 bf16), lane-major as in
+ *        moe_calib_mfma_bf16; the first 4096 fragments from workgroup g's
+ *        start also fill its LDS.
+ * b      [blocks*256*4] 16-byte B fragments (used when B is not decoded).
+ * codes  [codes_bytes] e2m1 codes, cut into blocks*4 equal regions (one per
+ *        wave, a multiple of 4 KiB, at least 4 KiB); a wave reads its region
+ *        as four streams that wrap.  Make it larger than the 256 MiB
+ *        last-level cache for HBM reads.
+ * x      [x_bytes] staging source, a multiple of 1 KiB; the copies wrap at
+ *        x_bytes (1 MiB stays in L2, 32 MiB does not).
+ * scale  decode scale; only its exponent is applied (a power of two is exact).
+ * out    [blocks*256] f32: each lane's sum of its accumulators (+1 if the
+ *        XOR of the codes it read is odd, MOE_PARTS_CODES_XOR only).
+ * FLOPs per call: blocks * 4 * chunks * 4 * rows16 * 4 * 16384.  Limits:
+ * 1 <= blocks <= 65535, 2 <= chunks <= 2^24 and even, a wave region below
+ * 2^31 bytes, 8 KiB <= x_bytes < 2^31; every pointer 16-byte aligned (out 4).
+ * An unsupported parts value or rows16 returns MOE_ERR_SHAPE.
+ */
+#define MOE_PARTS_LDS_A 1
+#define MOE_PARTS_CODES 2
+#define MOE_PARTS_STAGE 4
+#define MOE_PARTS_BARRIER 8
+#define MOE_PARTS_REG_DECODE 16
+#define MOE_PARTS_CODES_XOR 32
+int moe_calib_mfma_parts(int32_t parts, int32_t rows16, const uint16_t* a, const uint16_t* b,
+                         const void* codes, size_t codes_bytes, const uint16_t* x, size_t x_bytes,
+                         float scale, int32_t blocks, int32_t chunks, float* out, void* stream);
+
+/*
  * moe_calib_hbm_read - measurement support: the HBM read rate this part
  * sustains with the weight-streaming kernel's access pattern (each wave walks
  * its own contiguous region of src in 1 KiB runs, one 16-byte non-temporal

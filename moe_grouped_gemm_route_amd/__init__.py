@@ -52,6 +52,8 @@ _SIGNATURES = {
     "moe_debug_decode": (ctypes.c_int, [_vp, ctypes.c_int, _i32, _i32, _i32, _vp, _vp]),
     "moe_calib_mfma_bf16": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp]),
     "moe_calib_hbm_read": (ctypes.c_int, [_vp, _sz, _i32, _vp, _vp]),
+    "moe_calib_mfma_parts": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _sz, _vp, _sz, ctypes.c_float, _i32, _i32,
+                                            _vp, _vp]),
 }
 
 
@@ -332,6 +334,32 @@ def calib_mfma_bf16(a, b, blocks, iters):
         raise MoeGmmError("calib_mfma_bf16: a needs %d and b %d bf16 values" % (lanes * 64, lanes * 32))
     out = torch.empty(lanes, dtype=torch.float32, device=a.device)
     _check(library().moe_calib_mfma_bf16(_ptr(a), _ptr(b), blocks, iters, _ptr(out), _stream()))
+    return out
+
+
+PARTS_LDS_A, PARTS_CODES, PARTS_STAGE, PARTS_BARRIER, PARTS_REG_DECODE, PARTS_CODES_XOR = 1, 2, 4, 8, 16, 32
+
+
+def calib_mfma_parts(parts, rows16, a, b, codes, x, scale, blocks, chunks):
+    """moe_calib_mfma_parts: the tiled kernel's wave tile (rows16 row subtiles
+    x 4 column subtiles) over chunks 128-deep chunks per wave, with the data
+    movement named by parts (PARTS_* bits).  a and b as for calib_mfma_bf16;
+    codes and x are device buffers (any dtype) of the code stream and the
+    staging source.  Returns the [blocks*256] f32 sums; FLOPs = blocks * 4 *
+    chunks * 4 * rows16 * 4 * 16384."""
+    a = _bits16(a, "a")
+    b = _bits16(b, "b")
+    lanes = blocks * 256
+    if a.numel() < lanes * 64 or b.numel() < lanes * 32:
+        raise MoeGmmError("calib_mfma_parts: a needs %d and b %d bf16 values" % (lanes * 64, lanes * 32))
+    for name, t in (("codes", codes), ("x", x)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise MoeGmmError("%s must be a contiguous CUDA (HIP) tensor" % name)
+    out = torch.empty(lanes, dtype=torch.float32, device=a.device)
+    _check(library().moe_calib_mfma_parts(parts, rows16, _ptr(a), _ptr(b), _ptr(codes),
+                                          codes.numel() * codes.element_size(), _ptr(x),
+                                          x.numel() * x.element_size(), float(scale), blocks, chunks, _ptr(out),
+                                          _stream()))
     return out
 
 

@@ -252,6 +252,23 @@ int moe_calib_mfma_bf16(const uint16_t* a, const uint16_t* b, int32_t blocks, in
   return hip_status(moe::launch_calib_mfma(a, b, blocks, iters, out, static_cast<hipStream_t>(stream)));
 }
 
+int moe_calib_mfma_parts(int32_t parts, int32_t rows16, const uint16_t* a, const uint16_t* b,
+                         const void* codes, size_t codes_bytes, const uint16_t* x, size_t x_bytes,
+                         float scale, int32_t blocks, int32_t chunks, float* out, void* stream) {
+  if (!a || !b || !codes || !x || !out) return MOE_ERR_NULL;
+  if (!moe::calib_parts_supported(parts) || (rows16 != 6 && rows16 != 8)) return MOE_ERR_SHAPE;
+  if (blocks < 1 || blocks > 65535 || chunks < 2 || chunks > (1 << 24) || chunks % 2 != 0) return MOE_ERR_SHAPE;
+  const uint64_t region = (uint64_t)codes_bytes / ((uint64_t)blocks * 4) / 4096 * 4096;
+  if (region < 4096 || region >= (1ull << 31)) return MOE_ERR_SHAPE;
+  if (x_bytes < 8192 || x_bytes % 1024 != 0 || x_bytes >= (1ull << 31)) return MOE_ERR_SHAPE;
+  if (((uintptr_t)a & 15) || ((uintptr_t)b & 15) || ((uintptr_t)codes & 15) || ((uintptr_t)x & 15) ||
+      ((uintptr_t)out & 3))
+    return MOE_ERR_SHAPE;
+  return hip_status(moe::launch_calib_parts(parts, rows16, a, b, codes, (uint32_t)region, x,
+                                            (uint32_t)(x_bytes / 1024), scale, blocks, chunks, out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int moe_calib_hbm_read(const void* src, size_t bytes, int32_t blocks, uint32_t* out, void* stream) {
   if (!src || !out) return MOE_ERR_NULL;
   if (bytes < 16 || bytes % 16 != 0 || blocks < 1 || blocks > 65535) return MOE_ERR_SHAPE;

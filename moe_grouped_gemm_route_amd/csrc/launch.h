@@ -68,6 +68,14 @@ hipError_t launch_quantize_mxfp4(const uint16_t* x, int32_t R, int32_t K, uint8_
 hipError_t launch_calib_mfma(const uint16_t* a, const uint16_t* b, int32_t blocks, int32_t iters, float* out,
                              hipStream_t stream);
 
+// Matrix-unit build-up: the tiled kernel's wave tile (rows16 row subtiles,
+// 6 or 8) with the data movement named by parts (a supported combination of
+// the PARTS_* bits in calib.hip), chunks 128-deep chunks per wave.
+bool calib_parts_supported(int32_t parts);
+hipError_t launch_calib_parts(int32_t parts, int32_t rows16, const uint16_t* a, const uint16_t* b,
+                              const void* codes, uint32_t region, const uint16_t* x, uint32_t x_blocks,
+                              float scale, int32_t blocks, int32_t chunks, float* out, hipStream_t stream);
+
 // HBM read calibration: blocks workgroups of 256 threads XOR-reduce the
 // 16-byte words of src (bytes a multiple of 16) into out[blocks * 256].
 hipError_t launch_calib_hbm_read(const void* src, size_t bytes, int32_t blocks, uint32_t* out,

@@ -215,6 +215,36 @@ def test_calib_validation(lib):
     assert f(ctypes.c_void_p((1 << 30) + 8), FAKE_ALIGNED, 1, 1, FAKE_ALIGNED, None) == ERR_SHAPE
 
 
+def test_calib_parts_validation(lib):
+    f = lib.moe_calib_mfma_parts
+    A = FAKE_ALIGNED
+    ok = dict(parts=0, rows16=8, a=A, b=A, codes=A, codes_bytes=1 << 20, x=A, x_bytes=8192, scale=1.0,
+              blocks=4, chunks=2, out=A)
+
+    def call(**kw):
+        d = dict(ok, **kw)
+        return f(d["parts"], d["rows16"], d["a"], d["b"], d["codes"], d["codes_bytes"], d["x"], d["x_bytes"],
+                 ctypes.c_float(d["scale"]), d["blocks"], d["chunks"], d["out"], None)
+
+    for name in ("a", "b", "codes", "x", "out"):
+        assert call(**{name: None}) == ERR_NULL
+    for parts in (3, 5, 6, 64, -1, 1 | 2 | 4 | 8):
+        assert call(parts=parts) == ERR_SHAPE
+    assert call(rows16=7) == ERR_SHAPE
+    assert call(blocks=0) == ERR_SHAPE
+    assert call(blocks=65536) == ERR_SHAPE
+    assert call(chunks=0) == ERR_SHAPE
+    assert call(chunks=3) == ERR_SHAPE
+    assert call(chunks=(1 << 24) + 2) == ERR_SHAPE
+    assert call(codes_bytes=4 * 4096 - 1) == ERR_SHAPE        # a wave region under 4 KiB
+    assert call(blocks=1, codes_bytes=4 << 31) == ERR_SHAPE   # a wave region of 2 GiB
+    assert call(x_bytes=4096) == ERR_SHAPE
+    assert call(x_bytes=8192 + 512) == ERR_SHAPE
+    assert call(x_bytes=1 << 31) == ERR_SHAPE
+    assert call(a=ctypes.c_void_p((1 << 30) + 8)) == ERR_SHAPE
+    assert call(x=ctypes.c_void_p((1 << 30) + 8)) == ERR_SHAPE
+
+
 def test_binding_rejects_host_tensors():
     import torch
     with pytest.raises(moe.MoeGmmError):

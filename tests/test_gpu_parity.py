@@ -1024,6 +1024,31 @@ def test_calib_mfma_closed_form():
 
 
 
+def test_calib_parts_closed_form():
+    # all-ones A, B, staging source and decoded codes (byte 0x22: two e2m1
+    # codes of 1.0, scale 1): every MFMA adds 32 to each of a lane's 4
+    # accumulator elements, so a lane's sum is 4 * rows16 * 4 * 32 * 4 *
+    # chunks = 2048 * rows16 * chunks whatever data movement runs beside it
+    # (the code stream wraps inside each wave's 8 KiB region, the staging
+    # inside 8 KiB); the register-decode part decodes changing codes, so its
+    # sums are only finite
+    blocks, chunks = 3, 10
+    a = torch.full((blocks * 256 * 64,), 1.0, dtype=torch.bfloat16, device="cuda")
+    b = torch.full((blocks * 256 * 32,), 1.0, dtype=torch.bfloat16, device="cuda")
+    codes = torch.full((blocks * 4 * 8192,), 0x22, dtype=torch.uint8, device="cuda")
+    x = torch.full((4096,), 1.0, dtype=torch.bfloat16, device="cuda")
+    P = moe
+    for rows16 in (8, 6):
+        for parts in (0, P.PARTS_LDS_A, P.PARTS_CODES, P.PARTS_STAGE, P.PARTS_BARRIER, P.PARTS_CODES_XOR,
+                      P.PARTS_LDS_A | P.PARTS_CODES | P.PARTS_STAGE):
+            out = moe.calib_mfma_parts(parts, rows16, a, b, codes, x, 1.0, blocks, chunks)
+            torch.cuda.synchronize()
+            assert torch.all(out == 2048.0 * rows16 * chunks), (parts, rows16, out[:4])
+        out = moe.calib_mfma_parts(P.PARTS_REG_DECODE, rows16, a, b, codes, x, 1.0, blocks, chunks)
+        torch.cuda.synchronize()
+        assert torch.all(torch.isfinite(out))
+
+
 def test_calib_hbm_read_closed_form():
     # the XOR of every thread's partial is the XOR of the buffer's 32-bit
     # words: regions of unequal length, bytes past the last whole 1 KiB run,
