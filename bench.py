@@ -18,7 +18,9 @@ benchmark workload (fewer steps each, and a shorter CPU-baseline sample) and
 reports them in the same line under "workloads": tiny (64 tokens, 8 experts),
 w2_decode (256 tokens, Zipf routing, K = 2048, with the combine), w13_prefill
 (4,096 tokens), nvfp4_w13 (256 tokens, NVFP4 weights from the lossless cast),
-and the whole routed-expert layer at decode and at prefill.
+nvfp4_w13_prefill, the whole routed-expert layer at decode and at prefill
+(layer_decode, layer_prefill), and the W4A4 w13 prefill and layer
+(w4a4_w13_prefill, w4a4_layer_prefill).
 
 Other workloads, run alone with --workload:
   layer_decode / layer_prefill: route-sort -> w13 with the SiLU-gated gate/up
@@ -31,8 +33,8 @@ Other workloads, run alone with --workload:
   bf16_w13_decode, bf16_w2_decode, bf16_w13_prefill: the bf16-weight
     comparison arm on the decoded weights of configs 2, 3 and 4 (the same
     values, four times the bytes) next to the MXFP4 kernel on the same inputs;
-  nvfp4_w13_prefill: the 4,096-token w13 with NVFP4 weights from the lossless
-    cast, next to the MXFP4 kernel on the same inputs;
+  nvfp4_w13_prefill (also in the default run): the 4,096-token w13 with NVFP4
+    weights from the lossless cast, next to the MXFP4 kernel on the same inputs;
   route_sort_decode / route_sort_prefill: the route sort alone on config 2's
     384 or config 4's 24,576 token-expert pairs (Mpairs/s).
 --tokens T replaces a workload's token count (the weights stay the config's;
@@ -85,7 +87,7 @@ ROUTE_WORKLOADS = {"route_sort_decode": 2, "route_sort_prefill": 4}   # the rout
 WORKLOADS = sorted(list(GMM_WORKLOADS) + list(LAYER_WORKLOADS) + list(W4A4_WORKLOADS) + list(ROUTE_WORKLOADS))
 # timed after the headline in the default run
 EXTRA_WORKLOADS = ("tiny", "w2_decode", "w13_prefill", "nvfp4_w13", "nvfp4_w13_prefill", "layer_decode",
-                   "layer_prefill")
+                   "layer_prefill", "w4a4_w13_prefill", "w4a4_layer_prefill")
 KERNELS = {"auto": 0, "stream": 1, "tiled": 2}
 GMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_route_amd", "csrc", "gmm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
