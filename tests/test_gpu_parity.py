@@ -1009,6 +1009,64 @@ def test_config3_w2_then_combine():
     assert rel_err(out[np.ix_(toks, cols)], ref) <= REL_TOL
 
 
+# ----------------------------------------------------- graph capture ---
+@pytest.mark.parametrize("w4a4", [False, True])
+def test_graph_capture_layer_replays_match_eager(w4a4):
+    # one routed-expert layer (route sort into a caller workspace, w13 with
+    # the fused activation, w2, combine; the W4A4 layer also quantizes x and
+    # h) captured once in a HIP graph, then replayed on new routing,
+    # activations and router weights copied into the captured inputs: every
+    # replay equals the eager calls on the same inputs bit for bit, with eager
+    # work and host synchronisations between the replays.  No call of the
+    # path records a memset or an allocation of its own.
+    E, K, N, T, k = 8, 256, 512, 80, 3
+    H, M = N // 2, T * k
+    probs = [make_problem(T=T, k=k, E=E, K=K, N=N, seed=320 + i, routing="zipf" if i % 2 else "uniform")
+             for i in range(5)]
+    _, pk13 = weights_for(probs[0], "mxfp4")
+    rng = np.random.default_rng(330)
+    w2c = rng.integers(0, 256, size=(E, K, H // 2), dtype=np.uint8)
+    w2s = (rng.integers(-6, -1, size=(E, K, H // 32)) + 127).astype(np.uint8)
+    pk2 = moe.mxfp4_encode(to_dev(w2c), to_dev(w2s), None, moe.MXFP4)
+    ids, x, tw = to_dev(probs[0]["topk_ids"]), to_dev(probs[0]["x"]), to_dev(probs[0]["topk_weights"])
+    ws = torch.empty(moe.route_sort_workspace_bytes(T, k, E) // 4 + 1, dtype=torch.int32, device=DEV)
+
+    def layer():
+        r = moe.route_sort(ids, E, ws=ws)
+        if w4a4:
+            qc, qs = moe.mxfp4_quantize(x)
+            h = moe.moe_gmm_w4a4(pk13, E, N, K, qc, qs, r["group_offsets"], M, row_index=r["sorted_token"],
+                                 out_dtype=moe.BF16, act=moe.ACT_SILU_MUL)
+            hc, hs = moe.mxfp4_quantize(h)
+            y2 = moe.moe_gmm_w4a4(pk2, E, K, H, hc, hs, r["group_offsets"], M)
+        else:
+            h = moe.moe_gmm(pk13, moe.MXFP4, E, N, K, x, r["group_offsets"], M, row_index=r["sorted_token"],
+                            out_dtype=moe.BF16, act=moe.ACT_SILU_MUL)
+            y2 = moe.moe_gmm(pk2, moe.MXFP4, E, K, H, h, r["group_offsets"], M)
+        return moe.moe_combine(y2, tw, r["pair_row"])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out_g = layer()
+    torch.cuda.synchronize()
+    for i, p in enumerate(probs):
+        ids.copy_(to_dev(p["topk_ids"]))
+        x.copy_(to_dev(p["x"]))
+        tw.copy_(to_dev(p["topk_weights"]))
+        ref = layer()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, ref), i
+        assert bool(torch.isfinite(ref).all())
+
+
 # ------------------------------------------------------- calibration ---
 def test_calib_mfma_closed_form():
     # all-ones A with B = 1 or 2: every 16x16x32 MFMA adds 32 * b to each of
