@@ -140,24 +140,12 @@ __device__ __forceinline__ void chunk_scales(uint32_t word, int kc, float& lo, f
   }
 }
 
-// Stream kernel: NVFP4 chunks whose E4M3 scales are all powers of two (for
-// instance every chunk made by the lossless MXFP4 cast) take the
-// one-instruction decode; a wave with any other scale in the chunk takes the
-// general exact decode.  Both give the same bits.  (The tiled kernel makes
-// this choice once per walk: its unrolled chunk has no registers for two
-// decode paths.)
-template <int FMT, int NS>
-__device__ __forceinline__ bool general_scales(const float (&lo)[NS], const float (&hi)[NS]) {
-  if (FMT == 0) return false;
-  bool all = true;
-#pragma unroll
-  for (int ns = 0; ns < NS; ++ns) all = all && is_pow2_scale(lo[ns]) && is_pow2_scale(hi[ns]);
-  return __ballot(!all) != 0;
-}
-
-template <int FMT>
-__device__ __forceinline__ u32x4_t decode_step(uint32_t codes8, float scale, bool general) {
-  if (FMT == 1 && general) return decode8_any_scale(codes8, scale);
+// GEN (NVFP4 only): some block scale of the wave's columns is not a power of
+// two (span_scales_pow2 below), so every step takes the general exact decode;
+// otherwise the one-instruction decode.  Both give the same bits.
+template <int FMT, bool GEN>
+__device__ __forceinline__ u32x4_t decode_step(uint32_t codes8, float scale) {
+  if (FMT == 1 && GEN) return decode8_any_scale(codes8, scale);
   return decode8(codes8, scale);
 }
 
@@ -198,6 +186,22 @@ __device__ __forceinline__ void store_tile(void* y, int64_t N, int row0, int row
 template <int ACT>
 __device__ __forceinline__ int col_sub(int ns, int h16) {
   return (ACT == 1 && ns >= 2) ? ns - 2 + h16 : ns;
+}
+
+// NVFP4: true when every block scale (E4M3) in a wave's four 16-column
+// subtiles is a positive power of two, the case the one-instruction decode
+// handles exactly (for instance every pack made by the lossless MXFP4 cast).
+// The encoder stores a flag word per (expert, subtile); each kernel's wave
+// reads its four (uniform loads) once, before its K walk, and walks with one
+// decode.
+template <int ACT>
+__device__ __forceinline__ bool span_scales_pow2(const uint8_t* __restrict__ packed, const Layout& L, int64_t et,
+                                                 int h16) {
+  const uint32_t* flags = reinterpret_cast<const uint32_t*>(packed + L.flags_off) + et;
+  uint32_t any = 0;
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) any |= flags[col_sub<ACT>(ns, h16)];
+  return any == 0;
 }
 
 // The gate/up activation of one 16x16 tile pair: silu(gate) * up, with
@@ -253,7 +257,7 @@ constexpr uint32_t BUF_OOB = 0x7FFF0000u;  // a lane offset that reads zeros
 // lane offsets); activation rows past the band read zeros from outside the
 // buffer.
 // ---------------------------------------------------------------------------
-template <int NS, int D, int MSUB, int FMT, bool OBF16, int ACT>
+template <int NS, int D, int MSUB, int FMT, bool OBF16, int ACT, bool GEN>
 __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, const Layout& L,
                                             const Tile& tile, int n0, int h16, __amdgpu_buffer_rsrc_t xr,
                                             const uint32_t (&a_voff)[2], __amdgpu_buffer_rsrc_t cr,
@@ -323,11 +327,9 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
           for (int q = 0; q < 4; ++q) a[ms][q] = aring[d][ms][q];
         if (kc + D < KC) load_step(d, kc + D);
         float lo[NS], hi[NS];
-        bool general = false;
         if constexpr (FMT != 2) {
 #pragma unroll
           for (int ns = 0; ns < NS; ++ns) chunk_scales<FMT>(w[ns], kc, lo[ns], hi[ns]);
-          general = general_scales<FMT, NS>(lo, hi);
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -335,7 +337,7 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
           for (int ns = 0; ns < NS; ++ns) {
             u32x4_t b;
             if constexpr (FMT == 2) b = c[ns][s];
-            else b = decode_step<FMT>(c[ns][0][s], s < 2 ? lo[ns] : hi[ns], general);
+            else b = decode_step<FMT, GEN>(c[ns][0][s], s < 2 ? lo[ns] : hi[ns]);
 #pragma unroll
             for (int ms = 0; ms < MSUB; ++ms)
               acc[ms][ns] = mfma(as_bf16x8(a[ms][s]), as_bf16x8(b), acc[ms][ns]);
@@ -410,10 +412,21 @@ __global__ __launch_bounds__(256, NS > 4 ? 2 : 3) void gmm_stream_kernel(const u
       a_voff[ms] = (uint32_t)(src * K * 2 + g * 64);
     }
   }
+  if constexpr (FMT == 1) {
+    static_assert(NS == 4, "the NVFP4 flags cover a wave's four subtiles");
+    if (!span_scales_pow2<ACT>(packed, L, et, h16)) {
+      if (MS == 2 && tile.rows > 16)
+        stream_walk<NS, (D > 1 ? D - 1 : 1), 2, FMT, OBF16, ACT, true>(packed, L, tile, n0, h16, xr, a_voff, cr, sr,
+                                                                       y);
+      else
+        stream_walk<NS, D, 1, FMT, OBF16, ACT, true>(packed, L, tile, n0, h16, xr, a_voff, cr, sr, y);
+      return;
+    }
+  }
   if (MS == 2 && tile.rows > 16)
-    stream_walk<NS, (D > 1 ? D - 1 : 1), 2, FMT, OBF16, ACT>(packed, L, tile, n0, h16, xr, a_voff, cr, sr, y);
+    stream_walk<NS, (D > 1 ? D - 1 : 1), 2, FMT, OBF16, ACT, false>(packed, L, tile, n0, h16, xr, a_voff, cr, sr, y);
   else
-    stream_walk<NS, D, 1, FMT, OBF16, ACT>(packed, L, tile, n0, h16, xr, a_voff, cr, sr, y);
+    stream_walk<NS, D, 1, FMT, OBF16, ACT, false>(packed, L, tile, n0, h16, xr, a_voff, cr, sr, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -449,6 +462,7 @@ __global__ __launch_bounds__(256, NS > 4 ? 2 : 3) void gmm_stream_kernel(const u
 // ---------------------------------------------------------------------------
 constexpr int TL_MS = 8;                    // 16-row subtiles per tile
 constexpr int TL_NS = 4;                    // 16-column subtiles per wave
+static_assert(TL_NS == 4, "span_scales_pow2 reads the flags of four subtiles");
 constexpr int TL_WAVES = 4;
 constexpr int TL_BM = 16 * TL_MS;           // 128
 constexpr int TL_BN = TL_WAVES * 16 * TL_NS;   // 256
@@ -690,19 +704,6 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
   }
   if (k0 < KC) chunk(B0{}, k0);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>());
-}
-
-// True when every block scale (E4M3) in the wave's columns is a positive
-// power of two, the case the one-instruction decode handles exactly: the
-// encoder's per-subtile flags (uniform loads) say so.
-template <int ACT>
-__device__ __forceinline__ bool span_scales_pow2(const uint8_t* __restrict__ packed, const Layout& L, int64_t et,
-                                                 int h16) {
-  const uint32_t* flags = reinterpret_cast<const uint32_t*>(packed + L.flags_off) + et;
-  uint32_t any = 0;
-#pragma unroll
-  for (int ns = 0; ns < TL_NS; ++ns) any |= flags[col_sub<ACT>(ns, h16)];
-  return any == 0;
 }
 
 template <int FMT, bool OBF16, int ACT>
