@@ -451,7 +451,8 @@ __global__ __launch_bounds__(256, NS > 4 ? 2 : 3) void gmm_stream_kernel(const u
 // is refilled with chunk kc+2.  The last chunk still stages into buffer
 // (kc+1) & 1, which the previous barrier freed, but from an offset past the
 // activation buffer, so those loads write zeros without fetching anything;
-// its code loads repeat the last chunk's into the unused register slot.
+// its code loads take a lane offset past the codes, so they fetch nothing
+// either.
 //
 // A-fragment reads are ds_read_b128 issued P - 1 fragments ahead of their
 // MFMAs (inline asm, so the compiler cannot sink them next to their use);
@@ -616,11 +617,12 @@ __device__ __forceinline__ void tiled_k_walk_bf16(uint8_t* s_a, __amdgpu_buffer_
   auto chunk = [&](auto bc, int kc) {
     constexpr int d = decltype(bc)::value;   // kc & 1: LDS buffer
     const int kn = min(kc + 1, KC - 1);
+    const uint32_t cvn = kc + 1 < KC ? c_voff : BUF_OOB;   // past the last chunk: no fetch
     stage(d ^ 1, stage_soff(kc + 1, KC));
     __builtin_amdgcn_sched_barrier(0);       // the activation loads go first
     u32x4_t ar[P];
     tiled_prologue<NSUB, P, d>(std::make_index_sequence<PRO>{}, ar, va);
-    tiled_chunk_bf16<NSUB, P, d, ACT>(std::make_index_sequence<FT>{}, ar, va, bw, cr, c_voff, KC, h16, kn, acc);
+    tiled_chunk_bf16<NSUB, P, d, ACT>(std::make_index_sequence<FT>{}, ar, va, bw, cr, cvn, KC, h16, kn, acc);
     vm_wait_barrier<4 * TL_NS>();
   };
   using B0 = std::integral_constant<int, 0>;
@@ -668,20 +670,24 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
     for (int j = 0; j < TL_LOADS; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(dst + j * 1024), 16, avo[j], soff, 0, 0);
   };
-  auto load_codes = [&](int slot, int kc) {
+  // past the last chunk the lane offsets point beyond the codes and scale
+  // words, so the loads fetch nothing (a branch around them would cost
+  // registers across the unrolled walk)
+  auto load_codes = [&](int slot, int kc, bool live) {
     const int rec = scale_record<FMT>(kc);
+    const uint32_t cv = live ? c_voff : BUF_OOB, sv = live ? s_voff : BUF_OOB;
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) {
       const int sub = col_sub<ACT>(ns, h16);
-      cs[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, chunk_off<10>(sub * KC + kc), BUF_NT);
-      ws[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (sub * groups + rec) * 256, 0);
+      cs[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, cv, chunk_off<10>(sub * KC + kc), BUF_NT);
+      ws[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, sv, (sub * groups + rec) * 256, 0);
     }
   };
   auto chunk = [&](auto bc, int kc) {
     constexpr int d = decltype(bc)::value;   // kc & 1: LDS buffer and code slot
     stage(d ^ 1, stage_soff(kc + 1, KC));
     __builtin_amdgcn_sched_barrier(0);       // the activation loads go first
-    load_codes(d ^ 1, min(kc + 1, KC - 1));
+    load_codes(d ^ 1, min(kc + 1, KC - 1), kc + 1 < KC);
     float lo[TL_NS], hi[TL_NS];
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) chunk_scales<FMT>(ws[d][ns], kc, lo[ns], hi[ns]);
@@ -695,7 +701,7 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
   using B1 = std::integral_constant<int, 1>;
   stage(0, 0);
   __builtin_amdgcn_sched_barrier(0);
-  load_codes(0, 0);
+  load_codes(0, 0, true);
   vm_wait_barrier<0>();
   int k0 = 0;
   for (; k0 + 2 <= KC; k0 += 2) {
@@ -834,25 +840,26 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
 //
 // Same workgroup shape as the tiled kernel: 4 waves, 128 rows x 256
 // columns, the activation chunk staged in LDS by direct-to-LDS loads.  Two
-// chunks are staged (LDS buffers for the activations and each wave's weight
-// scale words, a register pair for the weight codes): chunk kc + 1 loads
-// while chunk kc is computed.  A staged chunk holds the 128 rows' codes (64
-// bytes per row, rows contiguous: 8 KiB) and their scale dwords (wave w
-// loads rows 32w .. 32w+31 into its own 256-byte slot; lanes 32..63 read
-// past the buffer and write zeros into the slot's unused half).
+// chunks are staged (LDS buffers for the activations, register pairs for
+// each wave's weight codes and weight scale words): chunk kc + 1 loads
+// while chunk kc is computed, and the last chunk fetches nothing.  A staged
+// chunk holds the 128 rows' codes (64 bytes per row, rows contiguous:
+// 8 KiB) and their scale dwords (wave w loads rows 32w .. 32w+31 into its
+// own 256-byte slot; lanes 32..63 read past the buffer and write zeros into
+// the slot's unused half).
 //
 // Each chunk ends by waiting for all of the wave's loads (vmcnt 0), not for
 // a count that leaves later loads in flight.  A counted wait let a third
 // staged chunk's loads stay in flight, and on MI355X some 4-byte
-// direct-to-LDS loads (the weight scale words) had then not landed when
-// their stage was read: one 16-column subtile of a few thin tiles came out
-// wrong, differently from run to run.  With the full wait a third stage
-// buys nothing, and two stages measured the same.
+// direct-to-LDS loads (the weight scale words, then staged in LDS) had not
+// landed when their stage was read: one 16-column subtile of a few thin
+// tiles came out wrong, differently from run to run.  With the full wait a
+// third stage buys nothing, and two stages measured the same.  The weight
+// scale words, which no other lane reads, now go to registers.
 // ---------------------------------------------------------------------------
 constexpr int Q_CODE_BYTES = TL_BM * 64;                     // 8 KiB
 constexpr int Q_SCALE_BYTES = TL_WAVES * 256;
-constexpr int Q_WSCALE_BYTES = TL_WAVES * TL_NS * 256;       // each wave's weight scale words
-constexpr int Q_STAGE_BYTES = Q_CODE_BYTES + Q_SCALE_BYTES + Q_WSCALE_BYTES;
+constexpr int Q_STAGE_BYTES = Q_CODE_BYTES + Q_SCALE_BYTES;
 constexpr int Q_LOADS = Q_CODE_BYTES / 1024 / TL_WAVES;      // 1 KiB code loads per wave per chunk
 constexpr int Q_STAGES = 2;                                   // chunks staged: one loading, one computed
 
@@ -895,42 +902,44 @@ __device__ __forceinline__ void w4a4_k_walk(uint8_t* s_q, __amdgpu_buffer_rsrc_t
   const int g = lane >> 4;
   const uint32_t c_voff = lane * 16, s_voff = lane * 4;
   u32x4_t cs[Q_STAGES][TL_NS];
-  // this wave's weight scale words in a stage: 256 bytes per subtile, the
-  // word of lane l at byte 4 l
-  const int wsc = Q_CODE_BYTES + Q_SCALE_BYTES + wave * TL_NS * 256;
+  uint32_t ws[Q_STAGES][TL_NS];
   // all loads of chunk kc into stage `slot`: the activation codes and scales
   // (direct to LDS, shared by the four waves), then this wave's weight codes
-  // (registers) and weight scale words (direct to LDS, its own slot)
-  auto issue = [&](auto sc, int kc) {
+  // and weight scale words (registers)
+  // (live false: lane offsets past every buffer, so the loads fetch nothing;
+  // a branch around them would cost registers across the unrolled walk)
+  auto issue = [&](auto sc, int kc, bool live) {
     constexpr int slot = decltype(sc)::value;
     uint8_t* buf = s_q + slot * Q_STAGE_BYTES;
 #pragma unroll
     for (int j = 0; j < Q_LOADS; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qcr, (lds_ptr_t)(buf + (wave * Q_LOADS + j) * 1024), 16, cvo[j],
-                                               kc * 64, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(qsr, (lds_ptr_t)(buf + Q_CODE_BYTES + wave * 256), 4, svo, kc * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qcr, (lds_ptr_t)(buf + (wave * Q_LOADS + j) * 1024), 16,
+                                               live ? cvo[j] : BUF_OOB, kc * 64, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(qsr, (lds_ptr_t)(buf + Q_CODE_BYTES + wave * 256), 4,
+                                             live ? svo : BUF_OOB, kc * 4, 0, 0);
     __builtin_amdgcn_sched_barrier(0);       // the activation loads go first
     const int rec = scale_record<FMT>(kc);
+    const uint32_t cv = live ? c_voff : BUF_OOB, sv = live ? s_voff : BUF_OOB;
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns) {
       const int sub = col_sub<ACT>(ns, h16);
-      cs[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, chunk_off<10>(sub * KC + kc), BUF_NT);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(buf + wsc + ns * 256), 4, s_voff,
-                                               (sub * groups + rec) * 256, 0, 0);
+      cs[slot][ns] = __builtin_amdgcn_raw_buffer_load_b128(cr, cv, chunk_off<10>(sub * KC + kc), BUF_NT);
+      ws[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, sv, (sub * groups + rec) * 256, 0);
     }
   };
   // Chunk kc (stage kc & 1) issues chunk kc + 1 into the other stage (freed
-  // by the barrier that ended chunk kc - 1; past the last chunk it re-loads
-  // the last one), computes, then waits for every load of the wave: chunk
-  // kc + 1 has then landed for every wave when the barrier opens.
+  // by the barrier that ended chunk kc - 1; the last chunk's loads fetch
+  // nothing),
+  // computes, then waits for every load of the wave: chunk kc + 1 has then
+  // landed for every wave when the barrier opens.
   auto chunk = [&](auto sc, int kc) {
     constexpr int d = decltype(sc)::value;
-    issue(std::integral_constant<int, d ^ 1>{}, min(kc + 1, KC - 1));
+    issue(std::integral_constant<int, d ^ 1>{}, min(kc + 1, KC - 1), kc + 1 < KC);
     const uint8_t* buf = s_q + d * Q_STAGE_BYTES;
     uint32_t sb[TL_NS];
 #pragma unroll
     for (int ns = 0; ns < TL_NS; ++ns)
-      sb[ns] = w4a4_block_scale<FMT>(*reinterpret_cast<const uint32_t*>(buf + wsc + ns * 256 + lane * 4), kc, bad);
+      sb[ns] = w4a4_block_scale<FMT>(ws[d][ns], kc, bad);
 #pragma unroll
     for (int ms = 0; ms < NSUB; ++ms) {
       const int row = ms * 16 + r;
@@ -944,7 +953,7 @@ __device__ __forceinline__ void w4a4_k_walk(uint8_t* s_q, __amdgpu_buffer_rsrc_t
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  issue(S0{}, 0);
+  issue(S0{}, 0, true);
   vm_wait_barrier<0>();
   int k0 = 0;
   for (; k0 + 2 <= KC; k0 += 2) {
