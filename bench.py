@@ -61,6 +61,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -93,9 +94,17 @@ GMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_route_amd", "csrc", "gmm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
 
 
+def code_hash(text):
+    """sha256 prefix of C++ source with its comments and blank space removed,
+    so that an edit of the comments keeps the hash of the code."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
+
+
 def gmm_source_hash():
-    with open(GMM_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(GMM_SOURCE, encoding="utf-8") as f:
+        return code_hash(f.read())
 
 
 def algorithmic_bytes(p, fmt):

@@ -21,8 +21,11 @@
 // 32-element scale block of its column: one 16-byte load of codes and one
 // scale per lane per chunk, and 64 contiguous activation bytes per row.
 //
-// Both kernels below issue, for every output element, the same MFMAs in the
-// same order (chunks ascending, steps 0..3), so they return identical bits.
+// The two W4A16 kernels below (the weight-streaming kernel for thin bands,
+// the LDS-tiled one for thick bands) issue, for every output element, the
+// same MFMAs in the same order (chunks ascending, steps 0..3), so they return
+// identical bits.  The W4A4 kernel at the end of the file multiplies MXFP4
+// activations by the same packed weights on the scaled FP4 MFMA.
 #include <type_traits>
 #include <utility>
 
@@ -247,8 +250,9 @@ constexpr uint32_t BUF_OOB = 0x7FFF0000u;  // a lane offset that reads zeros
 // code word loaded feeds one MFMA per row subtile, so a band of up to
 // MS * 16 rows streams its expert's codes once per column group.
 //
-// Pipelining.  A wave's vector loads complete in issue order, so waiting for
-// one load also waits for every load issued before it.  The activations of a
+// Pipelining.  A wave's vector loads into registers (this kernel has no
+// others) complete in issue order, so waiting for one load also waits for
+// every load issued before it.  The activations of a
 // step are therefore loaded together with its codes, D steps ahead, into a
 // ring of D register slots: step kc reads slot kc % D, then refills it with
 // step kc + D.  Waiting for step kc's data then never waits for a later
