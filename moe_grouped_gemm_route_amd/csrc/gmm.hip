@@ -508,11 +508,20 @@ __device__ __forceinline__ u32x4_t lds_read16(uint32_t addr) {
   return r;
 }
 
-// Scalar offset of the staging loads of chunk kn: its 256-byte slice of every
-// activation row, or, past the last chunk, an offset beyond any activation
-// buffer (below 2^31 bytes) so the loads write zeros to LDS without a fetch.
-__device__ __forceinline__ uint32_t stage_soff(int kn, int KC) {
-  return kn < KC ? (uint32_t)kn * 256u : BUF_OOB;
+// The staging loads of chunk kn into LDS buffer `buf`: chunk kn's 256-byte
+// slice of every activation row (scalar offset), each lane's row and segment
+// (lane offset avo).  Past the last chunk the lane offsets are moved beyond
+// the activation buffer, so the loads write zeros without a fetch.
+template <int LOADS>
+__device__ __forceinline__ void stage_chunk(uint8_t* s_a, int buf, int wave, __amdgpu_buffer_rsrc_t xr,
+                                            const uint32_t (&avo)[LOADS], int kn, int KC) {
+  const bool live = kn < KC;
+  const uint32_t soff = live ? (uint32_t)kn * 256u : 0u;
+  uint8_t* dst = s_a + buf * TL_BUF_BYTES + wave * LOADS * 1024;
+#pragma unroll
+  for (int j = 0; j < LOADS; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(dst + j * 1024), 16, live ? avo[j] : BUF_OOB, soff,
+                                             0, 0);
 }
 
 // Fragment f of a chunk (step s = f / NSUB, row subtile ms = f % NSUB) of
@@ -612,17 +621,12 @@ __device__ __forceinline__ void tiled_k_walk_bf16(uint8_t* s_a, __amdgpu_buffer_
   const int lane = threadIdx.x & 63;
   const uint32_t c_voff = lane * 16;
   u32x4_t bw[4][TL_NS];
-  auto stage = [&](int buf, uint32_t soff) {
-    uint8_t* dst = s_a + buf * TL_BUF_BYTES + wave * TL_LOADS * 1024;
-#pragma unroll
-    for (int j = 0; j < TL_LOADS; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(dst + j * 1024), 16, avo[j], soff, 0, 0);
-  };
+  auto stage = [&](int buf, int kn) { stage_chunk<TL_LOADS>(s_a, buf, wave, xr, avo, kn, KC); };
   auto chunk = [&](auto bc, int kc) {
     constexpr int d = decltype(bc)::value;   // kc & 1: LDS buffer
     const int kn = min(kc + 1, KC - 1);
     const uint32_t cvn = kc + 1 < KC ? c_voff : BUF_OOB;   // past the last chunk: no fetch
-    stage(d ^ 1, stage_soff(kc + 1, KC));
+    stage(d ^ 1, kc + 1);
     __builtin_amdgcn_sched_barrier(0);       // the activation loads go first
     u32x4_t ar[P];
     tiled_prologue<NSUB, P, d>(std::make_index_sequence<PRO>{}, ar, va);
@@ -668,12 +672,7 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
   // buffer: rows 4(LOADS w + j) .. +3, lane l landing at byte 16 l, i.e. row
   // 4(LOADS w + j) + l/16, physical segment l & 15, which holds logical
   // segment (l & 15) ^ (row & 15) (avo carries the source offsets).
-  auto stage = [&](int buf, uint32_t soff) {
-    uint8_t* dst = s_a + buf * TL_BUF_BYTES + wave * TL_LOADS * 1024;
-#pragma unroll
-    for (int j = 0; j < TL_LOADS; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(dst + j * 1024), 16, avo[j], soff, 0, 0);
-  };
+  auto stage = [&](int buf, int kn) { stage_chunk<TL_LOADS>(s_a, buf, wave, xr, avo, kn, KC); };
   // past the last chunk the lane offsets point beyond the codes and scale
   // words, so the loads fetch nothing (a branch around them would cost
   // registers across the unrolled walk)
@@ -689,7 +688,7 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
   };
   auto chunk = [&](auto bc, int kc) {
     constexpr int d = decltype(bc)::value;   // kc & 1: LDS buffer and code slot
-    stage(d ^ 1, stage_soff(kc + 1, KC));
+    stage(d ^ 1, kc + 1);
     __builtin_amdgcn_sched_barrier(0);       // the activation loads go first
     load_codes(d ^ 1, min(kc + 1, KC - 1), kc + 1 < KC);
     float lo[TL_NS], hi[TL_NS];
