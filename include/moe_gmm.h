@@ -171,7 +171,9 @@ size_t moe_packed_weight_bytes(int fmt, int32_t E, int32_t N, int32_t K);
  *                packed as given; the weights they scale do not decode to the
  *                format's values, so every output they feed is unspecified.
  *                A zero count means every packed weight decodes exactly.
- * Limits: K % 128 == 0, K < 2^26, N % 64 == 0, E >= 1, E*N*K/2 < 2^40.
+ * Limits: K % 128 == 0, K <= 33,553,408 (a wave's code range of eight
+ * 16-column subtiles stays below 2^31 - 64 KiB), N % 64 == 0, E >= 1,
+ * E*N*K/2 < 2^40.
  */
 int mxfp4_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
                  const float* tensor_scale, int32_t E, int32_t N, int32_t K,
@@ -191,7 +193,7 @@ int mxfp4_encode(int fmt, const uint8_t* codes, const uint8_t* scales,
  * weights   [E, N, K] bf16 bit patterns, K contiguous, 16-byte aligned.
  * packed    out, moe_packed_weight_bytes(MOE_W_BF16, E, N, K) = E*N*K*2
  *           bytes, 256-aligned.
- * Limits as mxfp4_encode, and K < 2^25.  (mxfp4_encode rejects MOE_W_BF16
+ * Limits as mxfp4_encode, and K <= 16,776,704.  (mxfp4_encode rejects MOE_W_BF16
  * with MOE_ERR_FORMAT.)
  */
 int moe_bf16_encode(const uint16_t* weights, int32_t E, int32_t N, int32_t K, void* packed,
@@ -222,7 +224,9 @@ int moe_bf16_encode(const uint16_t* weights, int32_t E, int32_t N, int32_t K, vo
  * Preconditions not checked: row_index values lie in [0, x_rows); group_offsets
  * is non-decreasing with group_offsets[0] = 0 and group_offsets[E] <= M.
  * Exact-decode domain: MXFP4 scale bytes 2..252 (block exponent -125..125).
- * Limits as mxfp4_encode; E <= 1024; M <= 2^24; x_rows * K * 2 < 2^31 bytes.
+ * Limits as mxfp4_encode; E <= 1024; M <= 2^24; K <= 33,553,408 and
+ * x_rows * K * 2 <= 2^31 - 64 KiB bytes (every buffer range a kernel builds
+ * stays below the lane offset its bounded loads use to read zeros).
  */
 int moe_gmm(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
             const uint16_t* x, int32_t x_rows, const int32_t* row_index,
@@ -255,7 +259,7 @@ int moe_gmm_ex(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
  *   y[r, j] = silu(g) * u,  g = out[r, j],  u = out[r, N/2 + j],
  *   silu(g) = g / (1 + e^-g), out the f32 matmul sums of moe_gmm (times the
  *   NVFP4 tensor scale), evaluated in f32; the [M, N] sums are never written.
- *   Requires N % 128 == 0 and (N/32 + 2) * (K/128) KiB < 4 GiB.
+ *   Requires N % 128 == 0 and (N/32 + 2) * (K/128) KiB <= 2^31 - 64 KiB.
  * Every kernel configuration returns bitwise identical y.  Other arguments,
  * limits and errors as moe_gmm; an unknown act returns MOE_ERR_FORMAT, and
  * MOE_ACT_SILU_MUL with MOE_W_BF16 weights MOE_ERR_UNSUPPORTED.
@@ -318,7 +322,7 @@ int moe_mxfp4_quantize(const uint16_t* x, int32_t R, int32_t K, uint8_t* codes, 
  *                on the device); outputs that read such a block are
  *                unspecified.  Always 0 for MXFP4.
  * Other arguments, limits and errors as moe_gmm_act, with
- * x_rows * K/2 < 2^31.  LDS-tiled kernel (meant for prefill bands).
+ * x_rows * K/2 <= 2^31 - 64 KiB.  LDS-tiled kernel (meant for prefill bands).
  */
 int moe_gmm_w4a4(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint8_t* xq_codes,
                  const uint8_t* xq_scales, int32_t x_rows, const int32_t* row_index,

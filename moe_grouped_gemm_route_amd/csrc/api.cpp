@@ -23,11 +23,10 @@ int check_weight_shape(int fmt, int32_t E, int32_t N, int32_t K) {
   if (K % 128 != 0 || N % 64 != 0) return MOE_ERR_SHAPE;
   if ((int64_t)E * N * (K / 2) >= kMaxCodeBytes) return MOE_ERR_SHAPE;
   // a wave's code range (up to eight 16-column subtiles of 1 KiB per chunk)
-  // is addressed with 32-bit offsets
-  if ((int64_t)8 * (K / 128) * 1024 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
-  // bf16 weights: a wave's (up to four) 4 KiB-per-chunk subtiles are
-  // addressed with 32-bit offsets
-  if (fmt == MOE_W_BF16 && (int64_t)4 * (K / 128) * 4096 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
+  // stays below the lane offset that reads zeros
+  if ((int64_t)8 * (K / 128) * 1024 > (int64_t)moe::kLaneOob) return MOE_ERR_SHAPE;
+  // bf16 weights: a wave's (up to four) 4 KiB-per-chunk subtiles likewise
+  if (fmt == MOE_W_BF16 && (int64_t)4 * (K / 128) * 4096 > (int64_t)moe::kLaneOob) return MOE_ERR_SHAPE;
   return MOE_OK;
 }
 
@@ -141,16 +140,17 @@ int moe_gmm_act(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, co
   if (!packed || !x || !group_offsets || !y) return MOE_ERR_NULL;
   if (M < 1 || M > kMaxRows) return MOE_ERR_SHAPE;
   if (x_rows < 1 || x_rows > kMaxRows || (!row_index && x_rows < M)) return MOE_ERR_SHAPE;
-  // activation rows are addressed with 32-bit byte offsets
-  if ((int64_t)x_rows * K * 2 >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  // activation rows are addressed with 32-bit byte offsets, below the lane
+  // offset that reads zeros
+  if ((int64_t)x_rows * K * 2 > (int64_t)moe::kLaneOob) return MOE_ERR_SHAPE;
   if (((uintptr_t)packed & 255) || ((uintptr_t)x & 15)) return MOE_ERR_SHAPE;
   // the bf16 comparison arm has no fused activation
   if (fmt == MOE_W_BF16 && act != MOE_ACT_NONE) return MOE_ERR_UNSUPPORTED;
   if (act == MOE_ACT_SILU_MUL) {
     // gate and up halves of 64-column multiples; one wave's code range spans
-    // both halves of an expert and is addressed with 32-bit offsets
+    // both halves of an expert and stays below the lane offset that reads zeros
     if (N % 128 != 0) return MOE_ERR_SHAPE;
-    if ((int64_t)(N / 32 + 2) * (K / 128) * 1024 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
+    if ((int64_t)(N / 32 + 2) * (K / 128) * 1024 > (int64_t)moe::kLaneOob) return MOE_ERR_SHAPE;
   }
   if (kernel == MOE_GMM_AUTO) {
     // Bands averaging 24 rows or more keep the matrix cores busy enough for
@@ -192,12 +192,13 @@ int moe_gmm_w4a4(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, c
   if (!packed || !xq_codes || !xq_scales || !group_offsets || !y) return MOE_ERR_NULL;
   if (M < 1 || M > kMaxRows) return MOE_ERR_SHAPE;
   if (x_rows < 1 || x_rows > kMaxRows || (!row_index && x_rows < M)) return MOE_ERR_SHAPE;
-  // activation codes are addressed with 32-bit byte offsets
-  if ((int64_t)x_rows * (K / 2) >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  // activation codes are addressed with 32-bit byte offsets, below the lane
+  // offset that reads zeros
+  if ((int64_t)x_rows * (K / 2) > (int64_t)moe::kLaneOob) return MOE_ERR_SHAPE;
   if (((uintptr_t)packed & 255) || ((uintptr_t)xq_codes & 15)) return MOE_ERR_SHAPE;
   if (act == MOE_ACT_SILU_MUL) {
     if (N % 128 != 0) return MOE_ERR_SHAPE;
-    if ((int64_t)(N / 32 + 2) * (K / 128) * 1024 >= (int64_t(1) << 32)) return MOE_ERR_SHAPE;
+    if ((int64_t)(N / 32 + 2) * (K / 128) * 1024 > (int64_t)moe::kLaneOob) return MOE_ERR_SHAPE;
   }
   return hip_status(moe::launch_gmm_w4a4(static_cast<const uint8_t*>(packed), fmt, E, N, K, xq_codes, xq_scales,
                                          x_rows, row_index, group_offsets, M, y, y_dtype == MOE_BF16, act,

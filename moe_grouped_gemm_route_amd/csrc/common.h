@@ -8,6 +8,12 @@
 
 namespace moe {
 
+// A buffer-load lane offset that lies past every buffer range the kernels
+// build: a load given it returns zeros (or, for a direct-to-LDS load, writes
+// zeros) without touching memory.  The host rejects sizes that would make a
+// range reach it.
+constexpr uint32_t kLaneOob = 0x7FFF0000u;
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));

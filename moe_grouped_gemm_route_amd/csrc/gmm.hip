@@ -241,7 +241,7 @@ __device__ __forceinline__ int chunk_off(int idx) {
 }
 
 constexpr int BUF_NT = 2;                  // buffer-load cache policy: non-temporal
-constexpr uint32_t BUF_OOB = 0x7FFF0000u;  // a lane offset that reads zeros
+constexpr uint32_t BUF_OOB = kLaneOob;     // a lane offset that reads zeros
 
 // ---------------------------------------------------------------------------
 // Weight-streaming kernel, for bands of a few rows (decode).  Each wave owns
@@ -508,22 +508,6 @@ __device__ __forceinline__ u32x4_t lds_read16(uint32_t addr) {
   return r;
 }
 
-// The staging loads of chunk kn into LDS buffer `buf`: chunk kn's 256-byte
-// slice of every activation row (scalar offset), each lane's row and segment
-// (lane offset avo).  Past the last chunk the lane offsets are moved beyond
-// the activation buffer, so the loads write zeros without a fetch.
-template <int LOADS>
-__device__ __forceinline__ void stage_chunk(uint8_t* s_a, int buf, int wave, __amdgpu_buffer_rsrc_t xr,
-                                            const uint32_t (&avo)[LOADS], int kn, int KC) {
-  const bool live = kn < KC;
-  const uint32_t soff = live ? (uint32_t)kn * 256u : 0u;
-  uint8_t* dst = s_a + buf * TL_BUF_BYTES + wave * LOADS * 1024;
-#pragma unroll
-  for (int j = 0; j < LOADS; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(dst + j * 1024), 16, live ? avo[j] : BUF_OOB, soff,
-                                             0, 0);
-}
-
 // Fragment f of a chunk (step s = f / NSUB, row subtile ms = f % NSUB) of
 // the LDS buffer BUF: decode the step's weights at its first fragment, wait
 // for the fragment's read, issue its NS MFMAs, then issue the read of
@@ -621,7 +605,20 @@ __device__ __forceinline__ void tiled_k_walk_bf16(uint8_t* s_a, __amdgpu_buffer_
   const int lane = threadIdx.x & 63;
   const uint32_t c_voff = lane * 16;
   u32x4_t bw[4][TL_NS];
-  auto stage = [&](int buf, int kn) { stage_chunk<TL_LOADS>(s_a, buf, wave, xr, avo, kn, KC); };
+  // The staging loads of chunk kn into LDS buffer `buf`: chunk kn's 256-byte
+  // slice of every activation row (scalar offset), each lane's row and
+  // segment (lane offset avo).  Past the last chunk the lane offsets are
+  // moved beyond the activation buffer, so the loads write zeros without a
+  // fetch.
+  auto stage = [&](int buf, int kn) {
+    const bool live = kn < KC;
+    const uint32_t soff = live ? (uint32_t)kn * 256u : 0u;
+    uint8_t* dst = s_a + buf * TL_BUF_BYTES + wave * TL_LOADS * 1024;
+#pragma unroll
+    for (int j = 0; j < TL_LOADS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(dst + j * 1024), 16, live ? avo[j] : BUF_OOB, soff,
+                                               0, 0);
+  };
   auto chunk = [&](auto bc, int kc) {
     constexpr int d = decltype(bc)::value;   // kc & 1: LDS buffer
     const int kn = min(kc + 1, KC - 1);
@@ -672,7 +669,20 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
   // buffer: rows 4(LOADS w + j) .. +3, lane l landing at byte 16 l, i.e. row
   // 4(LOADS w + j) + l/16, physical segment l & 15, which holds logical
   // segment (l & 15) ^ (row & 15) (avo carries the source offsets).
-  auto stage = [&](int buf, int kn) { stage_chunk<TL_LOADS>(s_a, buf, wave, xr, avo, kn, KC); };
+  // The staging loads of chunk kn into LDS buffer `buf`: chunk kn's 256-byte
+  // slice of every activation row (scalar offset), each lane's row and
+  // segment (lane offset avo).  Past the last chunk the lane offsets are
+  // moved beyond the activation buffer, so the loads write zeros without a
+  // fetch.
+  auto stage = [&](int buf, int kn) {
+    const bool live = kn < KC;
+    const uint32_t soff = live ? (uint32_t)kn * 256u : 0u;
+    uint8_t* dst = s_a + buf * TL_BUF_BYTES + wave * TL_LOADS * 1024;
+#pragma unroll
+    for (int j = 0; j < TL_LOADS; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(dst + j * 1024), 16, live ? avo[j] : BUF_OOB, soff,
+                                               0, 0);
+  };
   // past the last chunk the lane offsets point beyond the codes and scale
   // words, so the loads fetch nothing (a branch around them would cost
   // registers across the unrolled walk)

@@ -130,6 +130,9 @@ def test_gmm_validation(lib):
     assert f(*args(x_rows=0)) == ERR_SHAPE
     assert f(*args(x_rows=127)) == ERR_SHAPE        # band input needs x_rows >= M
     assert f(*args(x_rows=1 << 22, K=512)) == ERR_SHAPE   # 4 GiB of activations
+    # every byte offset stays below the lane offset that reads zeros (2^31 - 64 KiB)
+    assert f(*args(x_rows=0x7FFF0000 // 8192 + 1, K=4096)) == ERR_SHAPE
+    assert f(*args(E=1, N=64, K=0x7FFF0000 // 8 + 128)) == ERR_SHAPE     # a wave's code range
     assert lib.moe_gmm(None, 0, 8, 512, 256, FAKE, 128, None, FAKE, 128, FAKE, 0, None) == ERR_NULL
 
 
@@ -139,11 +142,14 @@ def test_bf16_arm_validation(lib):
     assert lib.moe_bf16_encode(None, 8, 512, 256, FAKE_ALIGNED, None) == ERR_NULL
     assert lib.moe_bf16_encode(FAKE, 8, 512, 200, FAKE_ALIGNED, None) == ERR_SHAPE
     assert lib.moe_bf16_encode(FAKE, 8, 512, 256, ctypes.c_void_p((1 << 30) + 16), None) == ERR_SHAPE
-    # both kernels take bf16 weights, whose four-subtile chunk ranges must fit
-    # 32-bit offsets: K = 2^25 is one past the limit (rejected before launch)
+    # a wave's code range (four 4 KiB-per-chunk subtiles of bf16 weights,
+    # eight 1 KiB-per-chunk subtiles of MXFP4 / NVFP4) stays below the lane
+    # offset the kernels use to read zeros, 2^31 - 64 KiB
+    assert lib.moe_packed_weight_bytes(2, 1, 64, 0x7FFF0000 // 16384 * 128) > 0
+    assert lib.moe_packed_weight_bytes(2, 1, 64, 0x7FFF0000 // 16384 * 128 + 128) == 0
     assert lib.moe_packed_weight_bytes(2, 1, 64, 1 << 25) == 0
-    # MXFP4 / NVFP4: up to eight subtiles of a wave, K < 2^26
-    assert lib.moe_packed_weight_bytes(0, 1, 128, (1 << 26) - 128) > 0
+    assert lib.moe_packed_weight_bytes(0, 1, 128, 0x7FFF0000 // 8192 * 128) > 0
+    assert lib.moe_packed_weight_bytes(0, 1, 128, 0x7FFF0000 // 8192 * 128 + 128) == 0
     assert lib.moe_packed_weight_bytes(0, 1, 128, 1 << 26) == 0
     assert lib.moe_bf16_encode(FAKE, 1, 64, 1 << 25, FAKE_ALIGNED, None) == ERR_SHAPE
     ex = lib.moe_gmm_ex
@@ -175,6 +181,7 @@ def test_w4a4_validation(lib):
     assert g(*args(fmt=5)) == ERR_FORMAT
     assert g(*args(fmt=1, K=200)) == ERR_SHAPE
     assert g(*args(E=1025)) == ERR_SHAPE
+    assert g(*args(rows=0x7FFF0000 // 2048 + 1, K=4096)) == ERR_SHAPE   # codes past 2^31 - 64 KiB
 
 
 def test_gmm_act_validation(lib):
@@ -187,6 +194,7 @@ def test_gmm_act_validation(lib):
     assert f(*args(N=192)) == ERR_SHAPE                 # halves must be 64-column multiples
     assert f(*args(packed=None)) == ERR_NULL
     assert f(*args(N=1 << 17, K=1 << 17, E=1)) == ERR_SHAPE   # code range past 32-bit offsets
+    assert f(*args(N=4096, K=(0x7FFF0000 // (130 * 1024) + 1) * 128, E=1)) == ERR_SHAPE
 
 
 def test_combine_validation(lib):

@@ -885,11 +885,12 @@ def test_gmm_w4a4_config4_whole_experts():
 @pytest.mark.slow
 @pytest.mark.parametrize("kernel", KERNELS)
 def test_gmm_largest_activation_matrix(kernel):
-    # the activations at the 32-bit byte-offset limit of the buffer loads:
-    # 262,143 token rows x 4096 bf16 = 2^31 - 8 KiB, every row its own
-    # expert band entry (top-1 of 8); the rows of the last tokens are checked
+    # the activations at the limit the call accepts (every byte offset below
+    # the lane offset that reads zeros): 262,136 token rows x 4096 bf16 =
+    # 2^31 - 64 KiB, every row its own expert band entry (top-1 of 8); the
+    # rows of the last tokens are checked
     K, N, E = 4096, 256, 8
-    T = ((1 << 31) - 1) // (2 * K)
+    T = 0x7FFF0000 // (2 * K)
     p = make_problem(T=1, k=1, E=E, K=K, N=N, seed=470)
     rng = np.random.default_rng(471)
     p["x"] = random_bf16_bits(rng, (T, K))
@@ -908,13 +909,13 @@ def test_gmm_largest_activation_matrix(kernel):
 
 
 def test_gmm_w4a4_largest_activation_codes():
-    # W4A4 at the 32-bit byte-offset limit of its activation-code loads:
-    # 1,048,575 token rows x 2048 code bytes = 2^31 - 2 KiB (random codes and
-    # E8M0 scales), every row its own band entry (top-1 of 8), gathered
-    # through row_index; the rows of the last tokens are among the samples
+    # W4A4 at the limit the call accepts for its activation codes: 1,048,544
+    # token rows x 2048 code bytes = 2^31 - 64 KiB (random codes and E8M0
+    # scales), every row its own band entry (top-1 of 8), gathered through
+    # row_index; the rows of the last tokens are among the samples
     from oracle.formats import decode_mxfp4
     K, N, E = 4096, 256, 8
-    T = ((1 << 31) - 1) // (K // 2)
+    T = 0x7FFF0000 // (K // 2)
     p = make_problem(T=1, k=1, E=E, K=K, N=N, seed=480)
     rng = np.random.default_rng(481)
     qc = rng.integers(0, 256, size=(T, K // 2), dtype=np.uint8)
