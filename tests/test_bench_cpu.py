@@ -1,6 +1,6 @@
 """bench.py's host logic on the CPU (no GPU needed): the one-GPU guard, the
-algorithmic byte count behind the roofline, the recorded-traffic guard, and
-the shape of the CPU-baseline record."""
+algorithmic byte count behind the roofline, the recorded-traffic guard and the
+code hash it keys on, and the shape of the CPU-baseline record."""
 
 import json
 import os
@@ -45,6 +45,15 @@ def test_recorded_traffic_needs_the_current_kernel_source(monkeypatch):
     monkeypatch.setattr(bench, "gmm_source_hash", lambda: "0" * 16)
     assert bench.recorded_traffic("w13_decode") is None
     assert bench.recorded_traffic("no_such_workload") is None
+
+
+def test_code_hash_ignores_comments_and_blank_space_only():
+    src = "int f(int a) {\n  // the sum\n  return a + 1;  /* one */\n}\n"
+    same = "int f(int a) {   return a + 1; }  // edited comment\n/* a new\n block */\n"
+    changed = "int f(int a) {\n  return a + 2;\n}\n"
+    assert bench.code_hash(src) == bench.code_hash(same)
+    assert bench.code_hash(src) != bench.code_hash(changed)
+    assert bench.gmm_source_hash() == bench.code_hash(open(bench.GMM_SOURCE, encoding="utf-8").read())
 
 
 def test_cpu_baseline_record():
