@@ -41,8 +41,9 @@ struct Tile {
   int first;  // 1 for the first tile of its expert's band
 };
 
-// Per-wave view of the tile list "for each expert e, ceil(count_e / BM)
-// tiles": lane l covers experts [l*per, l*per + per) and holds the number of
+// Per-wave view of the tile list "for each expert e whose band holds between
+// lo and hi rows, ceil(count_e / BM) tiles" (every non-empty band by
+// default): lane l covers experts [l*per, l*per + per) and holds the number of
 // tiles before them (excl) and up to their end (incl); total is uniform.  The
 // lane's band offsets go[0 .. per] are loaded in one batch and kept in
 // registers, so finding a tile costs one round trip to memory, not one per
@@ -50,13 +51,21 @@ struct Tile {
 constexpr int TS_PER_MAX = 16;   // experts per lane: E <= 1024 over 64 lanes
 
 struct TileScan {
-  int per, excl, incl, total;
+  int per, excl, incl, total, lo, hi;
   int go[TS_PER_MAX + 1];
 };
 
-__device__ __forceinline__ TileScan scan_tiles(const int32_t* __restrict__ goff, int E, int BM) {
+// Tiles of an expert whose band holds c rows, under the scan's band filter.
+__device__ __forceinline__ int band_tiles(int c, int BM, int lo, int hi) {
+  return (c >= lo && c <= hi) ? (c + BM - 1) / BM : 0;
+}
+
+__device__ __forceinline__ TileScan scan_tiles(const int32_t* __restrict__ goff, int E, int BM, int lo = 1,
+                                               int hi = 1 << 30) {
   const int lane = threadIdx.x & 63;
   TileScan ts;
+  ts.lo = lo;
+  ts.hi = hi;
   ts.per = (E + 63) >> 6;
   const int e0 = lane * ts.per;
 #pragma unroll
@@ -64,7 +73,7 @@ __device__ __forceinline__ TileScan scan_tiles(const int32_t* __restrict__ goff,
   int mine = 0;
 #pragma unroll
   for (int i = 0; i < TS_PER_MAX; ++i)
-    if (i < ts.per && e0 + i < E) mine += (ts.go[i + 1] - ts.go[i] + BM - 1) / BM;
+    if (i < ts.per && e0 + i < E) mine += band_tiles(ts.go[i + 1] - ts.go[i], BM, lo, hi);
   int incl = mine;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -91,7 +100,7 @@ __device__ __forceinline__ Tile locate_tile(int E, int BM, const TileScan& ts, i
     for (int i = 0; i < TS_PER_MAX; ++i) {
       if (i < ts.per && e0 + i < E && fe < 0) {
         const int c = ts.go[i + 1] - ts.go[i];
-        const int nt = (c + BM - 1) / BM;
+        const int nt = band_tiles(c, BM, ts.lo, ts.hi);
         if (t < acc + nt) {
           const int j = t - acc;
           fe = e0 + i;
@@ -368,29 +377,17 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
   }
 }
 
+// One unit of the weight-streaming kernel: column group nb (four waves of NS
+// 16-column subtiles each, or of two gate and two up subtiles) of a tile of
+// up to MS * 16 rows.
 template <int NS, int D, int MS, int FMT, bool OBF16, int ACT>
-__global__ __launch_bounds__(256, NS > 4 ? 2 : 3) void gmm_stream_kernel(const uint8_t* __restrict__ packed, Layout L,
-                                                         const uint16_t* __restrict__ x,
-                                                         uint32_t x_bytes,
-                                                         const int32_t* __restrict__ row_index,
-                                                         const int32_t* __restrict__ goff, int E,
-                                                         void* __restrict__ y, int NB) {
-  constexpr int BM = 16 * MS;
+__device__ __forceinline__ void stream_unit(const uint8_t* __restrict__ packed, const Layout& L,
+                                            const uint16_t* __restrict__ x, uint32_t x_bytes,
+                                            const int32_t* __restrict__ row_index, void* __restrict__ y,
+                                            const Tile& tile, int nb) {
+  static_assert(ACT == 0 || NS == 4, "the gate/up activation pairs two gate and two up subtiles");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Tiles are dealt round-robin to the 8 XCDs (the dispatcher deals
-  // consecutive workgroup ids round-robin), and each XCD walks all NB column
-  // groups of its tile before the next one: one expert's codes stream
-  // through one XCD in order, while the tiles of a popular expert spread
-  // over all XCDs and keep their work balanced.
-  const TileScan ts = scan_tiles(goff, E, BM);
-  const int bx = blockIdx.x;
-  const int xcd = bx & 7, kth = bx >> 3;
-  const int t = xcd + 8 * (kth / NB);
-  const int nb = kth - (kth / NB) * NB;
-  if (t >= ts.total) return;
-  static_assert(ACT == 0 || NS == 4, "the gate/up activation pairs two gate and two up subtiles");
-  const Tile tile = locate_tile(E, BM, ts, t);
   // first column (ACT 0) or first gate column (ACT 1) of this wave
   const int n0 = (nb * 4 + wave) * (ACT == 1 ? 32 : NS * 16);
   if (n0 >= (ACT == 1 ? L.N / 2 : L.N)) return;
@@ -431,6 +428,29 @@ __global__ __launch_bounds__(256, NS > 4 ? 2 : 3) void gmm_stream_kernel(const u
     stream_walk<NS, (D > 1 ? D - 1 : 1), 2, FMT, OBF16, ACT, false>(packed, L, tile, n0, h16, xr, a_voff, cr, sr, y);
   else
     stream_walk<NS, D, 1, FMT, OBF16, ACT, false>(packed, L, tile, n0, h16, xr, a_voff, cr, sr, y);
+}
+
+template <int NS, int D, int MS, int FMT, bool OBF16, int ACT>
+__global__ __launch_bounds__(256, NS > 4 ? 2 : 3) void gmm_stream_kernel(const uint8_t* __restrict__ packed, Layout L,
+                                                         const uint16_t* __restrict__ x,
+                                                         uint32_t x_bytes,
+                                                         const int32_t* __restrict__ row_index,
+                                                         const int32_t* __restrict__ goff, int E,
+                                                         void* __restrict__ y, int NB) {
+  constexpr int BM = 16 * MS;
+  // Tiles are dealt round-robin to the 8 XCDs (the dispatcher deals
+  // consecutive workgroup ids round-robin), and each XCD walks all NB column
+  // groups of its tile before the next one: one expert's codes stream
+  // through one XCD in order, while the tiles of a popular expert spread
+  // over all XCDs and keep their work balanced.
+  const TileScan ts = scan_tiles(goff, E, BM);
+  const int bx = blockIdx.x;
+  const int xcd = bx & 7, kth = bx >> 3;
+  const int t = xcd + 8 * (kth / NB);
+  const int nb = kth - (kth / NB) * NB;
+  if (t >= ts.total) return;
+  const Tile tile = locate_tile(E, BM, ts, t);
+  stream_unit<NS, D, MS, FMT, OBF16, ACT>(packed, L, x, x_bytes, row_index, y, tile, nb);
 }
 
 // ---------------------------------------------------------------------------
@@ -725,22 +745,16 @@ __device__ __forceinline__ void tiled_k_walk(uint8_t* s_a, __amdgpu_buffer_rsrc_
   __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>());
 }
 
+// One unit of the LDS-tiled kernel: column group nb (TL_BN columns, or
+// TL_BN / 2 activation columns) of a tile of up to TL_BM rows, staged through
+// the workgroup's LDS buffers s_a.
 template <int FMT, bool OBF16, int ACT>
-__global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __restrict__ packed, Layout L,
-                                                           const uint16_t* __restrict__ x, uint32_t x_bytes,
-                                                           const int32_t* __restrict__ row_index,
-                                                           const int32_t* __restrict__ goff, int E,
-                                                           void* __restrict__ y, int NB) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s_a[2 * TL_BUF_BYTES];
-
+__device__ __forceinline__ void tiled_unit(uint8_t* s_a, const uint8_t* __restrict__ packed, const Layout& L,
+                                           const uint16_t* __restrict__ x, uint32_t x_bytes,
+                                           const int32_t* __restrict__ row_index, void* __restrict__ y,
+                                           const Tile& tile, int nb) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const TileScan ts = scan_tiles(goff, E, TL_BM);
-  const int item = work_item(ts.total * NB, true);
-  if (item < 0) return;
-  const int t = item / NB;
-  const int nb = item - t * NB;
-  const Tile tile = locate_tile(E, TL_BM, ts, t);
   const int K = (int)L.K;
   const int KC = (int)L.KC;
   const int groups = (int)L.groups;
@@ -832,6 +846,72 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
       }
     }
   }
+}
+
+template <int FMT, bool OBF16, int ACT>
+__global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __restrict__ packed, Layout L,
+                                                           const uint16_t* __restrict__ x, uint32_t x_bytes,
+                                                           const int32_t* __restrict__ row_index,
+                                                           const int32_t* __restrict__ goff, int E,
+                                                           void* __restrict__ y, int NB) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a[2 * TL_BUF_BYTES];
+
+  const TileScan ts = scan_tiles(goff, E, TL_BM);
+  const int item = work_item(ts.total * NB, true);
+  if (item < 0) return;
+  const int t = item / NB;
+  const int nb = item - t * NB;
+  const Tile tile = locate_tile(E, TL_BM, ts, t);
+  tiled_unit<FMT, OBF16, ACT>(s_a, packed, L, x, x_bytes, row_index, y, tile, nb);
+}
+
+// ---------------------------------------------------------------------------
+// Split kernel, for MXFP4 bands of mixed sizes (the eight-subtile streaming
+// path: bands of 4 rows or more on average, for instance the down projection
+// under skewed routing).  The weight-streaming units walk a band once per
+// 32-row tile, so a band of 201 rows would stream its expert's codes seven
+// times; here every band of more than SPLIT_TH rows runs as LDS-tiled units
+// instead, which stream them once per 128 rows, and the other bands run as
+// weight-streaming units.  (A threshold of 64 rows measured faster than 32:
+// the host's bound on the tiled units, and so the workgroups that find none,
+// halves.)  One launch, so both kinds share the chip: the
+// first HB workgroups (an upper bound on the tiled units) take one tiled
+// unit each or exit after the scan, the rest one streaming tile each.  (A
+// loop over several tiled units per workgroup spilled registers; streaming
+// tiles placed right after the real tiled units spilled scalar registers and
+// measured the same.)  Both kinds issue the same MFMAs in the same order as the
+// stream and tiled kernels, so the output bits are the same.
+// ---------------------------------------------------------------------------
+constexpr int SPLIT_TH = 64;   // bands of more rows run as tiled units
+constexpr int SPLIT_BM = 32;   // rows of a streaming tile
+
+template <bool OBF16>
+__global__ __launch_bounds__(256, 2) void gmm_split_kernel(const uint8_t* __restrict__ packed, Layout L,
+                                                           const uint16_t* __restrict__ x, uint32_t x_bytes,
+                                                           const int32_t* __restrict__ row_index,
+                                                           const int32_t* __restrict__ goff, int E,
+                                                           void* __restrict__ y, int NB, int HB) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a[2 * TL_BUF_BYTES];
+  const int bx = blockIdx.x;
+  if (bx < HB) {
+    const int NBT = (int)((L.N + TL_BN - 1) / TL_BN);
+    const TileScan ts = scan_tiles(goff, E, TL_BM, SPLIT_TH + 1);
+    if (bx >= ts.total * NBT) return;
+    const int t = bx / NBT;
+    const Tile tile = locate_tile(E, TL_BM, ts, t);
+    tiled_unit<0, OBF16, 0>(s_a, packed, L, x, x_bytes, row_index, y, tile, bx - t * NBT);
+    return;
+  }
+  // streaming tiles dealt to the XCDs as in the stream kernel (HB is a
+  // multiple of 8, so workgroup bx still runs on XCD bx & 7)
+  const TileScan ts = scan_tiles(goff, E, SPLIT_BM, 1, SPLIT_TH);
+  const int sb = bx - HB;
+  const int xcd = sb & 7, kth = sb >> 3;
+  const int t = xcd + 8 * (kth / NB);
+  const int nb = kth - (kth / NB) * NB;
+  if (t >= ts.total) return;
+  const Tile tile = locate_tile(E, SPLIT_BM, ts, t);
+  stream_unit<8, 2, 2, 0, OBF16, 0>(packed, L, x, x_bytes, row_index, y, tile, nb);
 }
 
 // ---------------------------------------------------------------------------
@@ -1141,13 +1221,21 @@ static void launch_stream(const uint8_t* packed, const Layout& L, const uint16_t
   // With a mean band of 4 rows or more the activation loads (one 16-row
   // subtile of 16-byte loads per wave and chunk, whatever the weight count)
   // fetch real rows and cost as much load issue as the codes: eight
-  // subtiles per wave (two waves per SIMD) halve them per weight byte.
-  // Thinner bands keep four subtiles and three waves per SIMD.
+  // subtiles per wave (two waves per SIMD) halve them per weight byte, and
+  // such problems can hold bands long enough for the tiled units of the
+  // split kernel.  Thinner bands keep four subtiles and three waves per SIMD.
   if constexpr (ACT == 0 && FMT == 0) {
     if (M >= 4 * (int64_t)E && L.N % 128 == 0) {
+      // the split kernel: bands of more than SPLIT_TH rows (at most
+      // min(E, M / (SPLIT_TH + 1)) of them, with at most M / TL_BM more
+      // 128-row tiles than bands) as tiled units, one workgroup each; the
+      // other bands as streaming tiles of SPLIT_BM rows
       const int NB = (int)((cols + 512 - 1) / 512);
-      hipLaunchKernelGGL((gmm_stream_kernel<8, D, MS, FMT, OBF16, ACT>), dim3((unsigned)(tiles * NB)),
-                         dim3(256), 0, stream, packed, L, x, x_bytes, row_index, goff, E, y, NB);
+      const int64_t thick = M / (SPLIT_TH + 1) < em ? M / (SPLIT_TH + 1) : em;
+      const int HB = (int)(((M / TL_BM + thick) * ((cols + TL_BN - 1) / TL_BN) + 7) / 8 * 8);
+      const int64_t thin = (M / SPLIT_BM + em + 7) / 8 * 8;
+      hipLaunchKernelGGL((gmm_split_kernel<OBF16>), dim3((unsigned)(HB + thin * NB)), dim3(256), 0, stream, packed,
+                         L, x, x_bytes, row_index, goff, E, y, NB, HB);
       return;
     }
   }

@@ -258,7 +258,10 @@ def _banded_problem(seed, fmt_scales=(-6, -2), N=320):
 
 @pytest.mark.parametrize("fmt,N", [("mxfp4", 320), ("nvfp4", 320), ("mxfp4", 384)])
 def test_gmm_every_band_shape(fmt, N):
-    # N = 384 sends the MXFP4 stream walk through its eight-subtile waves
+    # N = 384 sends the MXFP4 streaming choice through the split kernel (the
+    # mean band is over 4 rows): its bands of more than 64 rows as LDS-tiled
+    # units, 65 .. 200 rows, and the others as eight-subtile streaming waves;
+    # f32 and bf16 output
     p = _banded_problem(260, N=N)
     w, packed = weights_for(p, fmt)
     ref_r = oracle.route_sort(p["topk_ids"], p["E"])
@@ -269,6 +272,8 @@ def test_gmm_every_band_shape(fmt, N):
         _, y = run_gpu(p, packed, fmt, kernel=kernel)
         assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
         ys.append(y)
+        _, yb = run_gpu(p, packed, fmt, kernel=kernel, out_dtype=moe.BF16)
+        assert torch.equal(yb, y.to(torch.bfloat16))
     assert torch.equal(ys[0], ys[1])
 
 
