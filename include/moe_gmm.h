@@ -226,7 +226,12 @@ int moe_bf16_encode(const uint16_t* weights, int32_t E, int32_t N, int32_t K, vo
  * Exact-decode domain: MXFP4 scale bytes 2..252 (block exponent -125..125).
  * Limits as mxfp4_encode; E <= 1024; M <= 2^24; K <= 33,553,408 and
  * x_rows * K * 2 <= 2^31 - 64 KiB bytes (every buffer range a kernel builds
- * stays below the lane offset its bounded loads use to read zeros).
+ * stays below the lane offset its bounded loads use to read zeros).  The
+ * grid, an upper bound on the row tiles times the column groups, stays within
+ * the 2^32 - 1 work-items a dispatch counts (16,777,215 workgroups): about
+ * (M/32 + min(E, M)) * N/256 workgroups for the streaming kernel (N/128 with
+ * bf16 weights or the fused activation) and (M/128 + min(E, M)) * N/256 for
+ * the tiled one; larger grids return MOE_ERR_SHAPE.
  */
 int moe_gmm(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
             const uint16_t* x, int32_t x_rows, const int32_t* row_index,
@@ -322,7 +327,8 @@ int moe_mxfp4_quantize(const uint16_t* x, int32_t R, int32_t K, uint8_t* codes, 
  *                on the device); outputs that read such a block are
  *                unspecified.  Always 0 for MXFP4.
  * Other arguments, limits and errors as moe_gmm_act, with
- * x_rows * K/2 <= 2^31 - 64 KiB.  LDS-tiled kernel (meant for prefill bands).
+ * x_rows * K/2 <= 2^31 - 64 KiB and the tiled kernel's grid.  LDS-tiled
+ * kernel (meant for prefill bands).
  */
 int moe_gmm_w4a4(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, const uint8_t* xq_codes,
                  const uint8_t* xq_scales, int32_t x_rows, const int32_t* row_index,
@@ -343,7 +349,7 @@ int moe_gmm_w4a4(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, c
  * topk_weights   [T, k] float.
  * pair_row       [T*k] int32 (moe_route_sort output).
  * out            [T, N] f32 or bf16 (out_dtype; bf16 = RNE of the f32 sum).
- * Limits: N % 4 == 0, 1 <= k <= 64.
+ * Limits: N % 4 == 0, 1 <= k <= 64, T*k <= 2^24, T*N < 2^40.
  */
 int moe_combine(const void* y, int y_dtype, const float* topk_weights,
                 const int32_t* pair_row, int32_t T, int32_t k, int32_t N,

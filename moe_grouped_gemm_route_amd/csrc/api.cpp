@@ -33,6 +33,9 @@ int check_weight_shape(int fmt, int32_t E, int32_t N, int32_t K) {
 // The matmul kernels find their tiles from the band offsets with 64 lanes
 // of at most 16 experts each.
 constexpr int32_t kMaxGmmExperts = 1024;
+// A dispatch packet counts the work-items of each grid dimension in 32 bits:
+// at 256 work-items per workgroup, at most this many workgroups.
+constexpr int64_t kMaxWorkgroups = 0xFFFFFFFFll / 256;
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
@@ -159,6 +162,7 @@ int moe_gmm_act(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, co
     // band of 18 rows, where streaming is 5-8 % faster, and 24.)
     kernel = ((int64_t)M >= 24 * (int64_t)E) ? MOE_GMM_TILED : MOE_GMM_STREAM;
   }
+  if (moe::gmm_workgroups(fmt, E, N, M, act, kernel) > kMaxWorkgroups) return MOE_ERR_SHAPE;
   return hip_status(moe::launch_gmm(static_cast<const uint8_t*>(packed), fmt, E, N, K, x, x_rows,
                                     row_index, group_offsets, M, y, y_dtype == MOE_BF16, act, kernel,
                                     static_cast<hipStream_t>(stream)));
@@ -200,6 +204,7 @@ int moe_gmm_w4a4(const void* packed, int fmt, int32_t E, int32_t N, int32_t K, c
     if (N % 128 != 0) return MOE_ERR_SHAPE;
     if ((int64_t)(N / 32 + 2) * (K / 128) * 1024 > (int64_t)moe::kLaneOob) return MOE_ERR_SHAPE;
   }
+  if (moe::gmm_workgroups(fmt, E, N, M, act, MOE_GMM_TILED) > kMaxWorkgroups) return MOE_ERR_SHAPE;
   return hip_status(moe::launch_gmm_w4a4(static_cast<const uint8_t*>(packed), fmt, E, N, K, xq_codes, xq_scales,
                                          x_rows, row_index, group_offsets, M, y, y_dtype == MOE_BF16, act,
                                          err_count, static_cast<hipStream_t>(stream)));

@@ -1162,17 +1162,76 @@ __global__ __launch_bounds__(256, 2) void gmm_w4a4_kernel(const uint8_t* __restr
   }
 }
 
+// Grids.  The host launches an upper bound on the tiles (the band sizes are
+// on the device) times the column groups; workgroups past the real tiles exit
+// at once.  A dispatch counts its work-items in 32 bits, so the host checks
+// these counts (gmm_workgroups) before it launches anything.
+struct TiledGrid {
+  int NB;           // column groups of TL_BN columns (TL_BN / 2 gated columns)
+  int64_t groups;
+};
+
+static TiledGrid tiled_grid(int act, int64_t N, int64_t E, int64_t M) {
+  const int64_t em = E < M ? E : M;
+  const int64_t cols = act == 1 ? N / 2 : N;
+  const int64_t bn = act == 1 ? TL_BN / 2 : TL_BN;
+  const int64_t NB = (cols + bn - 1) / bn;
+  return {(int)NB, ((M + TL_BM - 1) / TL_BM + em) * NB};
+}
+
+struct StreamGrid {
+  bool split;       // the split kernel (MXFP4, no activation, mean band >= 4 rows)
+  int NB;           // column groups of one streaming workgroup
+  int HB;           // split kernel: workgroups reserved for tiled units
+  int64_t groups;
+};
+
+// Stream-kernel shape: four 16-column subtiles per wave (64 columns, fewer
+// and longer waves amortise the tile lookup and activation loads), and tiles
+// of up to 32 rows: a popular expert's band streams its codes once per 32
+// rows instead of once per 16.  bf16 weights (fmt 2) carry four times the
+// bytes per column, so their waves own two subtiles (32 columns).
+//
+// With a mean band of 4 rows or more the activation loads (one 16-row
+// subtile of 16-byte loads per wave and chunk, whatever the weight count)
+// fetch real rows and cost as much load issue as the codes: eight subtiles
+// per wave (two waves per SIMD) halve them per weight byte, and such problems
+// can hold bands long enough for the tiled units of the split kernel.  That
+// kernel takes bands of more than SPLIT_TH rows (at most min(E, M /
+// (SPLIT_TH + 1)) of them, with at most M / TL_BM more 128-row tiles than
+// bands) as tiled units, one workgroup each, and the other bands as streaming
+// tiles of SPLIT_BM rows.  Thinner bands keep four subtiles and three waves
+// per SIMD.
+static StreamGrid stream_grid(int fmt, int act, int64_t N, int64_t E, int64_t M) {
+  const int64_t cols = act == 1 ? N / 2 : N;
+  const int64_t em = E < M ? E : M;
+  if (act == 0 && fmt == 0 && M >= 4 * E && N % 128 == 0) {
+    const int64_t NB = (cols + 512 - 1) / 512;
+    const int64_t thick = M / (SPLIT_TH + 1) < em ? M / (SPLIT_TH + 1) : em;
+    const int64_t HB = ((M / TL_BM + thick) * ((cols + TL_BN - 1) / TL_BN) + 7) / 8 * 8;
+    const int64_t thin = (M / SPLIT_BM + em + 7) / 8 * 8;
+    return {true, (int)NB, (int)HB, HB + thin * NB};
+  }
+  const int64_t BM = 32;
+  const int64_t tiles = ((M + BM - 1) / BM + em + 7) / 8 * 8;   // whole rounds of 8 tiles
+  // a workgroup covers 4 * 64 output columns (4 * 32 with bf16 weights), or
+  // 4 * 32 activation columns
+  const int64_t per = act == 1 ? 128 : (fmt == 2 ? 128 : 256);
+  const int64_t NB = (cols + per - 1) / per;
+  return {false, (int)NB, 0, tiles * NB};
+}
+
+int64_t gmm_workgroups(int fmt, int32_t E, int32_t N, int32_t M, int act, int kernel) {
+  return kernel == 1 ? stream_grid(fmt, act, N, E, M).groups : tiled_grid(act, N, E, M).groups;
+}
+
 template <int FMT, bool OBF16, int ACT>
 static void launch_w4a4_t(const uint8_t* packed, const Layout& L, const uint8_t* qcodes, const uint8_t* qscales,
                           int32_t x_rows, const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
                           void* y, int32_t* err_count, hipStream_t stream) {
-  const int64_t em = E < M ? E : M;
-  const int64_t cols = ACT == 1 ? L.N / 2 : L.N;
-  const int bn = ACT == 1 ? TL_BN / 2 : TL_BN;
-  const int NB = (int)((cols + bn - 1) / bn);
-  const int64_t tiles = (M + TL_BM - 1) / TL_BM + em;
-  hipLaunchKernelGGL((gmm_w4a4_kernel<FMT, OBF16, ACT>), dim3((unsigned)(tiles * NB)), dim3(64 * TL_WAVES), 0,
-                     stream, packed, L, qcodes, qscales, x_rows, row_index, goff, E, y, NB, err_count);
+  const TiledGrid g = tiled_grid(ACT, L.N, E, M);
+  hipLaunchKernelGGL((gmm_w4a4_kernel<FMT, OBF16, ACT>), dim3((unsigned)g.groups), dim3(64 * TL_WAVES), 0,
+                     stream, packed, L, qcodes, qscales, x_rows, row_index, goff, E, y, g.NB, err_count);
 }
 
 template <int FMT>
@@ -1203,59 +1262,32 @@ hipError_t launch_gmm_w4a4(const uint8_t* packed, int fmt, int32_t E, int32_t N,
   return hipGetLastError();
 }
 
-// Stream-kernel shape: four 16-column subtiles per wave (64 columns, fewer
-// and longer waves amortise the tile lookup and activation loads), a ring two
-// chunks deep, and tiles of up to 32 rows: a popular expert's band streams
-// its codes once per 32 rows instead of once per 16 (the two-subtile walk
-// keeps a one-chunk ring so that both walks fit three workgroups per CU).
 template <int FMT, bool OBF16, int ACT>
 static void launch_stream(const uint8_t* packed, const Layout& L, const uint16_t* x, uint32_t x_bytes,
                           const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
                           void* y, hipStream_t stream) {
-  // bf16 weights (FMT 2) carry four times the bytes per column, so their
-  // waves own two subtiles (32 columns) to keep the same register budget
-  constexpr int NS = FMT == 2 ? 2 : 4, D = 2, MS = 2, BM = 16 * MS;
-  const int64_t cols = ACT == 1 ? L.N / 2 : L.N;
-  const int64_t em = E < M ? E : M;
-  const int64_t tiles = ((M + BM - 1) / BM + em + 7) / 8 * 8;   // whole rounds of 8 tiles
-  // With a mean band of 4 rows or more the activation loads (one 16-row
-  // subtile of 16-byte loads per wave and chunk, whatever the weight count)
-  // fetch real rows and cost as much load issue as the codes: eight
-  // subtiles per wave (two waves per SIMD) halve them per weight byte, and
-  // such problems can hold bands long enough for the tiled units of the
-  // split kernel.  Thinner bands keep four subtiles and three waves per SIMD.
+  // a ring two chunks deep for one-subtile tiles; the two-subtile walk keeps
+  // a one-chunk ring so that both walks fit three workgroups per CU
+  constexpr int NS = FMT == 2 ? 2 : 4, D = 2, MS = 2;
+  const StreamGrid g = stream_grid(FMT, ACT, L.N, E, M);
   if constexpr (ACT == 0 && FMT == 0) {
-    if (M >= 4 * (int64_t)E && L.N % 128 == 0) {
-      // the split kernel: bands of more than SPLIT_TH rows (at most
-      // min(E, M / (SPLIT_TH + 1)) of them, with at most M / TL_BM more
-      // 128-row tiles than bands) as tiled units, one workgroup each; the
-      // other bands as streaming tiles of SPLIT_BM rows
-      const int NB = (int)((cols + 512 - 1) / 512);
-      const int64_t thick = M / (SPLIT_TH + 1) < em ? M / (SPLIT_TH + 1) : em;
-      const int HB = (int)(((M / TL_BM + thick) * ((cols + TL_BN - 1) / TL_BN) + 7) / 8 * 8);
-      const int64_t thin = (M / SPLIT_BM + em + 7) / 8 * 8;
-      hipLaunchKernelGGL((gmm_split_kernel<OBF16>), dim3((unsigned)(HB + thin * NB)), dim3(256), 0, stream, packed,
-                         L, x, x_bytes, row_index, goff, E, y, NB, HB);
+    if (g.split) {
+      hipLaunchKernelGGL((gmm_split_kernel<OBF16>), dim3((unsigned)g.groups), dim3(256), 0, stream, packed,
+                         L, x, x_bytes, row_index, goff, E, y, g.NB, g.HB);
       return;
     }
   }
-  // a workgroup covers 4 * 64 output columns, or 4 * 32 activation columns
-  const int NB = (int)((cols + (ACT == 1 ? 128 : 64 * NS) - 1) / (ACT == 1 ? 128 : 64 * NS));
-  hipLaunchKernelGGL((gmm_stream_kernel<NS, D, MS, FMT, OBF16, ACT>), dim3((unsigned)(tiles * NB)),
-                     dim3(256), 0, stream, packed, L, x, x_bytes, row_index, goff, E, y, NB);
+  hipLaunchKernelGGL((gmm_stream_kernel<NS, D, MS, FMT, OBF16, ACT>), dim3((unsigned)g.groups),
+                     dim3(256), 0, stream, packed, L, x, x_bytes, row_index, goff, E, y, g.NB);
 }
 
 template <int FMT, bool OBF16, int ACT>
 static void launch_tiled(const uint8_t* packed, const Layout& L, const uint16_t* x, uint32_t x_bytes,
                          const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
                          void* y, hipStream_t stream) {
-  const int64_t em = E < M ? E : M;
-  const int64_t cols = ACT == 1 ? L.N / 2 : L.N;
-  const int bn = ACT == 1 ? TL_BN / 2 : TL_BN;
-  const int NB = (int)((cols + bn - 1) / bn);
-  const int64_t tiles = (M + TL_BM - 1) / TL_BM + em;
-  hipLaunchKernelGGL((gmm_tiled_kernel<FMT, OBF16, ACT>), dim3((unsigned)(tiles * NB)), dim3(64 * TL_WAVES), 0,
-                     stream, packed, L, x, x_bytes, row_index, goff, E, y, NB);
+  const TiledGrid g = tiled_grid(ACT, L.N, E, M);
+  hipLaunchKernelGGL((gmm_tiled_kernel<FMT, OBF16, ACT>), dim3((unsigned)g.groups), dim3(64 * TL_WAVES), 0,
+                     stream, packed, L, x, x_bytes, row_index, goff, E, y, g.NB);
 }
 
 template <int FMT, bool OBF16, int ACT>

@@ -47,6 +47,10 @@ hipError_t launch_gmm(const uint8_t* packed, int fmt, int32_t E, int32_t N, int3
                       const int32_t* group_offsets,
                       int32_t M, void* y, int y_bf16, int act, int kernel, hipStream_t stream);
 
+// Workgroups that launch_gmm launches for these sizes (kernel 1 or 2; the
+// W4A4 kernel's grid is kernel 2's).
+int64_t gmm_workgroups(int fmt, int32_t E, int32_t N, int32_t M, int act, int kernel);
+
 // W4A4: MXFP4 (fmt 0) or NVFP4 (fmt 1, power-of-two block scales) weights
 // times MXFP4-quantized activations (codes [x_rows, K/2], E8M0 scales
 // [x_rows, K/32]) on the scaled FP4 MFMA; err_count (may be NULL) receives the

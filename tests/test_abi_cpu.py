@@ -136,6 +136,22 @@ def test_gmm_validation(lib):
     assert lib.moe_gmm(None, 0, 8, 512, 256, FAKE, 128, None, FAKE, 128, FAKE, 0, None) == ERR_NULL
 
 
+def test_gmm_grid_within_dispatch_limit(lib):
+    # one expert of 2^30 columns: an accepted weight shape whose grids pass
+    # the 2^32 - 1 work-items of a dispatch (16,777,215 workgroups of 256)
+    ex, act, g = lib.moe_gmm_ex, lib.moe_gmm_act, lib.moe_gmm_w4a4
+    N = 1 << 30
+    assert lib.moe_packed_weight_bytes(0, 1, N, 128) > 0
+    # streaming: 8 tile slots x 2^22 column groups of 256
+    assert ex(FAKE_ALIGNED, 0, 1, N, 128, FAKE_ALIGNED, 1, None, FAKE, 1, FAKE, 0, 1, None) == ERR_SHAPE
+    # with the fused activation: 8 x 2^22 groups of 128 gated columns
+    assert act(FAKE_ALIGNED, 0, 1, N, 128, FAKE_ALIGNED, 1, None, FAKE, 1, FAKE, 0, 1, 1, None) == ERR_SHAPE
+    # tiled: (ceil(M / 128) + 1) x 2^22 passes the limit from M = 385 rows
+    assert ex(FAKE_ALIGNED, 0, 1, N, 128, FAKE_ALIGNED, 385, None, FAKE, 385, FAKE, 0, 2, None) == ERR_SHAPE
+    assert g(FAKE_ALIGNED, 0, 1, N, 128, FAKE_ALIGNED, FAKE, 385, None, FAKE, 385, FAKE, 0, 0, None,
+             None) == ERR_SHAPE
+
+
 def test_bf16_arm_validation(lib):
     assert lib.moe_packed_weight_bytes(2, 8, 512, 256) == 8 * 512 * 256 * 2
     assert lib.mxfp4_encode(2, FAKE, FAKE, None, 8, 512, 256, FAKE_ALIGNED, None, None) == ERR_FORMAT

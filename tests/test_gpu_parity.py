@@ -994,6 +994,37 @@ def test_combine_matches_oracle(ydt):
 
 
 @pytest.mark.slow
+def test_combine_strides_past_its_grid_cap():
+    # 2^23 + 4096 tokens of 512 columns (k = 1): 2^30 + 2^19 four-column
+    # quads, more than the 2^22 workgroups of 256 threads the launch is capped
+    # at, so the last 4,096 tokens come from each thread's second stride.
+    # Every output against the closed form of one slot, RNE_bf16(f32(w * y)),
+    # and 96 tokens on both sides of the stride against the oracle.
+    T, N = (1 << 23) + 4096, 512
+    g = torch.Generator(device=DEV).manual_seed(520)
+    y = torch.randn((T, N), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    w = torch.rand((T, 1), generator=g, device=DEV, dtype=torch.float32) + 0.5
+    pair_row = torch.randperm(T, generator=g, device=DEV).to(torch.int32)
+    out = moe.moe_combine(y, w, pair_row, out_dtype=moe.BF16)
+    torch.cuda.synchronize()
+    step = 1 << 20
+    for t0 in range(0, T, step):
+        sl = slice(t0, min(T, t0 + step))
+        ref = (w[sl] * y[pair_row[sl].long()].float()).to(torch.bfloat16)
+        assert torch.equal(out[sl], ref), t0
+        del ref
+    toks = np.concatenate([np.arange(0, 32), np.arange((1 << 23) - 32, (1 << 23) + 32), np.arange(T - 32, T)])
+    pr = pair_row.cpu().numpy()
+    rows = pr[toks]
+    got = out[torch.from_numpy(toks).to(DEV)].float().cpu().numpy()
+    ref = oracle.combine(y[torch.from_numpy(rows).long().to(DEV)].float().cpu().numpy(),
+                         w[torch.from_numpy(toks).to(DEV)].cpu().numpy(),
+                         np.arange(len(toks), dtype=np.int32))
+    # one bf16 rounding (after an f32 one) of the exact product
+    assert np.all(np.abs(got - ref) <= bf16_ulp(ref))
+
+
+@pytest.mark.slow
 def test_config3_w2_then_combine():
     p = make_config(3)
     w, packed = weights_for(p, "mxfp4")
