@@ -19,8 +19,12 @@ reports them in the same line under "workloads": tiny (64 tokens, 8 experts),
 w2_decode (256 tokens, Zipf routing, K = 2048, with the combine), w13_prefill
 (4,096 tokens), nvfp4_w13 (256 tokens, NVFP4 weights from the lossless cast),
 nvfp4_w13_prefill, the whole routed-expert layer at decode and at prefill
-(layer_decode, layer_prefill), and the W4A4 w13 prefill and layer
-(w4a4_w13_prefill, w4a4_layer_prefill).
+(layer_decode, layer_prefill), the W4A4 w13 prefill and layer
+(w4a4_w13_prefill, w4a4_layer_prefill), and one GPU's share of the w13 and
+w2 decode under expert parallelism over 8 GPUs (ep8_w13_decode,
+ep8_w2_decode: experts dealt round-robin, e on GPU e % 8; GPU 0's 32 experts,
+the Zipf head among them, and one top-1 row per token-expert pair routed to
+them, as the dispatch would deliver them; no combine in the share's step).
 
 Other workloads, run alone with --workload:
   layer_decode / layer_prefill: route-sort -> w13 with the SiLU-gated gate/up
@@ -78,6 +82,9 @@ METRIC = "moe_gmm TFLOP/s and HBM GB/s (% roofline), w13/w2, 256 experts top-6"
 GMM_WORKLOADS = {
     "tiny": 1, "w13_decode": 2, "w2_decode": 3, "w13_prefill": 4, "nvfp4_w13": 5, "nvfp4_w13_prefill": 4,
     "bf16_w13_decode": 2, "bf16_w2_decode": 3, "bf16_w13_prefill": 4,
+    # one GPU's share under expert parallelism over 8 GPUs (experts dealt
+    # round-robin; rank 0, which holds the Zipf head expert)
+    "ep8_w13_decode": 2, "ep8_w2_decode": 3,
 }
 NVFP4_GMM = ("nvfp4_w13", "nvfp4_w13_prefill")   # NVFP4 weights from the lossless cast
 LAYER_WORKLOADS = ("layer_decode", "layer_prefill", "w4a4_layer_prefill")
@@ -88,7 +95,7 @@ ROUTE_WORKLOADS = {"route_sort_decode": 2, "route_sort_prefill": 4}   # the rout
 WORKLOADS = sorted(list(GMM_WORKLOADS) + list(LAYER_WORKLOADS) + list(W4A4_WORKLOADS) + list(ROUTE_WORKLOADS))
 # timed after the headline in the default run
 EXTRA_WORKLOADS = ("tiny", "w2_decode", "w13_prefill", "nvfp4_w13", "nvfp4_w13_prefill", "layer_decode",
-                   "layer_prefill", "w4a4_w13_prefill", "w4a4_layer_prefill")
+                   "layer_prefill", "w4a4_w13_prefill", "w4a4_layer_prefill", "ep8_w13_decode", "ep8_w2_decode")
 KERNELS = {"auto": 0, "stream": 1, "tiled": 2}
 GMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_route_amd", "csrc", "gmm.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
@@ -321,10 +328,14 @@ def run_gmm(gpu, workload, steps, warmup, cpu_s, kernel="auto", out_dtype=None, 
     """One grouped-matmul workload: route_sort + moe_gmm (+ moe_combine for
     the down projection) per step."""
     torch, moe = gpu.torch, gpu.moe
-    from moe_grouped_gemm_route_amd.synth import make_config, make_tokens_problem
+    from moe_grouped_gemm_route_amd.synth import make_config, make_ep_share, make_tokens_problem
 
     cfg = GMM_WORKLOADS[workload]
-    p = make_config(cfg) if tokens is None else make_tokens_problem(cfg, tokens)
+    ep = workload.startswith("ep8_")
+    if ep:
+        p = make_ep_share(cfg, gpus=8, rank=0)
+    else:
+        p = make_config(cfg) if tokens is None else make_tokens_problem(cfg, tokens)
     bf16_arm = workload.startswith("bf16_")
     fmt = "nvfp4" if workload in NVFP4_GMM else "mxfp4"
     out_dtype = out_dtype or p["out"]
@@ -352,7 +363,9 @@ def run_gmm(gpu, workload, steps, warmup, cpu_s, kernel="auto", out_dtype=None, 
         del dense
         fmt, wf = "bf16", moe.W_BF16
     tw = gpu.put(p["topk_weights"])
-    combine = cfg == 3
+    # the down matmul's step ends with the combine; under expert parallelism
+    # that runs on the tokens' own GPUs after the return exchange
+    combine = cfg == 3 and not ep
     y = torch.empty((M, N), dtype=torch.bfloat16 if odt == moe.BF16 else torch.float32, device=gpu.dev)
     kern = KERNELS[kernel]
     ws = gpu.route_workspace(T, k, E)
@@ -406,6 +419,9 @@ def run_gmm(gpu, workload, steps, warmup, cpu_s, kernel="auto", out_dtype=None, 
               "weights": fmt + (" (decoded MXFP4 weights)" if bf16_arm else ""),
               "activations": "bf16", "output": out_dtype, "kernel": kernel,
               "step": "route_sort + moe_gmm" + (" + moe_combine" if combine else "")}
+    if ep:
+        config["ep_share"] = ("GPU 0 of 8 after the dispatch: experts e % 8 == 0 of the 256, one top-1 row "
+                              "per (token, slot) pair routed to them")
     out = base_line(workload, steps, gpu.warmup_done, step_s, value, unit, "bf16", config)
     out.update({
         "gmm_us": round(gmm_s * 1e6, 2),

@@ -879,8 +879,11 @@ __global__ __launch_bounds__(256, 2) void gmm_tiled_kernel(const uint8_t* __rest
 // unit each or exit after the scan, the rest one streaming tile each.  (A
 // loop over several tiled units per workgroup spilled registers; streaming
 // tiles placed right after the real tiled units spilled scalar registers and
-// measured the same.)  Both kinds issue the same MFMAs in the same order as the
-// stream and tiled kernels, so the output bits are the same.
+// measured the same.)  A tiled unit covers TBM = 128 rows of a band, or 64
+// when the whole grid fits one round of workgroups (one GPU's share under
+// expert parallelism, say): a few thick bands then spread over twice the
+// CUs.  Both kinds issue the same MFMAs in the same order as the stream and
+// tiled kernels, so the output bits are the same.
 // ---------------------------------------------------------------------------
 constexpr int SPLIT_TH = 64;   // bands of more rows run as tiled units
 constexpr int SPLIT_BM = 32;   // rows of a streaming tile
@@ -890,15 +893,15 @@ __global__ __launch_bounds__(256, 2) void gmm_split_kernel(const uint8_t* __rest
                                                            const uint16_t* __restrict__ x, uint32_t x_bytes,
                                                            const int32_t* __restrict__ row_index,
                                                            const int32_t* __restrict__ goff, int E,
-                                                           void* __restrict__ y, int NB, int HB) {
+                                                           void* __restrict__ y, int NB, int HB, int TBM) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_a[2 * TL_BUF_BYTES];
   const int bx = blockIdx.x;
   if (bx < HB) {
     const int NBT = (int)((L.N + TL_BN - 1) / TL_BN);
-    const TileScan ts = scan_tiles(goff, E, TL_BM, SPLIT_TH + 1);
+    const TileScan ts = scan_tiles(goff, E, TBM, SPLIT_TH + 1);
     if (bx >= ts.total * NBT) return;
     const int t = bx / NBT;
-    const Tile tile = locate_tile(E, TL_BM, ts, t);
+    const Tile tile = locate_tile(E, TBM, ts, t);
     tiled_unit<0, OBF16, 0>(s_a, packed, L, x, x_bytes, row_index, y, tile, bx - t * NBT);
     return;
   }
@@ -1183,8 +1186,12 @@ struct StreamGrid {
   bool split;       // the split kernel (MXFP4, no activation, mean band >= 4 rows)
   int NB;           // column groups of one streaming workgroup
   int HB;           // split kernel: workgroups reserved for tiled units
+  int TBM;          // split kernel: rows of a tiled unit
   int64_t groups;
 };
+
+// Split-kernel workgroups that run at once (two per CU on 256 CUs).
+constexpr int64_t SPLIT_ROUND = 512;
 
 // Stream-kernel shape: four 16-column subtiles per wave (64 columns, fewer
 // and longer waves amortise the tile lookup and activation loads), and tiles
@@ -1198,19 +1205,30 @@ struct StreamGrid {
 // per wave (two waves per SIMD) halve them per weight byte, and such problems
 // can hold bands long enough for the tiled units of the split kernel.  That
 // kernel takes bands of more than SPLIT_TH rows (at most min(E, M /
-// (SPLIT_TH + 1)) of them, with at most M / TL_BM more 128-row tiles than
-// bands) as tiled units, one workgroup each, and the other bands as streaming
-// tiles of SPLIT_BM rows.  Thinner bands keep four subtiles and three waves
-// per SIMD.
+// (SPLIT_TH + 1)) of them) as tiled units, one workgroup each, and the other
+// bands as streaming tiles of SPLIT_BM rows.  Its tiled units cover 128 rows,
+// or 64 when the whole grid is one round of workgroups: 64-row units spread
+// the few thick bands of a small problem over twice the CUs (one GPU's share
+// of the w2 decode under 8-way expert parallelism: 40.9 -> 36.8 us, while
+// 32-row units gave 40.4 and every band as streaming tiles 49.5).  Thinner
+// bands keep four subtiles and three waves per SIMD.
 static StreamGrid stream_grid(int fmt, int act, int64_t N, int64_t E, int64_t M) {
   const int64_t cols = act == 1 ? N / 2 : N;
   const int64_t em = E < M ? E : M;
   if (act == 0 && fmt == 0 && M >= 4 * E && N % 128 == 0) {
     const int64_t NB = (cols + 512 - 1) / 512;
+    const int64_t NBT = (cols + TL_BN - 1) / TL_BN;
     const int64_t thick = M / (SPLIT_TH + 1) < em ? M / (SPLIT_TH + 1) : em;
-    const int64_t HB = ((M / TL_BM + thick) * ((cols + TL_BN - 1) / TL_BN) + 7) / 8 * 8;
     const int64_t thin = (M / SPLIT_BM + em + 7) / 8 * 8;
-    return {true, (int)NB, (int)HB, HB + thin * NB};
+    // the bands of more than SPLIT_TH rows hold at most M / TBM more tiles
+    // than bands
+    auto reserve = [&](int64_t tbm) { return ((M / tbm + thick) * NBT + 7) / 8 * 8; };
+    const int64_t HB = reserve(TL_BM);
+    if (HB + thin * NB <= SPLIT_ROUND) {
+      const int64_t HS = reserve(TL_BM / 2);
+      return {true, (int)NB, (int)HS, TL_BM / 2, HS + thin * NB};
+    }
+    return {true, (int)NB, (int)HB, TL_BM, HB + thin * NB};
   }
   const int64_t BM = 32;
   const int64_t tiles = ((M + BM - 1) / BM + em + 7) / 8 * 8;   // whole rounds of 8 tiles
@@ -1218,7 +1236,7 @@ static StreamGrid stream_grid(int fmt, int act, int64_t N, int64_t E, int64_t M)
   // 4 * 32 activation columns
   const int64_t per = act == 1 ? 128 : (fmt == 2 ? 128 : 256);
   const int64_t NB = (cols + per - 1) / per;
-  return {false, (int)NB, 0, tiles * NB};
+  return {false, (int)NB, 0, TL_BM, tiles * NB};
 }
 
 int64_t gmm_workgroups(int fmt, int32_t E, int32_t N, int32_t M, int act, int kernel) {
@@ -1273,7 +1291,7 @@ static void launch_stream(const uint8_t* packed, const Layout& L, const uint16_t
   if constexpr (ACT == 0 && FMT == 0) {
     if (g.split) {
       hipLaunchKernelGGL((gmm_split_kernel<OBF16>), dim3((unsigned)g.groups), dim3(256), 0, stream, packed,
-                         L, x, x_bytes, row_index, goff, E, y, g.NB, g.HB);
+                         L, x, x_bytes, row_index, goff, E, y, g.NB, g.HB, g.TBM);
       return;
     }
   }

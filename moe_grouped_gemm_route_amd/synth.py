@@ -159,6 +159,32 @@ def make_tokens_problem(cfg, T):
     return p
 
 
+def make_ep_share(cfg, gpus=8, rank=0):
+    """Config cfg as GPU `rank` holds it when the experts are dealt
+    round-robin to `gpus` GPUs (expert e on GPU e % gpus, which spreads a
+    Zipf head over the GPUs; rank 0 holds expert 0, the hottest), after the
+    dispatch: its E / gpus experts under local ids e // gpus, and one row per
+    (token, slot) pair routed to them, in pair order, each routed top-1 to its
+    local expert.  A gate/up problem receives the pairs' token rows, which the
+    local sort gathers again; a band-ordered input (the down matmul, fed by the
+    local gate/up output) takes the config's first rows."""
+    p = make_config(cfg)
+    if p["E"] % gpus:
+        raise ValueError("the experts must divide evenly over the GPUs")
+    ids = p["topk_ids"].reshape(-1)
+    mine = np.nonzero(ids % gpus == rank)[0]
+    M = len(mine)
+    q = dict(p)
+    q["E"], q["T"], q["k"] = p["E"] // gpus, M, 1
+    q["topk_ids"] = (ids[mine] // gpus).astype(np.int32).reshape(M, 1)
+    q["topk_weights"] = p["topk_weights"].reshape(-1)[mine].reshape(M, 1)
+    q["codes"] = np.ascontiguousarray(p["codes"][rank::gpus])
+    q["scales"] = np.ascontiguousarray(p["scales"][rank::gpus])
+    q["x"] = p["x"][mine // p["k"]] if p["gather"] else p["x"][:M]
+    q["name"] = "ep%d_%s" % (gpus, p["name"])
+    return q
+
+
 @lru_cache(maxsize=1)
 def make_layer_decode():
     """One MoE layer at decode: config 2's tokens, routing, router weights and

@@ -15,7 +15,7 @@ import torch
 
 import moe_grouped_gemm_route_amd as moe
 import oracle
-from moe_grouped_gemm_route_amd.synth import make_config, make_problem, random_bf16_bits
+from moe_grouped_gemm_route_amd.synth import make_config, make_ep_share, make_problem, random_bf16_bits
 from gpu_util import (DEV, REL_TOL, bf16_bits_to_f64, bf16_ulp, oracle_gmm_bands, rel_err, run_gpu,
                       to_dev, weights_for)
 
@@ -256,12 +256,14 @@ def _banded_problem(seed, fmt_scales=(-6, -2), N=320):
     return p
 
 
-@pytest.mark.parametrize("fmt,N", [("mxfp4", 320), ("nvfp4", 320), ("mxfp4", 384)])
+@pytest.mark.parametrize("fmt,N", [("mxfp4", 320), ("nvfp4", 320), ("mxfp4", 384), ("mxfp4", 4096)])
 def test_gmm_every_band_shape(fmt, N):
-    # N = 384 sends the MXFP4 streaming choice through the split kernel (the
-    # mean band is over 4 rows): its bands of more than 64 rows as LDS-tiled
-    # units, 65 .. 200 rows, and the others as eight-subtile streaming waves;
-    # f32 and bf16 output
+    # N = 384 and 4096 send the MXFP4 streaming choice through the split
+    # kernel (the mean band is over 4 rows): its bands of more than 64 rows as
+    # LDS-tiled units, 65 .. 200 rows, and the others as eight-subtile
+    # streaming waves; at N = 384 the grid is one round of workgroups and the
+    # tiled units cover 64 rows, at N = 4096 they cover 128; f32 and bf16
+    # output
     p = _banded_problem(260, N=N)
     w, packed = weights_for(p, fmt)
     ref_r = oracle.route_sort(p["topk_ids"], p["E"])
@@ -847,6 +849,31 @@ def test_gmm_config_full_output(cfg):
         assert torch.equal(yb, y32.to(torch.bfloat16))
         got = yb.float().cpu().numpy().astype(np.float64)
         assert np.all(np.abs(got - ref) <= bf16_ulp(ref) + REL_TOL * np.max(np.abs(ref)))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_gmm_ep_share_full_output(cfg):
+    # one GPU's share of the decode workloads under expert parallelism over 8
+    # GPUs (experts e % 8 == 0, local ids e // 8, one top-1 row per pair
+    # routed to them): 54 gathered rows over 32 experts for w13, 319
+    # band-ordered rows for w2 with the Zipf head band of 201 rows (the split
+    # kernel's tiled units).  Every output against the whole oracle, and the
+    # tiled kernel bit for bit equal
+    p = make_ep_share(cfg, gpus=8, rank=0)
+    assert p["E"] == 32 and p["k"] == 1
+    w, packed = weights_for(p, "mxfp4")
+    r, y = run_gpu(p, packed, "mxfp4")
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    assert np.array_equal(r["group_offsets"].cpu().numpy(), ref_r["group_offsets"])
+    assert np.array_equal(r["sorted_token"].cpu().numpy(), ref_r["sorted_token"])
+    ri = ref_r["sorted_token"] if p["gather"] else None
+    bands = oracle_gmm_bands(p["x"], ri, ref_r["group_offsets"], w)
+    ref = np.concatenate([bands[e] for e in sorted(bands)])
+    assert ref.shape == (p["T"], p["N"])
+    assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
+    _, yt = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_TILED, routed=r)
+    assert torch.equal(yt, y)
 
 
 @pytest.mark.slow

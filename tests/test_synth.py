@@ -68,3 +68,36 @@ def test_random_bf16_bits_range_and_determinism():
     v = np.abs(bf16_bits_to_f32(a))
     assert v.min() >= 1.0 / 16 and v.max() < 16.0
     assert 0.4 < np.mean(a >> 15) < 0.6                        # both signs
+
+
+def test_ep_share_partitions_the_pairs():
+    # the 8 shares of the w13 decode workload together hold every (token,
+    # slot) pair once, each with its token's row, its router weight and its
+    # expert's weights under local id e // 8
+    from moe_grouped_gemm_route_amd.synth import make_config, make_ep_share
+    p = make_config(2)
+    ids = p["topk_ids"].reshape(-1)
+    seen = np.zeros(ids.size, dtype=np.int64)
+    for rank in range(8):
+        q = make_ep_share(2, gpus=8, rank=rank)
+        assert q["E"] == 32 and q["k"] == 1 and q["gather"]
+        pairs = np.nonzero(ids % 8 == rank)[0]
+        seen[pairs] += 1
+        assert q["T"] == pairs.size
+        assert np.array_equal(q["topk_ids"].reshape(-1) * 8 + rank, ids[pairs])
+        assert np.array_equal(q["topk_weights"].reshape(-1), p["topk_weights"].reshape(-1)[pairs])
+        assert np.array_equal(q["x"], p["x"][pairs // p["k"]])
+        for le in (0, 31):
+            assert np.array_equal(q["codes"][le], p["codes"][le * 8 + rank])
+            assert np.array_equal(q["scales"][le], p["scales"][le * 8 + rank])
+    assert np.all(seen == 1)
+
+
+def test_ep_share_of_the_down_matmul_holds_the_zipf_head():
+    from moe_grouped_gemm_route_amd.synth import make_config, make_ep_share
+    p = make_config(3)
+    q = make_ep_share(3, gpus=8, rank=0)
+    counts = np.bincount(q["topk_ids"].reshape(-1), minlength=32)
+    full = np.bincount(p["topk_ids"].reshape(-1), minlength=256)
+    assert counts[0] == full[0] == full.max()          # expert 0, the head, on rank 0
+    assert not q["gather"] and q["x"].shape == (q["T"], p["K"])
