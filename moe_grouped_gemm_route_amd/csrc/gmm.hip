@@ -261,14 +261,19 @@ constexpr uint32_t BUF_OOB = kLaneOob;     // a lane offset that reads zeros
 //
 // Pipelining.  A wave's vector loads into registers (this kernel has no
 // others) complete in issue order, so waiting for one load also waits for
-// every load issued before it.  The activations of a
-// step are therefore loaded together with its codes, D steps ahead, into a
-// ring of D register slots: step kc reads slot kc % D, then refills it with
-// step kc + D.  Waiting for step kc's data then never waits for a later
-// step's, and D steps of codes stay in flight.  Codes, scale words and
-// activations go through buffer loads (base in scalar registers, 32-bit
-// lane offsets); activation rows past the band read zeros from outside the
-// buffer.
+// every load issued before it.  The activations of a step are therefore
+// loaded together with its codes, D steps ahead, into a ring of D + 1
+// register slots: step kc first refills slot (kc + D) % (D + 1), which step
+// kc - 1 has finished with, with step kc + D, then works on slot
+// kc % (D + 1).  Waiting for step kc's data then never waits for a later
+// step's, and D steps of codes stay in flight while a step computes.  (With
+// D slots, a slot read and refilled in the same step needs a second set of
+// registers, and the compiler's copy back into the slot at the loop's end
+// waits for the refill just issued: batch-1 w13 decode 25.5 -> 20.7 us and
+// the 64-token one 267.8 -> 264.7 us with the D + 1 ring.  The eight-subtile
+// waves keep D slots, measured faster for them.)  Codes, scale words and activations go
+// through buffer loads (base in scalar registers, 32-bit lane offsets);
+// activation rows past the band read zeros from outside the buffer.
 // ---------------------------------------------------------------------------
 template <int NS, int D, int MSUB, int FMT, bool OBF16, int ACT, bool GEN>
 __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, const Layout& L,
@@ -285,12 +290,23 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
   // 16-byte weight words per lane per chunk: one word of codes, or (bf16
   // weights, FMT 2) the four steps' bf16 operands themselves
   constexpr int CW = FMT == 2 ? 4 : 1;
-  u32x4_t cring[D][NS][CW];
-  uint32_t sring[D][NS];
-  u32x4_t aring[D][MSUB][4];
-  // the codes go first: they depend only on the expert, so the first ones
-  // are in flight while the gathered row indices are still arriving
+  // D + 1 slots (four-subtile waves), or D (eight-subtile waves, below)
+  constexpr bool SPARE = NS <= 4;
+  constexpr int R = SPARE ? D + 1 : D;
+  u32x4_t cring[R][NS][CW];
+  uint32_t sring[R][NS];
+  u32x4_t aring[R][MSUB][4];
+  // The codes go first: they depend only on the expert, so the first ones
+  // are in flight while the gathered row indices are still arriving.  A step
+  // past the last chunk still issues its loads, with lane offsets past every
+  // buffer (they fetch nothing and return zeros), so that no branch guards a
+  // load: a guarded refill makes the compiler merge the wait counts of both
+  // paths and wait for the refill just issued, which leaves one step in
+  // flight instead of D.
   auto load_step = [&](int slot, int kc) {
+    const bool live = kc < KC;
+    const int kq = live ? kc : KC - 1;
+    const uint32_t cv = live ? c_voff : BUF_OOB, sv = live ? s_voff : BUF_OOB;
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
       const int sub = col_sub<ACT>(ns, h16);
@@ -298,18 +314,19 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           cring[slot][ns][s] =
-              __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, chunk_off<12>(sub * KC + kc) + s * 1024, BUF_NT);
+              __builtin_amdgcn_raw_buffer_load_b128(cr, cv, chunk_off<12>(sub * KC + kq) + s * 1024, BUF_NT);
       } else {
-        cring[slot][ns][0] = __builtin_amdgcn_raw_buffer_load_b128(cr, c_voff, chunk_off<10>(sub * KC + kc), BUF_NT);
-        const int rec = FMT == 0 ? (kc >> 2) : (kc >> 1);
-        sring[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, s_voff, (sub * groups + rec) * 256, 0);
+        cring[slot][ns][0] = __builtin_amdgcn_raw_buffer_load_b128(cr, cv, chunk_off<10>(sub * KC + kq), BUF_NT);
+        const int rec = FMT == 0 ? (kq >> 2) : (kq >> 1);
+        sring[slot][ns] = __builtin_amdgcn_raw_buffer_load_b32(sr, sv, (sub * groups + rec) * 256, 0);
       }
     }
 #pragma unroll
     for (int ms = 0; ms < MSUB; ++ms)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        aring[slot][ms][q] = __builtin_amdgcn_raw_buffer_load_b128(xr, a_voff[ms], kc * 256 + q * 16, 0);
+        aring[slot][ms][q] =
+            __builtin_amdgcn_raw_buffer_load_b128(xr, live ? a_voff[ms] : BUF_OOB, kq * 256 + q * 16, 0);
   };
 
   f32x4_t acc[MSUB][NS];
@@ -317,44 +334,74 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
   for (int ms = 0; ms < MSUB; ++ms)
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) acc[ms][ns] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // step kc's decode (codes c, scale words w) and MFMAs (activations a)
+  auto mul = [&](const u32x4_t (&c)[NS][CW], const uint32_t (&w)[NS], const u32x4_t (&a)[MSUB][4], const int kc) {
+    float lo[NS], hi[NS];
+    if constexpr (FMT != 2) {
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d < KC) load_step(d, d);
-
-  for (int k0 = 0; k0 < KC; k0 += D) {
+      for (int ns = 0; ns < NS; ++ns) chunk_scales<FMT>(w[ns], kc, lo[ns], hi[ns]);
+    }
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int kc = k0 + d;
-      if (kc < KC) {
-        u32x4_t c[NS][CW], a[MSUB][4];
-        uint32_t w[NS];
+    for (int s = 0; s < 4; ++s) {
 #pragma unroll
-        for (int ns = 0; ns < NS; ++ns) {
-#pragma unroll
-          for (int i = 0; i < CW; ++i) c[ns][i] = cring[d][ns][i];
-          if (FMT != 2) w[ns] = sring[d][ns];
-        }
+      for (int ns = 0; ns < NS; ++ns) {
+        u32x4_t b;
+        if constexpr (FMT == 2) b = c[ns][s];
+        else b = decode_step<FMT, GEN>(c[ns][0][s], s < 2 ? lo[ns] : hi[ns]);
 #pragma unroll
         for (int ms = 0; ms < MSUB; ++ms)
+          acc[ms][ns] = mfma(as_bf16x8(a[ms][s]), as_bf16x8(b), acc[ms][ns]);
+      }
+    }
+  };
+
 #pragma unroll
-          for (int q = 0; q < 4; ++q) a[ms][q] = aring[d][ms][q];
-        if (kc + D < KC) load_step(d, kc + D);
-        float lo[NS], hi[NS];
-        if constexpr (FMT != 2) {
+  for (int d = 0; d < D; ++d) load_step(d, d);
+  if constexpr (SPARE) {
+    // step kc on slot d = kc % R: refill slot (d + D) % R, which step kc - 1
+    // finished with, with step kc + D, then work on slot d.  The scheduling
+    // barrier keeps the refill whole and ahead of the step's work, so that
+    // the loads stay grouped by step in issue order.  Whole rounds of R steps
+    // with no branch inside, then the KC % R left.
+    auto step = [&](const int d, const int kc) {
+      load_step((d + D) % R, kc + D);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(cring[d], sring[d], aring[d], kc);
+    };
+    const int KF = KC - KC % R;
+    for (int k0 = 0; k0 < KF; k0 += R) {
 #pragma unroll
-          for (int ns = 0; ns < NS; ++ns) chunk_scales<FMT>(w[ns], kc, lo[ns], hi[ns]);
-        }
+      for (int d = 0; d < R; ++d) step(d, k0 + d);
+    }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+    for (int d = 0; d + 1 < R; ++d)
+      if (KF + d < KC) step(d, KF + d);
+  } else {
+    // Eight-subtile waves (two waves per SIMD, the streaming units of the
+    // split kernel) keep D slots: step kc copies slot kc % D to registers,
+    // refills it with step kc + D unless that is past the end, and works on
+    // the copy.  Its waits are the compiler's merged ones, and with many
+    // waves per CU that measured faster than the D + 1 ring (w13 at 512
+    // tokens 365.8 against 381.3 us, w2 decode 174.0 against 176.3).
+    for (int k0 = 0; k0 < KC; k0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int kc = k0 + d;
+        if (kc < KC) {
+          u32x4_t c[NS][CW], a[MSUB][4];
+          uint32_t w[NS];
 #pragma unroll
           for (int ns = 0; ns < NS; ++ns) {
-            u32x4_t b;
-            if constexpr (FMT == 2) b = c[ns][s];
-            else b = decode_step<FMT, GEN>(c[ns][0][s], s < 2 ? lo[ns] : hi[ns]);
 #pragma unroll
-            for (int ms = 0; ms < MSUB; ++ms)
-              acc[ms][ns] = mfma(as_bf16x8(a[ms][s]), as_bf16x8(b), acc[ms][ns]);
+            for (int i = 0; i < CW; ++i) c[ns][i] = cring[d][ns][i];
+            if (FMT != 2) w[ns] = sring[d][ns];
           }
+#pragma unroll
+          for (int ms = 0; ms < MSUB; ++ms)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) a[ms][q] = aring[d][ms][q];
+          if (kc + D < KC) load_step(d, kc + D);
+          mul(c, w, a, kc);
         }
       }
     }
@@ -431,7 +478,7 @@ __device__ __forceinline__ void stream_unit(const uint8_t* __restrict__ packed, 
 }
 
 template <int NS, int D, int MS, int FMT, bool OBF16, int ACT>
-__global__ __launch_bounds__(256, NS > 4 ? 2 : 3) void gmm_stream_kernel(const uint8_t* __restrict__ packed, Layout L,
+__global__ __launch_bounds__(256, (NS > 4 || FMT == 1) ? 2 : 3) void gmm_stream_kernel(const uint8_t* __restrict__ packed, Layout L,
                                                          const uint16_t* __restrict__ x,
                                                          uint32_t x_bytes,
                                                          const int32_t* __restrict__ row_index,
@@ -1211,7 +1258,7 @@ constexpr int64_t SPLIT_ROUND = 512;
 // the few thick bands of a small problem over twice the CUs (one GPU's share
 // of the w2 decode under 8-way expert parallelism: 40.9 -> 36.8 us, while
 // 32-row units gave 40.4 and every band as streaming tiles 49.5).  Thinner
-// bands keep four subtiles and three waves per SIMD.
+// bands keep four subtiles and three waves per SIMD (two with NVFP4 weights).
 static StreamGrid stream_grid(int fmt, int act, int64_t N, int64_t E, int64_t M) {
   const int64_t cols = act == 1 ? N / 2 : N;
   const int64_t em = E < M ? E : M;
@@ -1284,8 +1331,10 @@ template <int FMT, bool OBF16, int ACT>
 static void launch_stream(const uint8_t* packed, const Layout& L, const uint16_t* x, uint32_t x_bytes,
                           const int32_t* row_index, const int32_t* goff, int32_t E, int32_t M,
                           void* y, hipStream_t stream) {
-  // a ring two chunks deep for one-subtile tiles; the two-subtile walk keeps
-  // a one-chunk ring so that both walks fit three workgroups per CU
+  // two chunks in flight for one-subtile tiles; the two-subtile walk keeps
+  // one so that both walks fit three workgroups per CU (two with NVFP4
+  // weights, whose walks for general E4M3 scales need more registers: at
+  // three they spilled and ran 3 % slower)
   constexpr int NS = FMT == 2 ? 2 : 4, D = 2, MS = 2;
   const StreamGrid g = stream_grid(FMT, ACT, L.N, E, M);
   if constexpr (ACT == 0 && FMT == 0) {
