@@ -239,9 +239,12 @@ int moe_gmm(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
             void* stream);
 
 /* moe_gmm_ex - moe_gmm with an explicit kernel configuration
- * (moe_gmm_kernel_t).  Every configuration computes the same sums in the same
- * order, so all of them return bitwise identical y; this holds for
- * MOE_W_BF16 weights too. */
+ * (moe_gmm_kernel_t).  AUTO takes the LDS-tiled kernel when M >= 24 * E (a
+ * mean band of 24 rows or more) and the weight-streaming one otherwise.  With
+ * MXFP4 weights, no fused activation and M >= 4 * E, the streaming choice
+ * runs bands of more than 64 rows as LDS-tiled units inside the same launch.
+ * Every configuration computes the same sums in the same order, so all of
+ * them return bitwise identical y; this holds for MOE_W_BF16 weights too. */
 int moe_gmm_ex(const void* packed, int fmt, int32_t E, int32_t N, int32_t K,
                const uint16_t* x, int32_t x_rows, const int32_t* row_index,
                const int32_t* group_offsets, int32_t M, void* y, int y_dtype,
