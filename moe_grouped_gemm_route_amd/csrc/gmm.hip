@@ -266,14 +266,19 @@ constexpr uint32_t BUF_OOB = kLaneOob;     // a lane offset that reads zeros
 // register slots: step kc first refills slot (kc + D) % (D + 1), which step
 // kc - 1 has finished with, with step kc + D, then works on slot
 // kc % (D + 1).  Waiting for step kc's data then never waits for a later
-// step's, and D steps of codes stay in flight while a step computes.  (With
-// D slots, a slot read and refilled in the same step needs a second set of
-// registers, and the compiler's copy back into the slot at the loop's end
-// waits for the refill just issued: batch-1 w13 decode 25.5 -> 20.7 us and
-// the 64-token one 267.8 -> 264.7 us with the D + 1 ring.  The eight-subtile
-// waves keep D slots, measured faster for them.)  Codes, scale words and activations go
-// through buffer loads (base in scalar registers, 32-bit lane offsets);
-// activation rows past the band read zeros from outside the buffer.
+// step's, and D steps of codes stay in flight while a step computes.
+//
+// With only D slots, a slot is read and refilled in the same step; its new
+// contents need a second set of registers, and the compiler's copy back
+// into the slot at the loop's end waits for the refill just issued, so one
+// step is in flight, not D.  The D + 1 ring took a batch-1 w13 decode from
+// 25.5 to 20.7 us and the 64-token one from 267.8 to 264.7 us.  The
+// eight-subtile waves (two per SIMD) keep D slots, which measured faster for
+// them.
+//
+// Codes, scale words and activations go through buffer loads (base in
+// scalar registers, 32-bit lane offsets); activation rows past the band read
+// zeros from outside the buffer.
 // ---------------------------------------------------------------------------
 template <int NS, int D, int MSUB, int FMT, bool OBF16, int ACT, bool GEN>
 __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, const Layout& L,
