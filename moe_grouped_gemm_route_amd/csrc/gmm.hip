@@ -483,7 +483,7 @@ __device__ __forceinline__ void stream_unit(const uint8_t* __restrict__ packed, 
 }
 
 template <int NS, int D, int MS, int FMT, bool OBF16, int ACT>
-__global__ __launch_bounds__(256, (NS > 4 || FMT == 1) ? 2 : 3) void gmm_stream_kernel(const uint8_t* __restrict__ packed, Layout L,
+__global__ __launch_bounds__(256, (NS > 4 || FMT == 1 || D > 2) ? 2 : 3) void gmm_stream_kernel(const uint8_t* __restrict__ packed, Layout L,
                                                          const uint16_t* __restrict__ x,
                                                          uint32_t x_bytes,
                                                          const int32_t* __restrict__ row_index,
@@ -1236,6 +1236,7 @@ static TiledGrid tiled_grid(int act, int64_t N, int64_t E, int64_t M) {
 
 struct StreamGrid {
   bool split;       // the split kernel (MXFP4, no activation, mean band >= 4 rows)
+  bool narrow;      // two-subtile waves with a deep ring (a grid of at most one wave per SIMD)
   int NB;           // column groups of one streaming workgroup
   int HB;           // split kernel: workgroups reserved for tiled units
   int TBM;          // split kernel: rows of a tiled unit
@@ -1244,6 +1245,8 @@ struct StreamGrid {
 
 // Split-kernel workgroups that run at once (two per CU on 256 CUs).
 constexpr int64_t SPLIT_ROUND = 512;
+// Waves of a grid that gets at most one wave per SIMD (4 SIMDs on 256 CUs).
+constexpr int64_t NARROW_WAVES = 1024;
 
 // Stream-kernel shape: four 16-column subtiles per wave (64 columns, fewer
 // and longer waves amortise the tile lookup and activation loads), and tiles
@@ -1264,6 +1267,15 @@ constexpr int64_t SPLIT_ROUND = 512;
 // of the w2 decode under 8-way expert parallelism: 40.9 -> 36.8 us, while
 // 32-row units gave 40.4 and every band as streaming tiles 49.5).  Thinner
 // bands keep four subtiles and three waves per SIMD (two with NVFP4 weights).
+//
+// A grid whose bound gives at most one wave per SIMD even with two subtiles
+// per wave (a batch-1 decode: six rows) is bound by each wave's serial walk:
+// its MFMAs on a one-row band and the load latency with two chunks in
+// flight each take about 0.4 us a chunk.  MXFP4 waves without the fused
+// activation then own two subtiles and keep four chunks in flight (two waves
+// per SIMD of registers): batch-1 w13 decode 20.5 -> 16.4 us, batch-1 w2
+// 14.5 -> 11.9 us.  With more waves than SIMDs the same shape was slower
+// (two tokens: 24.2 -> 26.5 us).
 static StreamGrid stream_grid(int fmt, int act, int64_t N, int64_t E, int64_t M) {
   const int64_t cols = act == 1 ? N / 2 : N;
   const int64_t em = E < M ? E : M;
@@ -1278,17 +1290,21 @@ static StreamGrid stream_grid(int fmt, int act, int64_t N, int64_t E, int64_t M)
     const int64_t HB = reserve(TL_BM);
     if (HB + thin * NB <= SPLIT_ROUND) {
       const int64_t HS = reserve(TL_BM / 2);
-      return {true, (int)NB, (int)HS, TL_BM / 2, HS + thin * NB};
+      return {true, false, (int)NB, (int)HS, TL_BM / 2, HS + thin * NB};
     }
-    return {true, (int)NB, (int)HB, TL_BM, HB + thin * NB};
+    return {true, false, (int)NB, (int)HB, TL_BM, HB + thin * NB};
   }
   const int64_t BM = 32;
   const int64_t tiles = ((M + BM - 1) / BM + em + 7) / 8 * 8;   // whole rounds of 8 tiles
+  if (act == 0 && fmt == 0) {
+    const int64_t NB2 = (cols + 128 - 1) / 128;
+    if (4 * tiles * NB2 <= NARROW_WAVES) return {false, true, (int)NB2, 0, TL_BM, tiles * NB2};
+  }
   // a workgroup covers 4 * 64 output columns (4 * 32 with bf16 weights), or
   // 4 * 32 activation columns
   const int64_t per = act == 1 ? 128 : (fmt == 2 ? 128 : 256);
   const int64_t NB = (cols + per - 1) / per;
-  return {false, (int)NB, 0, TL_BM, tiles * NB};
+  return {false, false, (int)NB, 0, TL_BM, tiles * NB};
 }
 
 int64_t gmm_workgroups(int fmt, int32_t E, int32_t N, int32_t M, int act, int kernel) {
@@ -1346,6 +1362,11 @@ static void launch_stream(const uint8_t* packed, const Layout& L, const uint16_t
     if (g.split) {
       hipLaunchKernelGGL((gmm_split_kernel<OBF16>), dim3((unsigned)g.groups), dim3(256), 0, stream, packed,
                          L, x, x_bytes, row_index, goff, E, y, g.NB, g.HB, g.TBM);
+      return;
+    }
+    if (g.narrow) {
+      hipLaunchKernelGGL((gmm_stream_kernel<2, 4, MS, FMT, OBF16, ACT>), dim3((unsigned)g.groups), dim3(256), 0,
+                         stream, packed, L, x, x_bytes, row_index, goff, E, y, g.NB);
       return;
     }
   }

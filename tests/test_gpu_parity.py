@@ -15,7 +15,8 @@ import torch
 
 import moe_grouped_gemm_route_amd as moe
 import oracle
-from moe_grouped_gemm_route_amd.synth import make_config, make_ep_share, make_problem, random_bf16_bits
+from moe_grouped_gemm_route_amd.synth import (make_config, make_ep_share, make_problem, make_tokens_problem,
+                                              random_bf16_bits)
 from gpu_util import (DEV, REL_TOL, bf16_bits_to_f64, bf16_ulp, oracle_gmm_bands, rel_err, run_gpu,
                       to_dev, weights_for)
 
@@ -872,6 +873,30 @@ def test_gmm_ep_share_full_output(cfg):
     ref = np.concatenate([bands[e] for e in sorted(bands)])
     assert ref.shape == (p["T"], p["N"])
     assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
+    _, yt = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_TILED, routed=r)
+    assert torch.equal(yt, y)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_gmm_batch1_decode_full_output(cfg):
+    # one token (six routed rows) with the config's weights: the streaming
+    # choice gets at most one wave per SIMD and runs two-subtile waves with
+    # four chunks in flight (K = 4096 and 2048: 32 and 16 chunks, both with a
+    # ragged last round of the ring).  Every output against the oracle, the
+    # bf16 output equal to the f32 one's RNE, and the tiled kernel bit for
+    # bit equal
+    p = make_tokens_problem(cfg, 1)
+    assert p["T"] * p["k"] == 6
+    w, packed = weights_for(p, "mxfp4")
+    r, y = run_gpu(p, packed, "mxfp4")
+    ref_r = oracle.route_sort(p["topk_ids"], p["E"])
+    ri = ref_r["sorted_token"] if p["gather"] else None
+    bands = oracle_gmm_bands(p["x"], ri, ref_r["group_offsets"], w)
+    ref = np.concatenate([bands[e] for e in sorted(bands)])
+    assert ref.shape == (6, p["N"])
+    assert rel_err(y.cpu().numpy(), ref) <= REL_TOL
+    _, yb = run_gpu(p, packed, "mxfp4", out_dtype=moe.BF16, routed=r)
+    assert torch.equal(yb, y.to(torch.bfloat16))
     _, yt = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_TILED, routed=r)
     assert torch.equal(yt, y)
 
