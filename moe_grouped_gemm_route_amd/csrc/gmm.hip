@@ -195,9 +195,12 @@ __device__ __forceinline__ void store_tile(void* y, int64_t N, int row0, int row
 // and 3 the up columns N/2 + n0 .. +31, and the wave writes columns
 // n0 .. n0+31 of the [M, N/2] activation.  col_sub is a subtile's 16-column
 // index relative to the wave's first subtile (h16 = N/32).
-template <int ACT>
+// Subtile ns of a wave that owns NS 16-column subtiles: with the fused
+// activation the first NS / 2 are gate subtiles and the rest the matching up
+// subtiles, h16 subtiles further on.
+template <int ACT, int NS = 4>
 __device__ __forceinline__ int col_sub(int ns, int h16) {
-  return (ACT == 1 && ns >= 2) ? ns - 2 + h16 : ns;
+  return (ACT == 1 && ns >= NS / 2) ? ns - NS / 2 + h16 : ns;
 }
 
 // NVFP4: true when every block scale (E4M3) in a wave's four 16-column
@@ -314,7 +317,7 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
     const uint32_t cv = live ? c_voff : BUF_OOB, sv = live ? s_voff : BUF_OOB;
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
-      const int sub = col_sub<ACT>(ns, h16);
+      const int sub = col_sub<ACT, NS>(ns, h16);
       if constexpr (FMT == 2) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
@@ -417,9 +420,9 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
   for (int ms = 0; ms < MSUB; ++ms) {
     if (ACT == 1) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NS / 2; ++j)
         store_tile_silu_mul<OBF16>(y, L.N / 2, tile.m0 + ms * 16, tile.rows - ms * 16, n0 + j * 16 + r,
-                                   acc[ms][j], acc[ms][j + 2], post);
+                                   acc[ms][j], acc[ms][j + NS / 2], post);
     } else {
 #pragma unroll
       for (int ns = 0; ns < NS; ++ns)
@@ -430,21 +433,21 @@ __device__ __forceinline__ void stream_walk(const uint8_t* __restrict__ packed, 
 }
 
 // One unit of the weight-streaming kernel: column group nb (four waves of NS
-// 16-column subtiles each, or of two gate and two up subtiles) of a tile of
-// up to MS * 16 rows.
+// 16-column subtiles each, or of NS / 2 gate and NS / 2 up subtiles) of a
+// tile of up to MS * 16 rows.
 template <int NS, int D, int MS, int FMT, bool OBF16, int ACT>
 __device__ __forceinline__ void stream_unit(const uint8_t* __restrict__ packed, const Layout& L,
                                             const uint16_t* __restrict__ x, uint32_t x_bytes,
                                             const int32_t* __restrict__ row_index, void* __restrict__ y,
                                             const Tile& tile, int nb) {
-  static_assert(ACT == 0 || NS == 4, "the gate/up activation pairs two gate and two up subtiles");
+  static_assert(ACT == 0 || NS % 2 == 0, "the gate/up activation pairs gate and up subtiles");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // first column (ACT 0) or first gate column (ACT 1) of this wave
-  const int n0 = (nb * 4 + wave) * (ACT == 1 ? 32 : NS * 16);
+  const int n0 = (nb * 4 + wave) * (ACT == 1 ? NS * 8 : NS * 16);
   if (n0 >= (ACT == 1 ? L.N / 2 : L.N)) return;
   const int h16 = ACT == 1 ? (int)(L.N / 32) : 0;
-  const int span = ACT == 1 ? h16 + 2 : NS;   // 16-column subtiles the buffer ranges cover
+  const int span = ACT == 1 ? h16 + NS / 2 : NS;   // 16-column subtiles the buffer ranges cover
   const int K = (int)L.K;
   const int r = lane & 15;
   const int g = lane >> 4;
@@ -1271,11 +1274,12 @@ constexpr int64_t NARROW_WAVES = 1024;
 // A grid whose bound gives at most one wave per SIMD even with two subtiles
 // per wave (a batch-1 decode: six rows) is bound by each wave's serial walk:
 // its MFMAs on a one-row band and the load latency with two chunks in
-// flight each take about 0.4 us a chunk.  MXFP4 waves without the fused
-// activation then own two subtiles and keep four chunks in flight (two waves
+// flight each take about 0.4 us a chunk.  MXFP4 waves then own two
+// subtiles and keep four chunks in flight (two waves
 // per SIMD of registers): batch-1 w13 decode 20.5 -> 16.4 us, batch-1 w2
 // 14.5 -> 11.9 us.  With more waves than SIMDs the same shape was slower
-// (two tokens: 24.2 -> 26.5 us).
+// (two tokens: 24.2 -> 26.5 us).  With the fused activation such a wave
+// owns one gate and one up subtile.
 static StreamGrid stream_grid(int fmt, int act, int64_t N, int64_t E, int64_t M) {
   const int64_t cols = act == 1 ? N / 2 : N;
   const int64_t em = E < M ? E : M;
@@ -1296,8 +1300,10 @@ static StreamGrid stream_grid(int fmt, int act, int64_t N, int64_t E, int64_t M)
   }
   const int64_t BM = 32;
   const int64_t tiles = ((M + BM - 1) / BM + em + 7) / 8 * 8;   // whole rounds of 8 tiles
-  if (act == 0 && fmt == 0) {
-    const int64_t NB2 = (cols + 128 - 1) / 128;
+  if (fmt == 0) {
+    // two-subtile waves: 32 output columns, or 16 gate and 16 up columns
+    const int64_t per2 = act == 1 ? 64 : 128;
+    const int64_t NB2 = (cols + per2 - 1) / per2;
     if (4 * tiles * NB2 <= NARROW_WAVES) return {false, true, (int)NB2, 0, TL_BM, tiles * NB2};
   }
   // a workgroup covers 4 * 64 output columns (4 * 32 with bf16 weights), or
@@ -1364,6 +1370,8 @@ static void launch_stream(const uint8_t* packed, const Layout& L, const uint16_t
                          L, x, x_bytes, row_index, goff, E, y, g.NB, g.HB, g.TBM);
       return;
     }
+  }
+  if constexpr (FMT == 0) {
     if (g.narrow) {
       hipLaunchKernelGGL((gmm_stream_kernel<2, 4, MS, FMT, OBF16, ACT>), dim3((unsigned)g.groups), dim3(256), 0,
                          stream, packed, L, x, x_bytes, row_index, goff, E, y, g.NB);

@@ -899,6 +899,15 @@ def test_gmm_batch1_decode_full_output(cfg):
     assert torch.equal(yb, y.to(torch.bfloat16))
     _, yt = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_TILED, routed=r)
     assert torch.equal(yt, y)
+    if cfg == 2:
+        # the w13 of a batch-1 layer: the fused activation on the same path,
+        # each wave one gate and one up subtile
+        ref_h = oracle.silu_mul(ref)
+        _, h = run_gpu(p, packed, "mxfp4", act=moe.ACT_SILU_MUL, routed=r)
+        assert tuple(h.shape) == (6, p["N"] // 2)
+        assert rel_err(h.cpu().numpy(), ref_h) <= REL_TOL
+        _, ht = run_gpu(p, packed, "mxfp4", kernel=moe.GMM_TILED, act=moe.ACT_SILU_MUL, routed=r)
+        assert torch.equal(ht, h)
 
 
 @pytest.mark.slow
